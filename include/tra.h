@@ -1,0 +1,191 @@
+/*
+ * tra.h - C ABI of the Token Radius Attention (TRA) hot path for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The method ("Token Radius Attention for Efficient Video Generation", summary
+ * page, section 2 "Méthodologie": Intuition I, Intuition II, "Le Pipeline TRA")
+ * gives every query token of a T x H x W latent video its own attention
+ * support: the query's attention entropy sets a token budget, the budget sets a
+ * spatial disk radius, the radius shrinks with temporal distance, and the
+ * resulting token-level masks are turned into a block-sparse tile list that a
+ * block-sparse attention kernel consumes.  The pages fix the shape of each step
+ * but no constants; the constants arrive here through tra_params.
+ *
+ * Two calls form the path:
+ *   tra_plan_create  entropy -> budget level -> radius table -> CSR tile lists
+ *   tra_attention    block-sparse softmax attention with the exact per-token mask
+ * A plan is reusable across calls whose Q/K/V have the plan's shape (the pages'
+ * warm-up reuse: entropy is measured once and reused in later denoising steps).
+ *
+ * Conventions shared by every call:
+ *   - Tensors q, k, v, o are DEVICE pointers to contiguous [B, heads, N, d]
+ *     arrays, N = T*H*W, token n = (t*H + h)*W + w (frame, then row, then
+ *     column), 16-byte aligned, all of the shape's dtype.  The caller owns them.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call is
+ *     asynchronous on that stream except where noted.
+ *   - Errors are reported by status code only; a failing call writes no
+ *     output and *out stays NULL.  tra_last_error() gives a message for the
+ *     last failure on the calling thread.
+ *   - Supported on the device: dtype TRA_BF16 with head_dim 64 or 128 (bf16
+ *     matrix cores), dtype TRA_F32 with head_dim 64 or 128 (fp32 vector path),
+ *     8 x 8 tiles (tile_h = tile_w = 8).
+ */
+#ifndef TRA_H
+#define TRA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TRA_OK = 0,
+  TRA_ERR_INVALID_ARG = 1,   /* bad parameter value or NULL pointer            */
+  TRA_ERR_SHAPE = 2,         /* unsupported or inconsistent shape              */
+  TRA_ERR_DTYPE = 3,         /* unsupported dtype / head_dim combination        */
+  TRA_ERR_PLAN_MISMATCH = 4, /* tensors do not match the plan's shape          */
+  TRA_ERR_OOM = 5,           /* device or host allocation failed               */
+  TRA_ERR_OVERFLOW = 6,      /* a count exceeds the 32-bit index range         */
+  TRA_ERR_HIP = 7            /* a HIP runtime call failed                       */
+} tra_status;
+
+typedef enum { TRA_F32 = 0, TRA_BF16 = 1 } tra_dtype;
+
+/* Problem shape.  B batch, heads, T x H x W latent grid, head_dim d. */
+typedef struct {
+  int32_t B, heads, T, H, W, head_dim;
+  int32_t dtype; /* tra_dtype */
+} tra_shape;
+
+/*
+ * Method constants.
+ *   a, c            log-linear entropy -> budget map: ln B = a*H_i + c.  The
+ *                   summary page's analytic map B ~ tau*exp(H_i) (Intuition I)
+ *                   is a = 1, c = ln tau.
+ *   budget_min/max  clamp of the token budget, in tokens (> 0, min <= max).
+ *   levels_per_nat  budget quantisation q: level k_i = floor(q*(a*H_i + c)),
+ *                   clamped to [ceil(q ln budget_min), floor(q ln budget_max)];
+ *                   the quantised budget is exp(k_i/q).
+ *   decay           phi in (0, 1]: radius at temporal distance delta is
+ *                   r0 * phi^delta (the pages' phi(delta) = exp(-gamma*delta),
+ *                   phi = exp(-gamma)).
+ *   pool_h, pool_w  key pooling rectangle inside a frame (entropy is taken over
+ *                   the mean-pooled keys, ragged rectangles weighted by size).
+ *   tile_h, tile_w  query/key tile inside a frame for the block-sparse lists.
+ *   radius_override < 0: off.  >= 0: every query uses r0 = radius_override
+ *                   (entropy is skipped and every exported level is -1).
+ */
+typedef struct {
+  double a, c, budget_min, budget_max, decay, radius_override;
+  int32_t levels_per_nat, pool_h, pool_w, tile_h, tile_w;
+} tra_params;
+
+typedef struct tra_plan tra_plan; /* opaque; owns its device buffers */
+
+/* Sizes of a plan, all counts per whole plan. */
+typedef struct {
+  int64_t n_queries;    /* B*heads*N                                             */
+  int64_t n_rows;       /* B*heads*n_qtiles: CSR rows, head-major                */
+  int64_t nnz;          /* CSR entries (listed query-tile/key-tile pairs)        */
+  int32_t n_qtiles;     /* tiles per head = T*ceil(H/tile_h)*ceil(W/tile_w)      */
+  int32_t n_pool;       /* pooled keys per head = T*ceil(H/pool_h)*ceil(W/pool_w)*/
+  int32_t n_levels;     /* rows of the radius table                              */
+  int32_t k_lo;         /* level of table row 0 (-1 under radius_override)       */
+  int32_t T;            /* columns of the radius table                           */
+  int32_t max_row_len;  /* longest CSR row                                       */
+} tra_plan_info;
+
+/*
+ * Host-only validation of a shape and parameter set (no GPU needed).
+ * Returns TRA_OK or the status tra_plan_create would fail with.
+ */
+tra_status tra_params_validate(const tra_shape* shape, const tra_params* params);
+
+/*
+ * Host-only radius table (step "budget -> radius", Intuition II and "Le
+ * Pipeline TRA"): with S = sum_{delta=-(T-1)}^{T-1} phi^(2|delta|) (the budget
+ * is spread over the disks of all frames) and r0^2(k) = exp(k/q)/(pi*S),
+ *   R2[k - k_lo][delta] = floor(r0^2(k) * phi^(2*delta)),  delta = 0..T-1,
+ * stored as -1 where delta >= 1 and the value is below 1 (frame inactive).
+ * r2 receives n_levels*T int32 (host memory, row-major); r0sq, if not NULL,
+ * n_levels doubles.  Query `*n_levels` first by passing r2 == NULL.
+ */
+tra_status tra_radius_table(const tra_shape* shape, const tra_params* params, int32_t* r2,
+                            double* r0sq, int32_t* n_levels, int32_t* k_lo);
+
+/*
+ * Build a plan from q and k (steps entropy -> level -> radius -> tile lists):
+ *   Kbar_b = mean of the keys of pool rectangle b, rounded once to the dtype;
+ *   H_i    = entropy of softmax_j(q_i . Kbar_{b(j)} / sqrt(d)) over all N keys;
+ *   k_i    = clamped level of H_i;
+ *   key tile Kb is listed for query tile Qa iff some query i in Qa retains some
+ *   key j in Kb: R2[k_i][|t_i-t_j|] >= 0 and
+ *   (h_i-h_j)^2 + (w_i-w_j)^2 <= R2[k_i][|t_i-t_j|].
+ * The CSR's columns are ascending key-tile ids (tile id = (t*ceil(H/tile_h) +
+ * h/tile_h)*ceil(W/tile_w) + w/tile_w) within each head.
+ * Synchronises `stream` once (to size the tile lists).  *out receives the plan.
+ */
+tra_status tra_plan_create(const tra_shape* shape, const tra_params* params, const void* q,
+                           const void* k, void* stream, tra_plan** out);
+
+/*
+ * Block-sparse attention with the plan's exact per-token mask:
+ *   O_i = sum_{j retained by i} softmax_j(q_i . k_j / sqrt(d)) v_j
+ * q, k, v, o: device [B, heads, N, d] of the plan's dtype; o must not alias
+ * q, k or v.  q and k may differ from the tensors the plan was built from (plan
+ * reuse).  Only listed tiles are visited.  The self key is always retained, so
+ * every row is well defined.
+ */
+tra_status tra_attention(const tra_plan* plan, const void* q, const void* k, const void* v,
+                         void* o, void* stream);
+
+/*
+ * Re-run the planning steps of tra_plan_create on new q and k into an existing
+ * plan (the refresh of a warm-up step), reusing its device buffers; the tile
+ * list buffer grows when needed.  The shape and parameters are the plan's.
+ * Synchronises `stream` once.  On failure the plan must not be used for
+ * attention until a rebuild succeeds.
+ */
+tra_status tra_plan_rebuild(tra_plan* plan, const void* q, const void* k, void* stream);
+
+/* TRA_OK if `shape` equals the plan's shape, else TRA_ERR_PLAN_MISMATCH.
+ * tra_attention trusts its caller on shapes; bindings call this first. */
+tra_status tra_plan_matches(const tra_plan* plan, const tra_shape* shape);
+
+tra_status tra_plan_get_info(const tra_plan* plan, tra_plan_info* info);
+
+/*
+ * Copy plan contents to HOST memory (any pointer may be NULL to skip):
+ *   levels   int16 [n_queries]            budget level k_i (-1 under override)
+ *   entropy  float [n_queries]            H_i (0 under override)
+ *   r2       int32 [n_levels*T]           radius table
+ *   row_ptr  int32 [n_rows + 1]           CSR offsets (global over all heads)
+ *   col_idx  int32 [nnz]                  key tile ids (per head)
+ *   kbar     [B*heads*n_pool*head_dim] of the dtype: pooled keys
+ * Synchronises `stream`.
+ */
+tra_status tra_plan_export(const tra_plan* plan, int16_t* levels, float* entropy, int32_t* r2,
+                           int32_t* row_ptr, int32_t* col_idx, void* kbar, void* stream);
+
+/*
+ * Exact pair counts of a plan (synchronises `stream`):
+ *   retained  sum over queries of the keys each retains (the FLOPs that count:
+ *             4*d per retained pair)
+ *   listed    sum over CSR entries of (valid queries x valid keys) of the pair
+ *             of tiles: the pairs a tile-granular kernel visits
+ */
+tra_status tra_plan_stats(const tra_plan* plan, int64_t* retained, int64_t* listed, void* stream);
+
+void tra_plan_destroy(tra_plan* plan);
+
+const char* tra_status_string(tra_status s);
+
+/* Message describing the last failing call on this thread ("" if none). */
+const char* tra_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRA_H */

@@ -1,0 +1,266 @@
+"""Token Radius Attention (TRA) on AMD Instinct MI355X.
+
+Thin Python binding over the C ABI of libtra.so (include/tra.h).  It only
+marshals arguments: every step of the hot path runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current stream.
+
+    plan = tra.plan(q, k, grid=(T, H, W), **params)   # entropy -> radius -> tile lists
+    o    = tra.attention(q, k, v, plan)                 # block-sparse masked attention
+
+q, k, v: contiguous [B, heads, T*H*W, d] CUDA tensors (bfloat16 or float32).
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = ["TraError", "Plan", "plan", "attention", "radius_table", "validate", "library_path",
+           "load_library", "DEFAULT_PARAMS", "EXPORTED_SYMBOLS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path():
+    return os.environ.get("TRA_LIBRARY", os.path.join(_HERE, "libtra.so"))
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("heads", ctypes.c_int32), ("T", ctypes.c_int32),
+                ("H", ctypes.c_int32), ("W", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class _Params(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_double), ("c", ctypes.c_double), ("budget_min", ctypes.c_double),
+                ("budget_max", ctypes.c_double), ("decay", ctypes.c_double),
+                ("radius_override", ctypes.c_double), ("levels_per_nat", ctypes.c_int32),
+                ("pool_h", ctypes.c_int32), ("pool_w", ctypes.c_int32), ("tile_h", ctypes.c_int32),
+                ("tile_w", ctypes.c_int32)]
+
+
+class _Info(ctypes.Structure):
+    _fields_ = [("n_queries", ctypes.c_int64), ("n_rows", ctypes.c_int64), ("nnz", ctypes.c_int64),
+                ("n_qtiles", ctypes.c_int32), ("n_pool", ctypes.c_int32),
+                ("n_levels", ctypes.c_int32), ("k_lo", ctypes.c_int32), ("T", ctypes.c_int32),
+                ("max_row_len", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_SIGS = {
+    "tra_params_validate": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.POINTER(_Params)]),
+    "tra_radius_table": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.POINTER(_Params), _P, _P,
+                                        ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]),
+    "tra_plan_create": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.POINTER(_Params), _P, _P, _P,
+                                       ctypes.POINTER(_P)]),
+    "tra_attention": (ctypes.c_int, [_P, _P, _P, _P, _P, _P]),
+    "tra_plan_rebuild": (ctypes.c_int, [_P, _P, _P, _P]),
+    "tra_plan_matches": (ctypes.c_int, [_P, ctypes.POINTER(_Shape)]),
+    "tra_plan_get_info": (ctypes.c_int, [_P, ctypes.POINTER(_Info)]),
+    "tra_plan_export": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P]),
+    "tra_plan_stats": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int64),
+                                      ctypes.POINTER(ctypes.c_int64), _P]),
+    "tra_plan_destroy": (None, [_P]),
+    "tra_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "tra_last_error": (ctypes.c_char_p, []),
+}
+EXPORTED_SYMBOLS = tuple(_SIGS)
+
+_lib = None
+
+
+def load_library():
+    """Loads libtra.so (raises if it has not been built: there is no fallback)."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with `python -m sparse_self_attention_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+class TraError(RuntimeError):
+    def __init__(self, status, fn):
+        lib = load_library()
+        self.status = status
+        self.name = lib.tra_status_string(status).decode()
+        super().__init__(f"{fn}: {self.name}: {lib.tra_last_error().decode()}")
+
+
+def _check(status, fn):
+    if status != 0:
+        raise TraError(status, fn)
+
+
+DEFAULT_PARAMS = dict(a=1.0, c=0.0, budget_min=16.0, budget_max=2048.0, decay=0.5,
+                      radius_override=-1.0, levels_per_nat=8, pool_h=16, pool_w=16,
+                      tile_h=8, tile_w=8)
+_DTYPES = {torch.bfloat16: 1, torch.float32: 0}
+
+
+def _make_params(params):
+    unknown = set(params) - set(DEFAULT_PARAMS)
+    if unknown:
+        raise TypeError(f"unknown TRA parameters: {sorted(unknown)}")
+    p = dict(DEFAULT_PARAMS)
+    p.update(params)
+    return _Params(**{k: (float(v) if isinstance(DEFAULT_PARAMS[k], float) else int(v)) for k, v in p.items()})
+
+
+def _make_shape(B, heads, grid, head_dim, dtype_code):
+    T, H, W = grid
+    return _Shape(B, heads, T, H, W, head_dim, dtype_code)
+
+
+def _shape_of(x, grid):
+    if x.dim() != 4:
+        raise ValueError("expected a [B, heads, T*H*W, d] tensor")
+    if x.dtype not in _DTYPES:
+        raise TypeError("dtype must be torch.bfloat16 or torch.float32")
+    T, H, W = grid
+    if x.shape[2] != T * H * W:
+        raise ValueError(f"token axis {x.shape[2]} != T*H*W = {T * H * W}")
+    return _make_shape(x.shape[0], x.shape[1], grid, x.shape[3], _DTYPES[x.dtype])
+
+
+def _dev_ptr(x, name):
+    if not x.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(x.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def validate(B, heads, grid, head_dim, dtype=torch.bfloat16, **params):
+    """Host-only check of a shape and parameter set; raises TraError if invalid."""
+    lib = load_library()
+    shape = _make_shape(B, heads, grid, head_dim, _DTYPES[dtype])
+    _check(lib.tra_params_validate(ctypes.byref(shape), ctypes.byref(_make_params(params))), "tra_params_validate")
+
+
+def radius_table(grid, dtype=torch.bfloat16, head_dim=128, **params):
+    """Host-only radius table: returns (R2 int32 [n_levels, T], r0^2 float64 [n_levels], k_lo)."""
+    import numpy as np
+    lib = load_library()
+    shape = _make_shape(1, 1, grid, head_dim, _DTYPES[dtype])
+    prm = _make_params(params)
+    n_levels, k_lo = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib.tra_radius_table(ctypes.byref(shape), ctypes.byref(prm), None, None,
+                                ctypes.byref(n_levels), ctypes.byref(k_lo)), "tra_radius_table")
+    r2 = np.zeros((n_levels.value, grid[0]), dtype=np.int32)
+    r0sq = np.zeros(n_levels.value, dtype=np.float64)
+    _check(lib.tra_radius_table(ctypes.byref(shape), ctypes.byref(prm), r2.ctypes.data_as(_P),
+                                r0sq.ctypes.data_as(_P), ctypes.byref(n_levels), ctypes.byref(k_lo)),
+           "tra_radius_table")
+    return r2, r0sq, k_lo.value
+
+
+class Plan:
+    """Owns a tra_plan.  Built by `plan(...)`; reusable across attention calls."""
+
+    def __init__(self, handle, shape, grid, params, device):
+        self._h = handle
+        self.shape = shape
+        self.grid = grid
+        self.params = params
+        self.device = device
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise RuntimeError("plan was destroyed")
+        return self._h
+
+    def info(self):
+        inf = _Info()
+        _check(load_library().tra_plan_get_info(self.handle, ctypes.byref(inf)), "tra_plan_get_info")
+        return {f: getattr(inf, f) for f, _ in _Info._fields_}
+
+    def rebuild(self, q, k):
+        """Re-plan from new q and k into the same buffers (a warm-up refresh)."""
+        for x, nm in ((q, "q"), (k, "k")):
+            self._check_tensor(x, nm)
+        _check(load_library().tra_plan_rebuild(self.handle, _dev_ptr(q, "q"), _dev_ptr(k, "k"),
+                                               _stream(self.device)), "tra_plan_rebuild")
+
+    def export(self):
+        """Host copies of the plan (numpy): levels, entropy, r2, row_ptr, col_idx, kbar."""
+        import numpy as np
+        inf = self.info()
+        levels = np.zeros(inf["n_queries"], dtype=np.int16)
+        entropy = np.zeros(inf["n_queries"], dtype=np.float32)
+        r2 = np.zeros((inf["n_levels"], inf["T"]), dtype=np.int32)
+        row_ptr = np.zeros(inf["n_rows"] + 1, dtype=np.int32)
+        col_idx = np.zeros(max(1, inf["nnz"]), dtype=np.int32)
+        s = self.shape
+        kb_dtype = np.uint16 if s.dtype == 1 else np.float32
+        kbar = np.zeros(s.B * s.heads * inf["n_pool"] * s.head_dim, dtype=kb_dtype)
+        _check(load_library().tra_plan_export(
+            self.handle, levels.ctypes.data_as(_P), entropy.ctypes.data_as(_P), r2.ctypes.data_as(_P),
+            row_ptr.ctypes.data_as(_P), col_idx.ctypes.data_as(_P), kbar.ctypes.data_as(_P),
+            _stream(self.device)), "tra_plan_export")
+        BH, N = s.B * s.heads, s.T * s.H * s.W
+        return {"levels": levels.reshape(BH, N), "entropy": entropy.reshape(BH, N), "r2": r2,
+                "row_ptr": row_ptr, "col_idx": col_idx[:inf["nnz"]],
+                "kbar": kbar.reshape(BH, inf["n_pool"], s.head_dim), "k_lo": inf["k_lo"],
+                "n_qtiles": inf["n_qtiles"]}
+
+    def stats(self):
+        """(retained pairs, listed pairs): exact counts over the whole plan."""
+        ret, lst = ctypes.c_int64(), ctypes.c_int64()
+        _check(load_library().tra_plan_stats(self.handle, ctypes.byref(ret), ctypes.byref(lst),
+                                             _stream(self.device)), "tra_plan_stats")
+        return ret.value, lst.value
+
+    def _check_tensor(self, x, name):
+        shape = _shape_of(x, self.grid)
+        st = load_library().tra_plan_matches(self.handle, ctypes.byref(shape))
+        if st != 0:
+            raise TraError(st, f"{name} vs plan")
+
+    def destroy(self):
+        if self._h is not None:
+            load_library().tra_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def plan(q, k, grid, **params):
+    """Builds a TRA plan from q and k ([B, heads, T*H*W, d] device tensors)."""
+    lib = load_library()
+    shape = _shape_of(q, grid)
+    if tuple(k.shape) != tuple(q.shape) or k.dtype != q.dtype:
+        raise ValueError("q and k must have the same shape and dtype")
+    prm = _make_params(params)
+    h = ctypes.c_void_p()
+    _check(lib.tra_plan_create(ctypes.byref(shape), ctypes.byref(prm), _dev_ptr(q, "q"),
+                               _dev_ptr(k, "k"), _stream(q.device), ctypes.byref(h)), "tra_plan_create")
+    return Plan(h, shape, tuple(grid), prm, q.device)
+
+
+def attention(q, k, v, plan, out=None):
+    """O = block-sparse masked softmax attention of q, k, v under `plan`."""
+    for x, nm in ((q, "q"), (k, "k"), (v, "v")):
+        plan._check_tensor(x, nm)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        plan._check_tensor(out, "out")
+    _check(load_library().tra_attention(plan.handle, _dev_ptr(q, "q"), _dev_ptr(k, "k"),
+                                        _dev_ptr(v, "v"), _dev_ptr(out, "out"), _stream(q.device)),
+           "tra_attention")
+    return out

@@ -1,0 +1,40 @@
+"""Builds libtra.so (the C-ABI library of the Token Radius Attention hot path)
+in-tree for gfx950 with hipcc.
+
+usage: python -m sparse_self_attention_amd.build
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(HERE, "libtra.so")
+SOURCES = [os.path.join(HERE, "csrc", "tra_api.cpp"), os.path.join(HERE, "csrc", "tra_kernels.hip")]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = os.environ.get("TRA_OFFLOAD_ARCH", "gfx950")
+
+
+def command(out=LIB):
+    return [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+            # packed fp32 VALU forms are kept out of every kernel
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
+            "-o", out] + SOURCES
+
+
+def build(verbose=True):
+    tmp = LIB + ".tmp"
+    cmd = command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building libtra.so")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build()

@@ -1,0 +1,389 @@
+// Host side of the C ABI declared in include/tra.h: validation, the radius
+// table, plan ownership and kernel sequencing.  Every step of the path itself
+// runs in the kernels of tra_kernels.hip.
+#include "tra.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "tra_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+tra_status fail(tra_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+#define TRA_HIP(call)                                                                    \
+  do {                                                                                   \
+    hipError_t e_ = (call);                                                              \
+    if (e_ != hipSuccess) {                                                              \
+      if (e_ == hipErrorOutOfMemory)                                                     \
+        return fail(TRA_ERR_OOM, std::string(#call) + ": " + hipGetErrorString(e_));     \
+      return fail(TRA_ERR_HIP, std::string(#call) + ": " + hipGetErrorString(e_));       \
+    }                                                                                    \
+  } while (0)
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+// Level range and radius table, fp64 on the host.
+struct Table {
+  int k_lo = 0, k_hi = 0, n_levels = 0;
+  std::vector<double> r0sq;     // per level row
+  std::vector<int32_t> r2;      // n_levels x T, -1 = inactive frame
+  std::vector<int32_t> dmax;    // largest active delta per row
+};
+
+tra_status check_shape(const tra_shape* s) {
+  if (!s) return fail(TRA_ERR_INVALID_ARG, "shape is NULL");
+  if (s->B < 1 || s->heads < 1 || s->T < 1 || s->H < 1 || s->W < 1)
+    return fail(TRA_ERR_SHAPE, "B, heads, T, H and W must be >= 1");
+  if (s->H > 32767 || s->W > 32767 || s->T > 32767)
+    return fail(TRA_ERR_SHAPE, "T, H and W must be <= 32767");
+  const int64_t N = static_cast<int64_t>(s->T) * s->H * s->W;
+  if (static_cast<int64_t>(s->B) * s->heads * N >= (int64_t(1) << 31))
+    return fail(TRA_ERR_SHAPE, "B*heads*T*H*W must be below 2^31");
+  if (s->dtype != TRA_F32 && s->dtype != TRA_BF16) return fail(TRA_ERR_DTYPE, "dtype must be TRA_F32 or TRA_BF16");
+  if (s->head_dim != 64 && s->head_dim != 128) return fail(TRA_ERR_DTYPE, "head_dim must be 64 or 128");
+  return TRA_OK;
+}
+
+tra_status check_params(const tra_shape* s, const tra_params* p, Table* tab) {
+  if (!p) return fail(TRA_ERR_INVALID_ARG, "params is NULL");
+  if (!std::isfinite(p->a) || !std::isfinite(p->c)) return fail(TRA_ERR_INVALID_ARG, "a and c must be finite");
+  if (!(p->budget_min > 0.0) || !std::isfinite(p->budget_max) || !(p->budget_max >= p->budget_min))
+    return fail(TRA_ERR_INVALID_ARG, "need 0 < budget_min <= budget_max < inf");
+  if (!(p->decay > 0.0 && p->decay <= 1.0)) return fail(TRA_ERR_INVALID_ARG, "decay must lie in (0, 1]");
+  if (p->levels_per_nat < 1 || p->levels_per_nat > 1024)
+    return fail(TRA_ERR_INVALID_ARG, "levels_per_nat must lie in [1, 1024]");
+  if (p->pool_h < 1 || p->pool_w < 1) return fail(TRA_ERR_INVALID_ARG, "pool_h and pool_w must be >= 1");
+  if (p->tile_h != 8 || p->tile_w != 8)
+    return fail(TRA_ERR_INVALID_ARG, "the device kernels use 8x8 tiles (tile_h = tile_w = 8)");
+  if (!std::isfinite(p->radius_override) || p->radius_override >= 32768.0)
+    return fail(TRA_ERR_INVALID_ARG, "radius_override must be finite and below 32768");
+  const int T = s->T;
+  const double phi = p->decay;
+  Table t;
+  if (p->radius_override >= 0.0) {
+    t.k_lo = -1;
+    t.k_hi = -1;
+    t.n_levels = 1;
+    t.r0sq.push_back(p->radius_override * p->radius_override);
+  } else {
+    const double q = p->levels_per_nat;
+    const double klo = std::ceil(q * std::log(p->budget_min));
+    const double khi = std::floor(q * std::log(p->budget_max));
+    if (!(klo <= khi)) return fail(TRA_ERR_INVALID_ARG, "budget range holds no quantisation level");
+    if (khi - klo + 1 > 4096) return fail(TRA_ERR_INVALID_ARG, "more than 4096 budget levels");
+    if (std::fabs(klo) > 30000 || std::fabs(khi) > 30000)
+      return fail(TRA_ERR_INVALID_ARG, "budget levels do not fit int16");
+    t.k_lo = static_cast<int>(klo);
+    t.k_hi = static_cast<int>(khi);
+    t.n_levels = t.k_hi - t.k_lo + 1;
+    // S = sum over delta in [-(T-1), T-1] of phi^(2|delta|): every frame's disk
+    // shares the budget, with area shrinking by phi^2 per frame of distance.
+    double S = 0.0;
+    for (int dl = -(T - 1); dl <= T - 1; ++dl) S += std::pow(phi, 2.0 * std::abs(dl));
+    for (int k = t.k_lo; k <= t.k_hi; ++k) t.r0sq.push_back(std::exp(k / q) / (M_PI * S));
+  }
+  if (t.r0sq.back() >= 1073741824.0) return fail(TRA_ERR_INVALID_ARG, "radius^2 must stay below 2^30");
+  if (static_cast<int64_t>(t.n_levels) * T > (int64_t(1) << 22))
+    return fail(TRA_ERR_INVALID_ARG, "radius table too large");
+  t.r2.resize(static_cast<size_t>(t.n_levels) * T);
+  t.dmax.resize(t.n_levels);
+  for (int r = 0; r < t.n_levels; ++r) {
+    int dm = 0;
+    for (int dl = 0; dl < T; ++dl) {
+      const double x = t.r0sq[r] * std::pow(phi, 2.0 * dl);
+      int32_t v = static_cast<int32_t>(std::floor(x));
+      if (dl > 0 && v < 1) v = -1;
+      if (v >= 0) dm = dl;
+      t.r2[static_cast<size_t>(r) * T + dl] = v;
+    }
+    t.dmax[r] = dm;
+  }
+  if (tab) *tab = std::move(t);
+  return TRA_OK;
+}
+
+size_t dtype_size(int dtype) { return dtype == TRA_BF16 ? 2 : 4; }
+
+}  // namespace
+
+struct tra_plan {
+  tra_shape shape;
+  tra_params params;
+  Table table;
+  tra::Grid pool, tiles;
+  int BH = 0;
+  int64_t N = 0, n_queries = 0, n_rows = 0;
+  int row_base = 0;
+  int device = 0;
+  // device buffers
+  void* kbar = nullptr;
+  float* H = nullptr;
+  int16_t* lv = nullptr;
+  int32_t* r2 = nullptr;
+  int32_t* dmax = nullptr;
+  float* pool_w = nullptr;
+  int32_t* counts = nullptr;
+  int32_t* row_ptr = nullptr;
+  int32_t* col_idx = nullptr;
+  int64_t col_cap = 0;
+  int64_t* totals = nullptr;      // device: nnz, longest row, overflow flag
+  int64_t* totals_host = nullptr; // pinned
+  int64_t nnz = 0;
+  int32_t max_row_len = 0;
+};
+
+namespace {
+
+void release(tra_plan* p) {
+  if (!p) return;
+  void* bufs[] = {p->kbar, p->H, p->lv, p->r2, p->dmax, p->pool_w, p->counts, p->row_ptr, p->col_idx, p->totals};
+  for (void* b : bufs)
+    if (b) (void)hipFree(b);
+  if (p->totals_host) (void)hipHostFree(p->totals_host);
+  delete p;
+}
+
+// Steps entropy -> level -> tile lists into the plan's buffers.
+tra_status build(tra_plan* p, const void* q, const void* k, hipStream_t st) {
+  const tra_shape& s = p->shape;
+  const int d = s.head_dim;
+  if (p->params.radius_override < 0.0) {
+    TRA_HIP(tra::launch_pool(s.dtype, d, k, p->kbar, p->BH, p->pool, st));
+    tra::EntropyArgs ea{p->params.a, p->params.c, p->params.levels_per_nat, p->table.k_lo, p->table.k_hi};
+    TRA_HIP(tra::launch_entropy(s.dtype, d, q, p->kbar, p->pool_w, p->BH, static_cast<int>(p->N),
+                                p->pool.count, ea, p->H, p->lv, st));
+  } else {
+    TRA_HIP(tra::launch_fill_levels(p->lv, p->H, p->n_queries, st));
+  }
+  TRA_HIP(tra::launch_csr_count(p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, p->counts, st));
+  TRA_HIP(tra::launch_scan(p->counts, p->n_rows, p->row_ptr, p->totals, st));
+  TRA_HIP(hipMemcpyAsync(p->totals_host, p->totals, 3 * sizeof(int64_t), hipMemcpyDeviceToHost, st));
+  TRA_HIP(hipStreamSynchronize(st));
+  if (p->totals_host[2]) return fail(TRA_ERR_OVERFLOW, "CSR has 2^31 or more entries");
+  p->nnz = p->totals_host[0];
+  p->max_row_len = static_cast<int32_t>(p->totals_host[1]);
+  if (p->nnz > p->col_cap) {
+    if (p->col_idx) TRA_HIP(hipFree(p->col_idx));
+    p->col_idx = nullptr;
+    p->col_cap = 0;
+    const int64_t cap = p->nnz + p->nnz / 8 + 64;
+    TRA_HIP(hipMalloc(&p->col_idx, cap * sizeof(int32_t)));
+    p->col_cap = cap;
+  }
+  TRA_HIP(tra::launch_csr_fill(p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, p->row_ptr,
+                               p->col_idx, st));
+  return TRA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tra_status tra_params_validate(const tra_shape* shape, const tra_params* params) {
+  tra_status st = check_shape(shape);
+  if (st != TRA_OK) return st;
+  return check_params(shape, params, nullptr);
+}
+
+tra_status tra_radius_table(const tra_shape* shape, const tra_params* params, int32_t* r2,
+                            double* r0sq, int32_t* n_levels, int32_t* k_lo) {
+  tra_status st = check_shape(shape);
+  if (st != TRA_OK) return st;
+  Table t;
+  st = check_params(shape, params, &t);
+  if (st != TRA_OK) return st;
+  if (n_levels) *n_levels = t.n_levels;
+  if (k_lo) *k_lo = t.k_lo;
+  if (r2) std::memcpy(r2, t.r2.data(), t.r2.size() * sizeof(int32_t));
+  if (r0sq) std::memcpy(r0sq, t.r0sq.data(), t.r0sq.size() * sizeof(double));
+  return TRA_OK;
+}
+
+tra_status tra_plan_create(const tra_shape* shape, const tra_params* params, const void* q,
+                           const void* k, void* stream, tra_plan** out) {
+  if (!out) return fail(TRA_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  tra_status st = check_shape(shape);
+  if (st != TRA_OK) return st;
+  Table tab;
+  st = check_params(shape, params, &tab);
+  if (st != TRA_OK) return st;
+  if (!q || !k) return fail(TRA_ERR_INVALID_ARG, "q and k must be device pointers");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k)) & 15)
+    return fail(TRA_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+
+  tra_plan* p = new tra_plan();
+  p->shape = *shape;
+  p->params = *params;
+  p->table = std::move(tab);
+  p->BH = shape->B * shape->heads;
+  p->N = static_cast<int64_t>(shape->T) * shape->H * shape->W;
+  p->n_queries = p->BH * p->N;
+  p->pool = tra::make_grid(shape->T, shape->H, shape->W, params->pool_h, params->pool_w);
+  p->tiles = tra::make_grid(shape->T, shape->H, shape->W, params->tile_h, params->tile_w);
+  p->n_rows = static_cast<int64_t>(p->BH) * p->tiles.count;
+  p->row_base = params->radius_override >= 0.0 ? -1 : p->table.k_lo;
+
+  auto fin = [&](tra_status s2) {
+    if (s2 != TRA_OK) release(p);
+    return s2;
+  };
+#define TRA_HIP_P(call)                                                                       \
+  do {                                                                                        \
+    hipError_t e_ = (call);                                                                   \
+    if (e_ != hipSuccess)                                                                     \
+      return fin(fail(e_ == hipErrorOutOfMemory ? TRA_ERR_OOM : TRA_ERR_HIP,                  \
+                      std::string(#call) + ": " + hipGetErrorString(e_)));                     \
+  } while (0)
+
+  TRA_HIP_P(hipGetDevice(&p->device));
+  const size_t es = dtype_size(shape->dtype);
+  TRA_HIP_P(hipMalloc(&p->kbar, static_cast<size_t>(p->BH) * p->pool.count * shape->head_dim * es));
+  TRA_HIP_P(hipMalloc(&p->H, p->n_queries * sizeof(float)));
+  TRA_HIP_P(hipMalloc(&p->lv, p->n_queries * sizeof(int16_t)));
+  TRA_HIP_P(hipMalloc(&p->r2, p->table.r2.size() * sizeof(int32_t)));
+  TRA_HIP_P(hipMalloc(&p->dmax, p->table.dmax.size() * sizeof(int32_t)));
+  TRA_HIP_P(hipMalloc(&p->pool_w, static_cast<size_t>(p->pool.count) * sizeof(float)));
+  TRA_HIP_P(hipMalloc(&p->counts, p->n_rows * sizeof(int32_t)));
+  TRA_HIP_P(hipMalloc(&p->row_ptr, (p->n_rows + 1) * sizeof(int32_t)));
+  TRA_HIP_P(hipMalloc(&p->totals, 4 * sizeof(int64_t)));
+  TRA_HIP_P(hipHostMalloc(&p->totals_host, 4 * sizeof(int64_t)));
+  if (params->radius_override >= 0.0)
+    TRA_HIP_P(hipMemsetAsync(p->kbar, 0, static_cast<size_t>(p->BH) * p->pool.count * shape->head_dim * es, hs));
+
+  std::vector<float> w(p->pool.count);
+  for (int b = 0; b < p->pool.count; ++b) {
+    const int rem = b % p->pool.per_frame;
+    const int h0 = (rem / p->pool.nw) * p->pool.th, w0 = (rem % p->pool.nw) * p->pool.tw;
+    w[b] = static_cast<float>(std::min(p->pool.th, shape->H - h0) * std::min(p->pool.tw, shape->W - w0));
+  }
+  TRA_HIP_P(hipMemcpy(p->r2, p->table.r2.data(), p->table.r2.size() * sizeof(int32_t), hipMemcpyHostToDevice));
+  TRA_HIP_P(hipMemcpy(p->dmax, p->table.dmax.data(), p->table.dmax.size() * sizeof(int32_t), hipMemcpyHostToDevice));
+  TRA_HIP_P(hipMemcpy(p->pool_w, w.data(), w.size() * sizeof(float), hipMemcpyHostToDevice));
+#undef TRA_HIP_P
+  st = build(p, q, k, hs);
+  if (st != TRA_OK) return fin(st);
+  *out = p;
+  return TRA_OK;
+}
+
+tra_status tra_attention(const tra_plan* plan, const void* q, const void* k, const void* v,
+                         void* o, void* stream) {
+  if (!plan) return fail(TRA_ERR_INVALID_ARG, "plan is NULL");
+  if (!q || !k || !v || !o) return fail(TRA_ERR_INVALID_ARG, "q, k, v and o must be device pointers");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) |
+       reinterpret_cast<uintptr_t>(o)) & 15)
+    return fail(TRA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+  if (o == q || o == k || o == v) return fail(TRA_ERR_INVALID_ARG, "o must not alias q, k or v");
+  const tra_shape& s = plan->shape;
+  TRA_HIP(tra::launch_attention(s.dtype, s.head_dim, q, k, v, o, plan->lv, plan->r2, plan->row_base,
+                                plan->BH, plan->tiles, plan->row_ptr, plan->col_idx,
+                                static_cast<hipStream_t>(stream)));
+  return TRA_OK;
+}
+
+tra_status tra_plan_rebuild(tra_plan* plan, const void* q, const void* k, void* stream) {
+  if (!plan) return fail(TRA_ERR_INVALID_ARG, "plan is NULL");
+  if (!q || !k) return fail(TRA_ERR_INVALID_ARG, "q and k must be device pointers");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k)) & 15)
+    return fail(TRA_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
+  return build(plan, q, k, static_cast<hipStream_t>(stream));
+}
+
+tra_status tra_plan_matches(const tra_plan* plan, const tra_shape* shape) {
+  if (!plan || !shape) return fail(TRA_ERR_INVALID_ARG, "plan and shape must not be NULL");
+  const tra_shape& s = plan->shape;
+  if (s.B != shape->B || s.heads != shape->heads || s.T != shape->T || s.H != shape->H ||
+      s.W != shape->W || s.head_dim != shape->head_dim || s.dtype != shape->dtype)
+    return fail(TRA_ERR_PLAN_MISMATCH, "tensor shape or dtype differs from the plan's");
+  return TRA_OK;
+}
+
+tra_status tra_plan_get_info(const tra_plan* plan, tra_plan_info* info) {
+  if (!plan || !info) return fail(TRA_ERR_INVALID_ARG, "plan and info must not be NULL");
+  info->n_queries = plan->n_queries;
+  info->n_rows = plan->n_rows;
+  info->nnz = plan->nnz;
+  info->n_qtiles = plan->tiles.count;
+  info->n_pool = plan->pool.count;
+  info->n_levels = plan->table.n_levels;
+  info->k_lo = plan->table.k_lo;
+  info->T = plan->shape.T;
+  info->max_row_len = plan->max_row_len;
+  return TRA_OK;
+}
+
+tra_status tra_plan_export(const tra_plan* plan, int16_t* levels, float* entropy, int32_t* r2,
+                           int32_t* row_ptr, int32_t* col_idx, void* kbar, void* stream) {
+  if (!plan) return fail(TRA_ERR_INVALID_ARG, "plan is NULL");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  TRA_HIP(hipStreamSynchronize(hs));
+  if (levels) TRA_HIP(hipMemcpy(levels, plan->lv, plan->n_queries * sizeof(int16_t), hipMemcpyDeviceToHost));
+  if (entropy) TRA_HIP(hipMemcpy(entropy, plan->H, plan->n_queries * sizeof(float), hipMemcpyDeviceToHost));
+  if (r2) std::memcpy(r2, plan->table.r2.data(), plan->table.r2.size() * sizeof(int32_t));
+  if (row_ptr) TRA_HIP(hipMemcpy(row_ptr, plan->row_ptr, (plan->n_rows + 1) * sizeof(int32_t), hipMemcpyDeviceToHost));
+  if (col_idx && plan->nnz > 0)
+    TRA_HIP(hipMemcpy(col_idx, plan->col_idx, plan->nnz * sizeof(int32_t), hipMemcpyDeviceToHost));
+  if (kbar)
+    TRA_HIP(hipMemcpy(kbar, plan->kbar,
+                      static_cast<size_t>(plan->BH) * plan->pool.count * plan->shape.head_dim *
+                          dtype_size(plan->shape.dtype),
+                      hipMemcpyDeviceToHost));
+  return TRA_OK;
+}
+
+tra_status tra_plan_stats(const tra_plan* plan, int64_t* retained, int64_t* listed, void* stream) {
+  if (!plan) return fail(TRA_ERR_INVALID_ARG, "plan is NULL");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  unsigned long long* dev = nullptr;
+  TRA_HIP(hipMalloc(&dev, 2 * sizeof(unsigned long long)));
+  unsigned long long host[2] = {0, 0};
+  hipError_t e = hipMemsetAsync(dev, 0, 2 * sizeof(unsigned long long), hs);
+  if (e == hipSuccess)
+    e = tra::launch_stats(plan->lv, plan->r2, plan->shape.T, plan->row_base, plan->BH, plan->tiles,
+                          plan->row_ptr, plan->col_idx, dev, hs);
+  if (e == hipSuccess) e = hipMemcpyAsync(host, dev, sizeof(host), hipMemcpyDeviceToHost, hs);
+  if (e == hipSuccess) e = hipStreamSynchronize(hs);
+  (void)hipFree(dev);
+  if (e != hipSuccess) return fail(TRA_ERR_HIP, std::string("tra_plan_stats: ") + hipGetErrorString(e));
+  if (retained) *retained = static_cast<int64_t>(host[0]);
+  if (listed) *listed = static_cast<int64_t>(host[1]);
+  return TRA_OK;
+}
+
+void tra_plan_destroy(tra_plan* plan) {
+  if (!plan) return;
+  (void)hipDeviceSynchronize();
+  release(plan);
+}
+
+const char* tra_status_string(tra_status s) {
+  switch (s) {
+    case TRA_OK: return "TRA_OK";
+    case TRA_ERR_INVALID_ARG: return "TRA_ERR_INVALID_ARG";
+    case TRA_ERR_SHAPE: return "TRA_ERR_SHAPE";
+    case TRA_ERR_DTYPE: return "TRA_ERR_DTYPE";
+    case TRA_ERR_PLAN_MISMATCH: return "TRA_ERR_PLAN_MISMATCH";
+    case TRA_ERR_OOM: return "TRA_ERR_OOM";
+    case TRA_ERR_OVERFLOW: return "TRA_ERR_OVERFLOW";
+    case TRA_ERR_HIP: return "TRA_ERR_HIP";
+  }
+  return "TRA_ERR_UNKNOWN";
+}
+
+const char* tra_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// Internal declarations shared by the host API (tra_api.cpp) and the kernels
+// (tra_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tra {
+
+// Geometry of one head's T x H x W grid cut into th x tw rectangles per frame.
+struct Grid {
+  int T, H, W;
+  int th, tw;     // rectangle size
+  int nh, nw;     // rectangles per frame along h and w (ceil)
+  int per_frame;  // nh * nw
+  int count;      // T * per_frame
+};
+
+inline Grid make_grid(int T, int H, int W, int th, int tw) {
+  Grid g;
+  g.T = T; g.H = H; g.W = W; g.th = th; g.tw = tw;
+  g.nh = (H + th - 1) / th;
+  g.nw = (W + tw - 1) / tw;
+  g.per_frame = g.nh * g.nw;
+  g.count = T * g.per_frame;
+  return g;
+}
+
+struct EntropyArgs {
+  double a, c;
+  int levels_per_nat, k_lo, k_hi;
+};
+
+// Launchers (tra_kernels.hip).  All enqueue on `s` and return the launch status.
+hipError_t launch_pool(int dtype, int d, const void* k, void* kbar, int BH, const Grid& pool,
+                       hipStream_t s);
+hipError_t launch_entropy(int dtype, int d, const void* q, const void* kbar, const float* pool_w,
+                          int BH, int N, int n_pool, const EntropyArgs& ea, float* H_out,
+                          int16_t* lv_out, hipStream_t s);
+hipError_t launch_fill_levels(int16_t* lv, float* H, int64_t n, hipStream_t s);
+hipError_t launch_csr_count(const int16_t* lv, const int32_t* r2, const int32_t* dmax, int T,
+                            int row_base, int BH, const Grid& tiles, int32_t* counts,
+                            hipStream_t s);
+hipError_t launch_scan(const int32_t* counts, int64_t n_rows, int32_t* row_ptr,
+                       int64_t* totals, hipStream_t s);
+hipError_t launch_csr_fill(const int16_t* lv, const int32_t* r2, const int32_t* dmax, int T,
+                           int row_base, int BH, const Grid& tiles, const int32_t* row_ptr,
+                           int32_t* col_idx, hipStream_t s);
+hipError_t launch_attention(int dtype, int d, const void* q, const void* k, const void* v,
+                            void* o, const int16_t* lv, const int32_t* r2, int row_base,
+                            int BH, const Grid& tiles, const int32_t* row_ptr,
+                            const int32_t* col_idx, hipStream_t s);
+hipError_t launch_stats(const int16_t* lv, const int32_t* r2, int T, int row_base, int BH,
+                        const Grid& tiles, const int32_t* row_ptr, const int32_t* col_idx,
+                        unsigned long long* out2, hipStream_t s);
+
+}  // namespace tra

@@ -1,0 +1,105 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+The library must load, export every function include/tra.h declares, reject bad
+shapes and parameters with the documented status codes, and compute the same
+radius table as the oracle, bit for bit.
+"""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import sparse_self_attention_amd as tra
+from workloads import CONFIGS, small_workload
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "tra.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(tra_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    lib = tra.load_library()
+    declared = _declared_functions()
+    assert len(declared) >= 12
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(tra.EXPORTED_SYMBOLS)
+
+
+def test_status_strings():
+    lib = tra.load_library()
+    assert lib.tra_status_string(0) == b"TRA_OK"
+    assert lib.tra_status_string(4) == b"TRA_ERR_PLAN_MISMATCH"
+
+
+def _validate(**kw):
+    shape = dict(B=1, heads=2, grid=(4, 9, 10), head_dim=128, dtype=torch.bfloat16)
+    params = {}
+    for k, v in kw.items():
+        if k in shape:
+            shape[k] = v
+        else:
+            params[k] = v
+    return tra.validate(shape["B"], shape["heads"], shape["grid"], shape["head_dim"], shape["dtype"], **params)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), "TRA_ERR_DTYPE"),
+    (dict(grid=(0, 4, 4)), "TRA_ERR_SHAPE"),
+    (dict(B=0), "TRA_ERR_SHAPE"),
+    (dict(decay=0.0), "TRA_ERR_INVALID_ARG"),
+    (dict(decay=1.5), "TRA_ERR_INVALID_ARG"),
+    (dict(budget_min=0.0), "TRA_ERR_INVALID_ARG"),
+    (dict(budget_min=100.0, budget_max=50.0), "TRA_ERR_INVALID_ARG"),
+    (dict(budget_min=17.0, budget_max=17.5), "TRA_ERR_INVALID_ARG"),  # no level inside
+    (dict(levels_per_nat=0), "TRA_ERR_INVALID_ARG"),
+    (dict(pool_h=0), "TRA_ERR_INVALID_ARG"),
+    (dict(tile_h=4, tile_w=16), "TRA_ERR_INVALID_ARG"),
+    (dict(a=math.inf), "TRA_ERR_INVALID_ARG"),
+    (dict(radius_override=1e9), "TRA_ERR_INVALID_ARG"),
+    (dict(budget_max=1e12), "TRA_ERR_INVALID_ARG"),
+])
+def test_validation_rejects(kw, code):
+    with pytest.raises(tra.TraError) as ei:
+        _validate(**kw)
+    assert ei.value.name == code
+
+
+def test_validation_accepts_every_workload():
+    for cfg in CONFIGS.values():
+        dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        tra.validate(cfg.batch, cfg.heads, (cfg.T, cfg.H, cfg.W), cfg.head_dim, dt, **cfg.params())
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_radius_table_matches_oracle(name):
+    cfg = CONFIGS[name]
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    r2, r0sq, k_lo = tra.radius_table((cfg.T, cfg.H, cfg.W), dt, cfg.head_dim, **cfg.params())
+    ref = O.radius_table(cfg.params(), cfg.T)
+    assert k_lo == O.level_range(cfg.params())[0]
+    assert np.array_equal(r2.astype(np.int64), ref)
+
+
+@pytest.mark.parametrize("r", [0.0, 1.0, 2.5, 7.0, 40.0])
+@pytest.mark.parametrize("decay", [1.0, 0.5, 0.35])
+def test_radius_table_override_matches_oracle(r, decay):
+    cfg = small_workload(T=9, radius_override=r, decay=decay)
+    r2, _, k_lo = tra.radius_table((cfg.T, cfg.H, cfg.W), torch.bfloat16, 128, **cfg.params())
+    assert k_lo == -1
+    assert np.array_equal(r2.astype(np.int64), O.radius_table(cfg.params(), cfg.T))
+
+
+def test_binding_rejects_host_tensors():
+    q = torch.zeros((1, 1, 8 * 8, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        tra.plan(q, q, grid=(1, 8, 8))

@@ -1,0 +1,180 @@
+"""GPU parity of the HIP path against the fp64 oracle (through the C ABI)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import sparse_self_attention_amd as tra
+from workloads import CONFIGS, make_inputs, perturb, small_workload
+
+from parity_util import check_csr_properties, check_head, gpu_run
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def test_tiny_workload_full_parity(gpu):
+    cfg = CONFIGS["tiny"]
+    _say("case: tiny fp32", cfg)
+    run = gpu_run(cfg, gpu)
+    for h in range(cfg.heads):
+        m = check_head(cfg, run, 0, h)
+        _say("head", h, {k: v for k, v in m.items() if k not in ("excused", "level_mismatch")},
+             "excused", len(m["excused"]), "mismatch", len(m["level_mismatch"]))
+        assert m["o_max_abs"] < 1e-4  # fp32 path
+
+
+@pytest.mark.parametrize("shape", [(3, 13, 21, 128), (2, 17, 9, 64), (4, 8, 8, 128), (1, 30, 37, 128)])
+def test_small_bf16_full_parity(gpu, shape):
+    T, H, W, d = shape
+    cfg = small_workload(T=T, H=H, W=W, heads=2, head_dim=d, c=-0.5, budget_max=float(T * H * W))
+    _say("case: small bf16", shape)
+    run = gpu_run(cfg, gpu)
+    check_csr_properties(cfg, run)
+    for h in range(cfg.heads):
+        m = check_head(cfg, run, 0, h)
+        _say("head", h, m["o_max_abs"], m["o_mean_abs"], m.get("entropy_max_abs_err"),
+             "excused", len(m.get("excused", [])))
+
+
+def test_small_fp32_d128_parity(gpu):
+    cfg = small_workload(T=2, H=11, W=19, heads=1, head_dim=128, dtype="fp32", budget_max=418.0)
+    _say("case: small fp32 d128")
+    run = gpu_run(cfg, gpu)
+    m = check_head(cfg, run, 0, 0)
+    assert m["o_max_abs"] < 1e-4
+
+
+def test_batch_of_two(gpu):
+    cfg = small_workload(T=2, H=9, W=12, heads=2, batch=2, c=-0.25, budget_max=216.0)
+    _say("case: batch 2")
+    run = gpu_run(cfg, gpu)
+    for b in range(2):
+        for h in range(2):
+            check_head(cfg, run, b, h)
+
+
+def test_degenerate_grids(gpu):
+    for (T, H, W) in [(1, 1, 1), (1, 1, 5), (2, 3, 2), (1, 7, 1)]:
+        cfg = small_workload(T=T, H=H, W=W, heads=1, head_dim=64, pool_h=2, pool_w=2,
+                             budget_min=1.0, budget_max=max(1.0, float(T * H * W)))
+        _say("case: degenerate", (T, H, W))
+        run = gpu_run(cfg, gpu)
+        check_head(cfg, run, 0, 0)
+
+
+def test_radius_zero_returns_own_value(gpu):
+    cfg = small_workload(T=3, H=10, W=12, heads=2, radius_override=0.0)
+    _say("case: radius 0")
+    run = gpu_run(cfg, gpu)
+    assert torch.equal(run["o"], run["v"])
+    for h in range(2):
+        check_head(cfg, run, 0, h)
+
+
+def test_dense_limit_matches_dense_attention(gpu):
+    T, H, W = 2, 9, 11
+    cfg = small_workload(T=T, H=H, W=W, heads=1, radius_override=math.hypot(H - 1, W - 1) + 0.01,
+                         decay=1.0)
+    _say("case: dense limit")
+    run = gpu_run(cfg, gpu)
+    assert run["plan"].info()["nnz"] == (T * 2 * 2) ** 2  # every tile pair listed
+    q, k, v = (run[x][0, 0].double().cpu().numpy() for x in "qkv")
+    ref = O.dense_attention(q, k, v)
+    err = np.abs(run["o"][0, 0].double().cpu().numpy() - ref)
+    _say("dense", err.max(), err.mean())
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3
+
+
+def test_stats_match_oracle_counts(gpu):
+    cfg = small_workload(T=3, H=13, W=21, heads=2, c=-0.5, budget_max=819.0)
+    run = gpu_run(cfg, gpu)
+    retained, listed = run["plan"].stats()
+    exp = run["export"]
+    R2 = O.radius_table(cfg.params(), cfg.T)
+    ref = sum(int(O.retained_counts(exp["levels"][bh].astype(np.int64), R2, cfg.T, cfg.H, cfg.W,
+                                    cfg.params()).sum()) for bh in range(cfg.heads))
+    assert retained == ref
+    tiles = O.Geometry(cfg.T, cfg.H, cfg.W, 8, 8)
+    sizes = tiles.block_sizes()
+    rp, ci = exp["row_ptr"], exp["col_idx"]
+    ref_listed = sum(int(sizes[r % tiles.count]) * int(sizes[ci[e]])
+                     for r in range(len(rp) - 1) for e in range(rp[r], rp[r + 1]))
+    assert listed == ref_listed
+
+
+def test_rebuild_equals_create(gpu):
+    cfg = small_workload(T=3, H=13, W=21, heads=2, c=-0.5, budget_max=819.0)
+    q, k, v = make_inputs(cfg, device=gpu)
+    p1 = tra.plan(q, k, grid=(cfg.T, cfg.H, cfg.W), **cfg.params())
+    q2, k2 = perturb(q, 2, 0, rel=0.5), perturb(k, 2, 1, rel=0.5)
+    p1.rebuild(q2, k2)
+    p2 = tra.plan(q2, k2, grid=(cfg.T, cfg.H, cfg.W), **cfg.params())
+    e1, e2 = p1.export(), p2.export()
+    for key in ("levels", "row_ptr", "col_idx", "kbar"):
+        assert np.array_equal(e1[key], e2[key]), key
+
+
+def test_plan_mismatch_rejected(gpu):
+    cfg = small_workload(T=2, H=8, W=8, heads=1)
+    q, k, v = make_inputs(cfg, device=gpu)
+    plan = tra.plan(q, k, grid=(cfg.T, cfg.H, cfg.W), **cfg.params())
+    q2 = torch.zeros((1, 2, cfg.N, 128), dtype=torch.bfloat16, device=gpu)
+    with pytest.raises(tra.TraError) as ei:
+        tra.attention(q2, q2, q2, plan)
+    assert ei.value.name == "TRA_ERR_PLAN_MISMATCH"
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads, in the launch configuration the benchmark times:
+# every head runs on the GPU; two heads are compared against the oracle (all
+# levels, sampled tile lists and sampled outputs), the rest by properties.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["wan21_1p3b_480p", "wan21_14b_720p", "hunyuan_720p", "long_video_2x"])
+def test_full_size_workload(gpu, name):
+    cfg = CONFIGS[name]
+    _say("case: full size", name)
+    run = gpu_run(cfg, gpu)
+    check_csr_properties(cfg, run)
+    assert torch.isfinite(run["o"].float()).all()
+    rng = np.random.default_rng(11)
+    tiles = O.Geometry(cfg.T, cfg.H, cfg.W, 8, 8)
+    excused = 0
+    for h in (0, cfg.heads - 1):
+        tile_sample = rng.choice(tiles.count, size=12, replace=False)
+        tile_sample = np.concatenate([tile_sample, [0, tiles.count - 1]])  # corners incl. ragged
+        qs = np.concatenate([rng.choice(cfg.N, size=48, replace=False), [0, cfg.N - 1]])
+        m = check_head(cfg, run, 0, h, tile_sample=tile_sample, query_sample=qs)
+        excused += len(m["excused"])
+        _say(name, "head", h, "H err", m["entropy_max_abs_err"], "O", m["o_max_abs"], m["o_mean_abs"],
+             "excused", m["excused"][:20], "mismatched", m["level_mismatch"])
+    retained, listed = run["plan"].stats()
+    _say(name, "density", retained / (cfg.heads * cfg.N ** 2), "tile efficiency", retained / listed)
+
+
+def test_plan_reuse_path(gpu):
+    """Plan from call 1 reused for calls 2..4 with 1% perturbed Q and K."""
+    cfg = CONFIGS["wan21_14b_720p"]
+    _say("case: reuse path")
+    q, k, v = make_inputs(cfg, device=gpu)
+    plan = tra.plan(q, k, grid=(cfg.T, cfg.H, cfg.W), **cfg.params())
+    exp = plan.export()
+    rng = np.random.default_rng(12)
+    R2 = O.radius_table(cfg.params(), cfg.T)
+    for call in range(2, 5):
+        qc, kc = perturb(q, call, 0), perturb(k, call, 1)
+        o = tra.attention(qc, kc, v, plan)
+        torch.cuda.synchronize()
+        h = int(rng.integers(cfg.heads))
+        qs = rng.choice(cfg.N, size=32, replace=False)
+        ref = O.attention_rows(qc[0, h].double().cpu().numpy(), kc[0, h].double().cpu().numpy(),
+                               v[0, h].double().cpu().numpy(), qs, exp["levels"][h].astype(np.int64),
+                               R2, cfg.T, cfg.H, cfg.W, cfg.params())
+        err = np.abs(o[0, h].double().cpu().numpy()[qs] - ref)
+        _say("call", call, "head", h, err.max(), err.mean())
+        assert err.max() <= 2e-2 and err.mean() <= 2e-3
