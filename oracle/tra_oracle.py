@@ -222,6 +222,8 @@ def excused_queries(H, p, tol=ENTROPY_EXCUSE):
     if p["radius_override"] >= 0:
         return np.zeros(0, dtype=np.int64)
     k_lo, k_hi = level_range(p)
+    if k_hi <= k_lo:
+        return np.zeros(0, dtype=np.int64)  # a single level: no boundary changes it
     H = np.asarray(H, dtype=np.float64)
     L = p["levels_per_nat"] * (p["a"] * H + p["c"])
     nearest = np.clip(np.round(L), k_lo + 1, k_hi)

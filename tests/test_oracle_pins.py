@@ -185,6 +185,8 @@ def test_excused_queries_window():
     Hb = (k_lo + 5) / 8.0
     Hs = np.array([Hb - 2e-5, Hb - 5e-6, Hb, Hb + 5e-6, Hb + 2e-5, (k_lo - 3) / 8.0, (k_hi + 3) / 8.0])
     assert list(O.excused_queries(Hs, p)) == [1, 2, 3]
+    single = _p(budget_min=1.0, budget_max=1.0)  # one level: nothing can move it
+    assert len(O.excused_queries(np.array([0.0, 1e-7]), single)) == 0
 
 
 # ---------------------------------------------------------------------------
