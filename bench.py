@@ -1,0 +1,189 @@
+"""Benchmark of the Token Radius Attention hot path on one MI355X.
+
+One step = one pass of the whole path over the Wan2.1-14B-shaped 720p layer
+call (B=1, 40 heads, d=128, latent grid 21x45x80 = 75,600 tokens, bf16): the
+plan (key pooling, entropy, levels, tile lists) is rebuilt from (Q, K) and then
+reused by four attention calls whose Q and K are perturbed by 1% (the warm-up
+reuse path).  All inputs are synthetic, generated on the GPU and resident in
+HBM before the timed region.
+
+Printed: one JSON line.  `value` is retained-FLOP throughput of the whole step,
+4*d*(retained pairs) per attention call times 4 calls, divided by the step time.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import sparse_self_attention_amd as tra  # noqa: E402
+from workloads import get_config, make_inputs, perturb  # noqa: E402
+
+WORKLOAD = "wan21_14b_720p"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBPS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(cfg, q, k, v, plan_export, budget_s=12.0):
+    """The oracle, unchanged, on a bounded sample of the same workload: pooling
+    and entropy of one head, then exact attention rows for sampled queries of
+    that head until about `budget_s` seconds of CPU work have been spent."""
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+    p = cfg.params()
+    rng = np.random.default_rng(0)
+    h = 0
+    qh, kh, vh = (x[0, h].double().cpu().numpy() for x in (q, k, v))
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        pools = O.Geometry(cfg.T, cfg.H, cfg.W, cfg.pool_h, cfg.pool_w)
+        kbar = O.pool_keys(kh, pools, cfg.dtype)
+        Hh = O.entropy(qh, kbar, pools.block_sizes())
+        lv = O.levels(Hh, p)
+        t_plan = time.perf_counter() - t0
+        R2 = O.radius_table(p, cfg.T)
+        pairs, nq = 0, 0
+        t1 = time.perf_counter()
+        order = rng.permutation(cfg.N)
+        while time.perf_counter() - t1 < budget_s and nq < cfg.N:
+            batch = order[nq:nq + 16]
+            O.attention_rows(qh, kh, vh, batch, lv, R2, cfg.T, cfg.H, cfg.W, p)
+            pairs += sum(O.retained_count(int(i), int(lv[i]), R2, cfg.T, cfg.H, cfg.W, p) for i in batch)
+            nq += len(batch)
+        t_attn = time.perf_counter() - t1
+    flops = 4.0 * cfg.head_dim * pairs
+    return {"value": flops / t_attn / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": (f"head 0: fp64 pooling+entropy+levels of all {cfg.N} queries in {t_plan:.2f}s; "
+                       f"exact masked attention of {nq} random queries ({pairs} retained pairs) "
+                       f"in {t_attn:.2f}s; value = 4*d*pairs/attention time")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path has no multi-GPU mode",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    tra.load_library()  # fails loudly when libtra.so is missing
+
+    cfg = get_config(args.workload)
+    dev = torch.device("cuda:0")
+    grid = (cfg.T, cfg.H, cfg.W)
+    calls = max(1, cfg.reuse_calls)
+    log(f"[bench] generating {cfg.name}: heads={cfg.heads} N={cfg.N} d={cfg.head_dim} {cfg.dtype}")
+    q, k, v = make_inputs(cfg, device=dev)
+    qs, ks = [q], [k]
+    for c in range(2, calls + 1):
+        qs.append(perturb(q, c, 0))
+        ks.append(perturb(k, c, 1))
+    outs = [torch.empty_like(q) for _ in range(calls)]
+    torch.cuda.synchronize()
+
+    plan = tra.plan(q, k, grid=grid, **cfg.params())
+    retained, listed = plan.stats()
+    info = plan.info()
+    flops_call = 4.0 * cfg.head_dim * retained
+    log(f"[bench] plan: nnz={info['nnz']} retained={retained} density={retained / (cfg.heads * cfg.N ** 2):.4f} "
+        f"tile efficiency={retained / listed:.3f}")
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(rec=None):
+        if rec is not None:
+            rec["p0"].record(stream)
+        plan.rebuild(qs[0], ks[0])
+        if rec is not None:
+            rec["p1"].record(stream)
+        for c in range(calls):
+            if rec is not None:
+                rec["a0"][c].record(stream)
+            tra.attention(qs[c], ks[c], v, plan, out=outs[c])
+            if rec is not None:
+                rec["a1"][c].record(stream)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup {i + 1}/{args.warmup}")
+
+    recs = [{"p0": torch.cuda.Event(enable_timing=True), "p1": torch.cuda.Event(enable_timing=True),
+             "a0": [torch.cuda.Event(enable_timing=True) for _ in range(calls)],
+             "a1": [torch.cuda.Event(enable_timing=True) for _ in range(calls)]} for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(recs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    plan_ms = float(np.mean([r["p0"].elapsed_time(r["p1"]) for r in recs]))
+    attn_ms_all = [r["a0"][c].elapsed_time(r["a1"][c]) for r in recs for c in range(calls)]
+    attn_ms = float(np.mean(attn_ms_all))
+    log(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step, plan {plan_ms:.3f} ms, attention {attn_ms:.3f} ms/call")
+
+    value = calls * flops_call / (ms_step * 1e-3) / 1e12
+    achieved = flops_call / (attn_ms * 1e-3) / 1e12
+    elem = 2 if cfg.dtype == "bf16" else 4
+    plan_bytes = (2 * cfg.heads * cfg.N * cfg.head_dim * elem          # read Q and K
+                  + cfg.heads * cfg.N * (2 + 4)                          # write levels + entropy
+                  + 4 * (info["nnz"] + info["n_rows"] + 1))              # write tile lists
+    result = {
+        "metric": "ms/call + retained-FLOP TFLOPS (% bf16 MFMA peak), Wan2.1-14B 720p, 1 GPU",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.batch, "heads": cfg.heads, "grid": list(grid),
+                   "head_dim": cfg.head_dim, "attention_calls_per_plan": calls,
+                   "retained_density": retained / (cfg.heads * cfg.N ** 2),
+                   "tile_efficiency": retained / listed},
+        "ms_per_call": {"attention": attn_ms, "plan": plan_ms, "step_per_call": ms_step / calls},
+        "attention": {"retained_tflops": achieved, "frac_bf16_peak": achieved / PEAK_BF16_TFLOPS,
+                      "listed_pair_tflops": 4.0 * cfg.head_dim * listed / (attn_ms * 1e-3) / 1e12,
+                      "retained_flops_per_call": flops_call},
+        "plan": {"ms": plan_ms, "algorithmic_bytes": plan_bytes,
+                 "gbps": plan_bytes / (plan_ms * 1e-3) / 1e9,
+                 "frac_hbm_peak": plan_bytes / (plan_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(cfg, q, k, v, None)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
