@@ -40,6 +40,8 @@ struct Table {
   std::vector<double> r0sq;     // per level row
   std::vector<int32_t> r2;      // n_levels x T, -1 = inactive frame
   std::vector<int32_t> dmax;    // largest active delta per row
+  std::vector<int32_t> r2c;     // compact: active entries of each row, row r at r2off[r]
+  std::vector<int32_t> r2off;
 };
 
 tra_status check_shape(const tra_shape* s) {
@@ -110,6 +112,13 @@ tra_status check_params(const tra_shape* s, const tra_params* p, Table* tab) {
     }
     t.dmax[r] = dm;
   }
+  t.r2off.resize(t.n_levels);
+  for (int r = 0; r < t.n_levels; ++r) {
+    t.r2off[r] = static_cast<int32_t>(t.r2c.size());
+    for (int dl = 0; dl <= t.dmax[r]; ++dl) t.r2c.push_back(t.r2[static_cast<size_t>(r) * T + dl]);
+  }
+  if (s->dtype == TRA_BF16 && tra::attention_lds_bytes(s->head_dim, static_cast<int>(t.r2c.size())) > 163840)
+    return fail(TRA_ERR_INVALID_ARG, "radius table too large for the attention kernel's LDS");
   if (tab) *tab = std::move(t);
   return TRA_OK;
 }
@@ -133,6 +142,8 @@ struct tra_plan {
   int16_t* lv = nullptr;
   int32_t* r2 = nullptr;
   int32_t* dmax = nullptr;
+  int32_t* r2c = nullptr;
+  int32_t* r2off = nullptr;
   float* pool_w = nullptr;
   int32_t* counts = nullptr;
   int32_t* row_ptr = nullptr;
@@ -148,7 +159,8 @@ namespace {
 
 void release(tra_plan* p) {
   if (!p) return;
-  void* bufs[] = {p->kbar, p->H, p->lv, p->r2, p->dmax, p->pool_w, p->counts, p->row_ptr, p->col_idx, p->totals};
+  void* bufs[] = {p->kbar, p->H, p->lv, p->r2, p->dmax, p->r2c, p->r2off, p->pool_w,
+                  p->counts, p->row_ptr, p->col_idx, p->totals};
   for (void* b : bufs)
     if (b) (void)hipFree(b);
   if (p->totals_host) (void)hipHostFree(p->totals_host);
@@ -256,6 +268,8 @@ tra_status tra_plan_create(const tra_shape* shape, const tra_params* params, con
   TRA_HIP_P(hipMalloc(&p->lv, p->n_queries * sizeof(int16_t)));
   TRA_HIP_P(hipMalloc(&p->r2, p->table.r2.size() * sizeof(int32_t)));
   TRA_HIP_P(hipMalloc(&p->dmax, p->table.dmax.size() * sizeof(int32_t)));
+  TRA_HIP_P(hipMalloc(&p->r2c, p->table.r2c.size() * sizeof(int32_t)));
+  TRA_HIP_P(hipMalloc(&p->r2off, p->table.r2off.size() * sizeof(int32_t)));
   TRA_HIP_P(hipMalloc(&p->pool_w, static_cast<size_t>(p->pool.count) * sizeof(float)));
   TRA_HIP_P(hipMalloc(&p->counts, p->n_rows * sizeof(int32_t)));
   TRA_HIP_P(hipMalloc(&p->row_ptr, (p->n_rows + 1) * sizeof(int32_t)));
@@ -273,6 +287,8 @@ tra_status tra_plan_create(const tra_shape* shape, const tra_params* params, con
   TRA_HIP_P(hipMemcpy(p->r2, p->table.r2.data(), p->table.r2.size() * sizeof(int32_t), hipMemcpyHostToDevice));
   TRA_HIP_P(hipMemcpy(p->dmax, p->table.dmax.data(), p->table.dmax.size() * sizeof(int32_t), hipMemcpyHostToDevice));
   TRA_HIP_P(hipMemcpy(p->pool_w, w.data(), w.size() * sizeof(float), hipMemcpyHostToDevice));
+  TRA_HIP_P(hipMemcpy(p->r2c, p->table.r2c.data(), p->table.r2c.size() * sizeof(int32_t), hipMemcpyHostToDevice));
+  TRA_HIP_P(hipMemcpy(p->r2off, p->table.r2off.data(), p->table.r2off.size() * sizeof(int32_t), hipMemcpyHostToDevice));
 #undef TRA_HIP_P
   st = build(p, q, k, hs);
   if (st != TRA_OK) return fin(st);
@@ -289,7 +305,9 @@ tra_status tra_attention(const tra_plan* plan, const void* q, const void* k, con
     return fail(TRA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
   if (o == q || o == k || o == v) return fail(TRA_ERR_INVALID_ARG, "o must not alias q, k or v");
   const tra_shape& s = plan->shape;
-  TRA_HIP(tra::launch_attention(s.dtype, s.head_dim, q, k, v, o, plan->lv, plan->r2, plan->row_base,
+  const tra::RadiusTable tab{plan->r2, plan->dmax, plan->r2c, plan->r2off,
+                             static_cast<int>(plan->table.r2c.size()), s.T};
+  TRA_HIP(tra::launch_attention(s.dtype, s.head_dim, q, k, v, o, plan->lv, tab, plan->row_base,
                                 plan->BH, plan->tiles, plan->row_ptr, plan->col_idx,
                                 static_cast<hipStream_t>(stream)));
   return TRA_OK;

@@ -26,6 +26,19 @@ inline Grid make_grid(int T, int H, int W, int th, int tw) {
   return g;
 }
 
+// Radius table on the device: the full table (n_levels x T, -1 = inactive
+// frame), the largest active frame distance per level row, and a compact copy
+// holding only the active entries of each row (row r at r2off[r], dmax[r] + 1
+// entries) for staging in LDS.
+struct RadiusTable {
+  const int32_t* r2;
+  const int32_t* dmax;
+  const int32_t* r2c;
+  const int32_t* r2off;
+  int n_r2c;
+  int T;
+};
+
 struct EntropyArgs {
   double a, c;
   int levels_per_nat, k_lo, k_hi;
@@ -47,9 +60,13 @@ hipError_t launch_csr_fill(const int16_t* lv, const int32_t* r2, const int32_t* 
                            int row_base, int BH, const Grid& tiles, const int32_t* row_ptr,
                            int32_t* col_idx, hipStream_t s);
 hipError_t launch_attention(int dtype, int d, const void* q, const void* k, const void* v,
-                            void* o, const int16_t* lv, const int32_t* r2, int row_base,
+                            void* o, const int16_t* lv, const RadiusTable& tab, int row_base,
                             int BH, const Grid& tiles, const int32_t* row_ptr,
                             const int32_t* col_idx, hipStream_t s);
+// Dynamic LDS the bf16 attention kernel needs for its staged K/V buffers
+// plus a compact radius table of n_r2c entries; 0 if it exceeds the device limit.
+size_t attention_lds_bytes(int d, int n_r2c);
+
 hipError_t launch_stats(const int16_t* lv, const int32_t* r2, int T, int row_base, int BH,
                         const Grid& tiles, const int32_t* row_ptr, const int32_t* col_idx,
                         unsigned long long* out2, hipStream_t s);

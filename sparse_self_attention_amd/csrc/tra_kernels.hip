@@ -24,6 +24,7 @@
 #include "tra_internal.h"
 
 #include <math.h>
+#include <stdlib.h>
 
 namespace tra {
 
@@ -61,10 +62,25 @@ __device__ __forceinline__ int swz(int r) {
   }
 }
 
-// Transposing LDS read of 4 bf16 (ds_read_b64_tr_b16); elem_off in elements.
-__device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t* base, int elem_off) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (lds_bf16x4*)((__attribute__((address_space(3))) char*)(base) + elem_off * 2));
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane 4r + j supplies the address of 4 consecutive bf16 (row r, columns
+// 4j..4j+3 of a 4 x 16 block); lane i of the group receives column i of rows
+// 0..3.  elem_off is in elements.  Results stay packed: element-wise access
+// to bf16 vectors is avoided throughout (whole-vector bit casts only).
+__device__ __forceinline__ uint2 lds_read_tr(const uint16_t* base, int elem_off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4*)((__attribute__((address_space(3))) char*)(base) + elem_off * 2)));
+}
+
+// Transposing LDS read at a byte address.
+__device__ __forceinline__ uint2 lds_read_tr_b(const char* p) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4*)((__attribute__((address_space(3))) char*)(p))));
+}
+
+// Two floats -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
 // Wave-wide min / max (64 lanes): DPP inside rows of 16, then lane swaps.
@@ -249,10 +265,12 @@ __global__ __launch_bounds__(256) void entropy_bf16_kernel(
       for (int ks = 0; ks < KS; ++ks)
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qf[cb][ks], acc, 0, 0, 0);
       if (partial) {
+        // Padded rows: weight 0 and a finite sentinel score, so that they add
+        // exactly 0 to both sums (an infinite score would make 0 * inf = NaN).
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int r = 8 * (i >> 2) + 4 * h + (i & 3);
-          if (ci * 32 + r >= NP) acc[i] = TRA_NEG_INF;
+          if (ci * 32 + r >= NP) acc[i] = -3.0e38f;
         }
       }
       float mx = acc[0];
@@ -469,91 +487,208 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Block-sparse attention, bf16, 8x8 tiles.  One workgroup (2 waves) per query
-// tile; wave w owns tile rows 4w..4w+3 (32 queries), lane%32 = query.
+// Block-sparse attention, bf16, 8x8 tiles.
+//
+// Work decomposition.  A workgroup of 4 waves owns a group of G = 2*QB
+// neighbouring query tiles of one frame (QB = 1: a 1x2 pair, QB = 2: a 2x2
+// square) and walks the ascending union of their tile lists, merged on the fly
+// from the CSR rows.  Each key tile is fetched once per workgroup into one of
+// two LDS buffers with global_load_lds_dwordx4, so the next tile streams in
+// while the current one is consumed, and all 4 waves use it.  A wave owns QB
+// blocks of 32 queries (lane % 32 = query) and skips a 32-key half of a tile
+// whenever none of its queries retains a key there: tiles that only a
+// neighbouring query tile needs cost loads but no matrix work.
+//
 //   S^T (keys x queries) = K Q^T :  A = K rows from LDS, B = Q^T in registers
-//   O^T (d x queries) += V^T P^T :  A = V^T via ds_read_b64_tr_b16, B = P^T
+//   O^T (d x queries)   += V^T P^T : A = V^T via ds_read_b64_tr_b16, B = P^T
 // The 32x32 output layout puts key rows {8(i/4) + 4(lane/32) + i%4} of a
 // 32-key block in register i of a lane, which is exactly the k-slot order of
 // the next MFMA's B operand, so P never leaves registers.
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(128) void attn_bf16_kernel(
+// Workgroup barrier for LDS hand-offs: this wave's LDS reads are complete
+// (lgkmcnt(0)) before it arrives.  Unlike __syncthreads() it carries no
+// release fence, so it does not wait for this wave's outstanding DMA loads into
+// the other buffer; those are ordered by wait_vmcnt before the next barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 16-byte global -> LDS DMA (global_load_lds_dwordx4): lane l's 16 bytes land
+// at LDS byte address lds_base + 16*l (lds_base wave-uniform, through M0).
+// Issued from inline assembly so that the compiler's wait-count insertion does
+// not treat every later LDS read as dependent on it; the kernel orders the
+// hand-off itself with wait_vmcnt + lds_barrier.  The instruction has no
+// register results; one wait state separates the M0 write from its use.
+__device__ __forceinline__ void lds_dma16(const void* gaddr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gaddr), "s"(lds_base)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  // s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left unconstrained)
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// LDS row strides (bytes) of the staged K and V tiles.  K rows are read as
+// 16-byte MFMA operands by 16 lanes at a time (same chunk, 16 consecutive rows):
+// a stride of 4 banks mod 64 spreads them over all banks.  V rows are read with
+// ds_read_b64_tr_b16 by 32 lanes at a time (4 consecutive rows x 64 bytes): a
+// stride of 16 banks mod 64 does the same.  Both make every LDS address a
+// per-lane base plus an immediate offset.
+template <int D> struct AttnLds {
+  static constexpr int KSTR = 2 * D + 16;
+  static constexpr int VSTR = 2 * D + 64;
+  static constexpr int KSEG = 64 * KSTR / 1024;  // 1 KB DMA segments per K tile
+  static constexpr int VSEG = 64 * VSTR / 1024;
+  static constexpr int BUF = (KSEG + VSEG) * 1024;
+  static_assert(64 * KSTR % 1024 == 0 && 64 * VSTR % 1024 == 0, "tile must be whole segments");
+};
+
+template <int D, int QB>
+__global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, const int16_t* __restrict__ lv,
-    const int32_t* __restrict__ r2, int row_base, int T, Grid g,
-    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx) {
-  constexpr int NCH = D / 8;   // 16-byte chunks per key row
-  constexpr int KS = D / 16;   // k-steps of S^T
-  constexpr int DB = D / 32;   // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[64 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[64 * D];
+    const int32_t* __restrict__ r2c, const int32_t* __restrict__ r2off,
+    const int32_t* __restrict__ dmax, int n_r2c, int row_base, Grid g, int ngh, int ngw,
+    int n_groups, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx) {
+  using L = AttnLds<D>;
+  constexpr int KS = D / 16;                  // k-steps of S^T
+  constexpr int DB = D / 32;                  // 32-row blocks of O^T
+  constexpr int GH = QB == 2 ? 2 : 1, G = GH * 2;
+  __shared__ __attribute__((aligned(1024))) char kv0[L::BUF];  // K | V, buffer 0
+  __shared__ __attribute__((aligned(1024))) char kv1[L::BUF];  // K | V, buffer 1
+  extern __shared__ int32_t r2s[];  // compact radius table (dynamic LDS)
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int h = lane >> 5, col = lane & 31;
-  const int row = blockIdx.x;
-  const int bh = row / g.count, tile = row % g.count;
+  // Dispatch goes round-robin over the 8 XCDs; give each XCD a contiguous
+  // range of groups so that neighbouring groups, which share most key tiles,
+  // run under the same L2.  The grid is padded to a multiple of 8.
+  const int per_xcd = gridDim.x / 8;
+  const int gid = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (gid >= n_groups) return;  // uniform over the workgroup, before any barrier
+  for (int i = threadIdx.x; i < n_r2c; i += 256) r2s[i] = r2c[i];
+  __syncthreads();
+
+  const int groups_per_frame = ngh * ngw;
+  const int per_head = g.T * groups_per_frame;
+  const int bh = gid / per_head;
+  const int grem = gid % per_head;
+  const int tq = grem / groups_per_frame;
+  const int gr = (grem % groups_per_frame) / ngw, gc = grem % ngw;
   const size_t N = static_cast<size_t>(g.T) * g.H * g.W;
-  const int tq = tile / g.per_frame, trem = tile % g.per_frame;
-  const int h0 = (trem / g.nw) * 8, w0 = (trem % g.nw) * 8;
-  const int mq = wave * 32 + col;
-  const int hq = h0 + (mq >> 3), wq = w0 + (mq & 7);
-  const bool qvalid = hq < g.H && wq < g.W;
-  const size_t nq = (static_cast<size_t>(tq) * g.H + (qvalid ? hq : h0)) * g.W + (qvalid ? wq : w0);
 
-  bf16x8 qf[KS];
-  {
-    const uint16_t* qp = q + (static_cast<size_t>(bh) * N + nq) * D;
+  // This wave's query tile and queries (lane % 32 -> tile column, 4 rows per block).
+  const int tr = QB == 2 ? gr * 2 + (wave >> 1) : gr;
+  const int tc = QB == 2 ? gc * 2 + (wave & 1) : gc * 2 + (wave >> 1);
+  const bool tvalid = tr < g.nh && tc < g.nw;
+  const int wq = tc * 8 + (col & 7);
+  int hq[QB], toff[QB], tdmax[QB];
+  bool qvalid[QB];
+  size_t nq[QB];
+  bf16x8 qf[QB][KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks + 8 * h);
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row_in_tile = (QB == 2 ? 4 * qb : 4 * (wave & 1)) + (col >> 3);
+    hq[qb] = tr * 8 + row_in_tile;
+    qvalid[qb] = tvalid && hq[qb] < g.H && wq < g.W;
+    const int hh = qvalid[qb] ? hq[qb] : 0, ww = qvalid[qb] ? wq : 0;
+    nq[qb] = (static_cast<size_t>(tq) * g.H + hh) * g.W + ww;
+    const uint16_t* qp = q + (static_cast<size_t>(bh) * N + nq[qb]) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[qb][ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks + 8 * h);
+    const int trow = qvalid[qb] ? lv[static_cast<size_t>(bh) * N + nq[qb]] - row_base : 0;
+    toff[qb] = r2off[trow];
+    tdmax[qb] = qvalid[qb] ? dmax[trow] : -1;
   }
-  const int trow = qvalid ? lv[static_cast<size_t>(bh) * N + nq] - row_base : 0;
-  const int32_t* r2row = r2 + trow * T;
 
-  f32x16 oacc[DB];
+  // Tile lists of the group's query tiles (empty for tiles outside the grid).
+  int ptr[G], endp[G];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) oacc[db] = (f32x16){0.f};
-  float mref = TRA_NEG_INF, lsum = 0.f;
-  const float c1 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
+  for (int gi = 0; gi < G; ++gi) {
+    const int rr = QB == 2 ? gr * 2 + (gi >> 1) : gr;
+    const int cc = gc * 2 + (gi & 1);
+    ptr[gi] = endp[gi] = 0;
+    if (rr < g.nh && cc < g.nw) {
+      const int64_t row = static_cast<int64_t>(bh) * g.count + (tq * g.nh + rr) * g.nw + cc;
+      ptr[gi] = row_ptr[row];
+      endp[gi] = row_ptr[row + 1];
+    }
+  }
+  auto next_tile = [&]() {
+    int kt = 0x7fffffff;
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi)
+      if (ptr[gi] < endp[gi]) kt = min(kt, col_idx[ptr[gi]]);
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi)
+      if (ptr[gi] < endp[gi] && col_idx[ptr[gi]] == kt) ++ptr[gi];
+    return kt;
+  };
 
   const uint16_t* kbase = k + static_cast<size_t>(bh) * N * D;
   const uint16_t* vbase = v + static_cast<size_t>(bh) * N * D;
-  const int beg = row_ptr[row], end = row_ptr[row + 1];
 
-  // Transposed-read addressing (per lane, fixed): group g4 of 16 lanes, lane
-  // r4 = (lane%16)/4 picks the key row, j4 = lane%4 the 4-column slice.
-  const int g4 = lane >> 4, r4 = (lane & 15) >> 2, j4 = lane & 3;
-
-  for (int e = beg; e < end; ++e) {
-    const int kt = col_idx[e];
+  // Streams key tile kt into buffer buf.  DMA segment s (1 KB) receives lane
+  // l's 16 bytes at s*1KB + 16*l; the lane fetches the (key row, chunk) that
+  // the padded layout puts there (pad chunks re-fetch the row's first chunk).
+  // Every wave issues the same number of DMA loads per tile (a wave without a
+  // segment of its own repeats the last one, writing identical bytes), so the
+  // loop's memory counters follow a fixed pattern.
+  auto issue_part = [&](const uint16_t* base, char* dst, int stride, int nseg, int kr0, int kc0, int tk) {
+#pragma unroll
+    for (int i = 0; i < (L::VSEG + 3) / 4; ++i) {
+      if (4 * i >= nseg) break;  // compile-time after unrolling (nseg is KSEG or VSEG)
+      const int seg = min(wave + 4 * i, nseg - 1);
+      const int ob = seg * 1024 + lane * 16;
+      const int kk = ob / stride;
+      int c = (ob % stride) / 16;
+      c = c < D / 8 ? c : 0;
+      const int kr = min(kr0 + (kk >> 3), g.H - 1), kc = min(kc0 + (kk & 7), g.W - 1);
+      const size_t off = ((static_cast<size_t>(tk) * g.H + kr) * g.W + kc) * D + c * 8;
+      lds_dma16(base + off, __builtin_amdgcn_readfirstlane(
+                                static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+                                    (__attribute__((address_space(3))) char*)(dst))) + seg * 1024));
+    }
+  };
+  auto issue = [&](int kt, char* buf) {
     const int tk = kt / g.per_frame, krem = kt % g.per_frame;
     const int kr0 = (krem / g.nw) * 8, kc0 = (krem % g.nw) * 8;
-    __syncthreads();
-#pragma unroll
-    for (int it = 0; it < (64 * NCH) / 128; ++it) {
-      const int idx = threadIdx.x + it * 128;
-      const int kk = idx / NCH, c = idx % NCH;
-      const int kr = min(kr0 + (kk >> 3), g.H - 1), kc = min(kc0 + (kk & 7), g.W - 1);
-      const size_t nk = (static_cast<size_t>(tk) * g.H + kr) * g.W + kc;
-      const uint4 kv = *reinterpret_cast<const uint4*>(kbase + nk * D + c * 8);
-      const uint4 vv = *reinterpret_cast<const uint4*>(vbase + nk * D + c * 8);
-      const int off = kk * D + ((c ^ swz<NCH>(kk)) << 3);
-      *reinterpret_cast<uint4*>(&k_lds[off]) = kv;
-      *reinterpret_cast<uint4*>(&v_lds[off]) = vv;
-    }
-    __syncthreads();
+    issue_part(kbase, buf, L::KSTR, L::KSEG, kr0, kc0, tk);
+    issue_part(vbase, buf + L::KSEG * 1024, L::VSTR, L::VSEG, kr0, kc0, tk);
+  };
 
-    // Exact mask: key (kr0 + 4*blk + a, kc0 + 4*h + b) for register i = 4a + b.
+  f32x16 oacc[QB][DB];
+  float mref[QB], lsum[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    mref[qb] = TRA_NEG_INF;
+    lsum[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[qb][db] = (f32x16){0.f};
+  }
+  const float c1 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
+  // Per-lane LDS byte bases; every read below adds a compile-time offset.
+  const int g4 = lane >> 4, r4 = (lane & 15) >> 2, j4 = lane & 3;
+  const int kread = col * L::KSTR + h * 16;
+  const int vread = (4 * (g4 >> 1) + r4) * L::VSTR + (16 * (g4 & 1) + 4 * j4) * 2;
+
+  auto compute = [&](int kt, const char* buf) {
+    const int tk = kt / g.per_frame, krem = kt % g.per_frame;
+    const int kr0 = (krem / g.nw) * 8, kc0 = (krem % g.nw) * 8;
     const int delta = tk > tq ? tk - tq : tq - tk;
-    const int thr = qvalid ? r2row[delta] : -1;
-    int remr[2][4], dw2[4];
+    int thr[QB];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int kr = kr0 + 4 * blk + a, dh = hq - kr;
-        remr[blk][a] = (kr < g.H && thr >= 0) ? thr - dh * dh : -1;
-      }
+    for (int qb = 0; qb < QB; ++qb) {
+      const int t = r2s[toff[qb] + min(delta, max(tdmax[qb], 0))];
+      thr[qb] = delta <= tdmax[qb] ? t : -1;
+    }
+    // Exact mask: key (kr0 + 4*blk + a, kc0 + 4*h + b) sits in register i = 4a + b.
+    int dw2[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int kc = kc0 + 4 * h + b, dw = wq - kc;
@@ -561,110 +696,140 @@ __global__ __launch_bounds__(128) void attn_bf16_kernel(
     }
     const int mindw = min(min(dw2[0], dw2[1]), min(dw2[2], dw2[3]));
     const int maxdw = max(max(dw2[0], dw2[1]), max(dw2[2], dw2[3]));
-    bool doblk[2], fullblk[2];
+    int remr[QB][2][4];
+    bool doq[QB][2], fullq[QB][2];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const int mxr = max(max(remr[blk][0], remr[blk][1]), max(remr[blk][2], remr[blk][3]));
-      const int mnr = min(min(remr[blk][0], remr[blk][1]), min(remr[blk][2], remr[blk][3]));
-      doblk[blk] = __any(mxr >= mindw);
-      fullblk[blk] = __all(mnr >= maxdw);
-    }
-    if (!doblk[0] && !doblk[1]) continue;
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int kr = kr0 + 4 * blk + a, dh = hq[qb] - kr;
+          remr[qb][blk][a] = (kr < g.H && thr[qb] >= 0) ? thr[qb] - dh * dh : -1;
+        }
+        const int mxr = max(max(remr[qb][blk][0], remr[qb][blk][1]), max(remr[qb][blk][2], remr[qb][blk][3]));
+        const int mnr = min(min(remr[qb][blk][0], remr[qb][blk][1]), min(remr[qb][blk][2], remr[qb][blk][3]));
+        doq[qb][blk] = __any(mxr >= mindw);
+        fullq[qb][blk] = __all(mnr >= maxdw);
+      }
 
-    f32x16 sacc[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      sacc[blk] = (f32x16){0.f};
-      if (!doblk[blk]) continue;
-      const int kk = 32 * blk + col;
+      bool any = false;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) any = any || doq[qb][blk];
+      if (!any) continue;
+      f32x16 sacc[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sacc[qb] = (f32x16){0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 af =
-            *reinterpret_cast<const bf16x8*>(&k_lds[kk * D + (((2 * ks + h) ^ swz<NCH>(kk)) << 3)]);
-        sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], sacc[blk], 0, 0, 0);
+        const bf16x8 af = *reinterpret_cast<const bf16x8*>(buf + kread + 32 * blk * L::KSTR + 32 * ks);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          if (doq[qb][blk]) sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[qb][ks], sacc[qb], 0, 0, 0);
       }
-      if (!fullblk[blk]) {
+      bf16x8 pf[QB][2];
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (dw2[i & 3] > remr[blk][i >> 2]) sacc[blk][i] = TRA_NEG_INF;
-      }
-    }
-
-    float mx = TRA_NEG_INF;
+      for (int qb = 0; qb < QB; ++qb) {
+        if (!doq[qb][blk]) continue;
+        if (!fullq[qb][blk]) {
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-      if (doblk[blk]) {
+          for (int i = 0; i < 16; ++i)
+            if (dw2[i & 3] > remr[qb][blk][i >> 2]) sacc[qb][i] = TRA_NEG_INF;
+        }
+        float mx = sacc[qb][0];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[blk][i]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mcand = mx * c1;
-    // Lazy rescale: the reference max moves only when a score exceeds it by
-    // more than 2^8, so probabilities stay <= 256 between rescales.
-    if (__any(mcand > mref + 8.f)) {
-      const float mn = fmaxf(mref, mcand);
-      const float alpha = mref == TRA_NEG_INF ? 0.f : __builtin_amdgcn_exp2f(mref - mn);
-      lsum *= alpha;
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[qb][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mcand = mx * c1;
+        // Lazy rescale: the reference moves only when a score exceeds it by
+        // more than 2^8, so probabilities stay <= 256 between rescales.
+        if (__any(mcand > mref[qb] + 8.f)) {
+          const float mn = fmaxf(mref[qb], mcand);
+          const float alpha = mref[qb] == TRA_NEG_INF ? 0.f : __builtin_amdgcn_exp2f(mref[qb] - mn);
+          lsum[qb] *= alpha;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-      mref = mn;
-    }
-    const float msub = mref == TRA_NEG_INF ? 0.f : mref;
-
+          for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha;
+          mref[qb] = mn;
+        }
+        const float msub = mref[qb] == TRA_NEG_INF ? 0.f : mref[qb];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      if (!doblk[blk]) continue;
-      bf16x8 pf[2];
+        for (int j = 0; j < 2; ++j) {
+          uint32_t pk[4];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[blk][8 * j + 2 * x], c1, -msub));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[blk][8 * j + 2 * x + 1], c1, -msub));
-          lsum += p0 + p1;
-          const bf16x2 pp = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
-          pf[j][2 * x] = pp[0];
-          pf[j][2 * x + 1] = pp[1];
+          for (int x = 0; x < 4; ++x) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[qb][8 * j + 2 * x], c1, -msub));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[qb][8 * j + 2 * x + 1], c1, -msub));
+            lsum[qb] += p0 + p1;
+            pk[x] = pack_bf16x2(p0, p1);
+          }
+          pf[qb][j] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
         }
       }
+      const char* vb = buf + L::KSEG * 1024 + vread;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          bf16x8 vf;
+          const uint2 lo = lds_read_tr_b(vb + (32 * blk + 16 * j) * L::VSTR + 64 * db);
+          const uint2 hi = lds_read_tr_b(vb + (32 * blk + 16 * j + 8) * L::VSTR + 64 * db);
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 #pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            const int kr = 32 * blk + 16 * j + 8 * s + 4 * (g4 >> 1) + r4;
-            const int d = 32 * db + 16 * (g4 & 1) + 4 * j4;
-            const int off = kr * D + ((((d >> 3)) ^ swz<NCH>(kr)) << 3) + (d & 7);
-            const bf16x4 t4 = lds_read_tr(v_lds, off);
-            vf[4 * s + 0] = t4[0];
-            vf[4 * s + 1] = t4[1];
-            vf[4 * s + 2] = t4[2];
-            vf[4 * s + 3] = t4[3];
-          }
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[j], oacc[db], 0, 0, 0);
+          for (int qb = 0; qb < QB; ++qb)
+            if (doq[qb][blk]) oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][j], oacc[qb][db], 0, 0, 0);
         }
       }
     }
+  };
+
+  // Loads complete in order: waiting until at most this wave's DMA loads of
+  // the next tile are outstanding leaves the current tile complete.
+  constexpr int LOADS_NEXT = (L::KSEG + 3) / 4 + (L::VSEG + 3) / 4;
+  // Two-stage pipeline with one DMA site per buffer: kv0 receives tile A while
+  // kv1's tile B is consumed, then kv1 receives the next B while A is consumed.
+  constexpr int NONE = 0x7fffffff;
+  int kt_a = next_tile(), kt_b = NONE;
+  while (true) {
+    if (kt_a != NONE) issue(kt_a, kv0);
+    if (kt_b != NONE) {
+      if (kt_a != NONE) wait_vmcnt<LOADS_NEXT>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      compute(kt_b, kv1);
+      lds_barrier();
+    }
+    if (kt_a == NONE) break;
+    kt_b = next_tile();
+    if (kt_b != NONE) {
+      issue(kt_b, kv1);
+      wait_vmcnt<LOADS_NEXT>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();
+    compute(kt_a, kv0);
+    lds_barrier();
+    kt_a = next_tile();
   }
 
-  const float ltot = lsum + __shfl_xor(lsum, 32);
-  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-  if (qvalid) {
-    uint16_t* op = o + (static_cast<size_t>(bh) * N + nq) * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const float ltot = lsum[qb] + __shfl_xor(lsum[qb], 32);
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    if (qvalid[qb]) {
+      uint16_t* op = o + (static_cast<size_t>(bh) * N + nq[qb]) * D;
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int d0 = 32 * db + 8 * a + 4 * h;
-        const bf16x2 lo2 = __builtin_convertvector(
-            ((f32x2){oacc[db][4 * a] * inv, oacc[db][4 * a + 1] * inv}), bf16x2);
-        const bf16x2 hi2 = __builtin_convertvector(
-            ((f32x2){oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv}), bf16x2);
-        const bf16x4 out4 = {lo2[0], lo2[1], hi2[0], hi2[1]};
-        *reinterpret_cast<bf16x4*>(op + d0) = out4;
-      }
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int d0 = 32 * db + 8 * a + 4 * h;
+          const uint2 out4 =
+              make_uint2(pack_bf16x2(oacc[qb][db][4 * a] * inv, oacc[qb][db][4 * a + 1] * inv),
+                         pack_bf16x2(oacc[qb][db][4 * a + 2] * inv, oacc[qb][db][4 * a + 3] * inv));
+          *reinterpret_cast<uint2*>(op + d0) = out4;
+        }
+    }
   }
 }
 
@@ -873,20 +1038,48 @@ hipError_t launch_csr_fill(const int16_t* lv, const int32_t* r2, const int32_t* 
   return hipGetLastError();
 }
 
+size_t attention_lds_bytes(int d, int n_r2c) {
+  const size_t kv = d == 128 ? 2 * AttnLds<128>::BUF : 2 * AttnLds<64>::BUF;
+  return kv + static_cast<size_t>(n_r2c) * sizeof(int32_t);
+}
+
+// Query blocks of 32 per wave in the bf16 attention kernel (1 or 2); the
+// environment variable TRA_ATTN_QB selects one for tuning, default 1.
+static int attention_query_blocks() {
+  static const int qb = [] {
+    const char* e = getenv("TRA_ATTN_QB");
+    return (e && e[0] == '2') ? 2 : 1;
+  }();
+  return qb;
+}
+
 hipError_t launch_attention(int dtype, int d, const void* q, const void* k, const void* v,
-                            void* o, const int16_t* lv, const int32_t* r2, int row_base,
+                            void* o, const int16_t* lv, const RadiusTable& tab, int row_base,
                             int BH, const Grid& tiles, const int32_t* row_ptr,
                             const int32_t* col_idx, hipStream_t s) {
+  const int32_t* r2 = tab.r2;
   const unsigned rows = static_cast<unsigned>(BH) * tiles.count;
   if (dtype == 1) {
     const auto* qq = static_cast<const uint16_t*>(q);
     const auto* kk = static_cast<const uint16_t*>(k);
     const auto* vv = static_cast<const uint16_t*>(v);
     auto* oo = static_cast<uint16_t*>(o);
-    if (d == 128)
-      attn_bf16_kernel<128><<<rows, 128, 0, s>>>(qq, kk, vv, oo, lv, r2, row_base, tiles.T, tiles, row_ptr, col_idx);
-    else
-      attn_bf16_kernel<64><<<rows, 128, 0, s>>>(qq, kk, vv, oo, lv, r2, row_base, tiles.T, tiles, row_ptr, col_idx);
+    const int qb = attention_query_blocks();
+    const int ngh = qb == 2 ? (tiles.nh + 1) / 2 : tiles.nh, ngw = (tiles.nw + 1) / 2;
+    const int64_t groups = static_cast<int64_t>(BH) * tiles.T * ngh * ngw;
+    const unsigned grid = static_cast<unsigned>((groups + 7) / 8 * 8);
+    const int ng = static_cast<int>(groups);
+    const size_t lds_tab = static_cast<size_t>(tab.n_r2c) * sizeof(int32_t);
+#define TRA_ATTN(DD, QQ)                                                                        \
+  attn_bf16_kernel<DD, QQ><<<grid, 256, lds_tab, s>>>(qq, kk, vv, oo, lv, tab.r2c, tab.r2off, tab.dmax, \
+                                                 tab.n_r2c, row_base, tiles, ngh, ngw, ng, row_ptr, \
+                                                 col_idx)
+    if (d == 128) {
+      if (qb == 2) TRA_ATTN(128, 2); else TRA_ATTN(128, 1);
+    } else {
+      if (qb == 2) TRA_ATTN(64, 2); else TRA_ATTN(64, 1);
+    }
+#undef TRA_ATTN
   } else {
     const auto* qq = static_cast<const float*>(q);
     const auto* kk = static_cast<const float*>(k);
