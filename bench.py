@@ -79,6 +79,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (a reference for "
+                         "hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path has no multi-GPU mode",
@@ -91,6 +94,12 @@ def main():
 
     cfg = get_config(args.workload)
     dev = torch.device("cuda:0")
+    if args.copy_probe_mb > 0:
+        src = torch.ones(args.copy_probe_mb << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     grid = (cfg.T, cfg.H, cfg.W)
     calls = max(1, cfg.reuse_calls)
     log(f"[bench] generating {cfg.name}: heads={cfg.heads} N={cfg.N} d={cfg.head_dim} {cfg.dtype}")

@@ -24,7 +24,6 @@
 #include "tra_internal.h"
 
 #include <math.h>
-#include <stdlib.h>
 
 namespace tra {
 
@@ -547,17 +546,31 @@ template <int D> struct AttnLds {
   static_assert(64 * KSTR % 1024 == 0 && 64 * VSTR % 1024 == 0, "tile must be whole segments");
 };
 
-template <int D, int QB>
-__global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_bf16_kernel(
+// Division by a constant divisor d (1 <= d < 2^16) for 0 <= n < 2^24:
+// floor(n / d) = (n * m) >> 40 with m = ceil(2^40 / d).
+struct FastDiv {
+  uint64_t m;
+  int d;
+};
+__host__ __device__ inline FastDiv make_fastdiv(int d) {
+  return FastDiv{((uint64_t(1) << 40) + static_cast<uint64_t>(d) - 1) / static_cast<uint64_t>(d), d};
+}
+__device__ __forceinline__ int fdiv(int n, const FastDiv& f) {
+  return static_cast<int>((static_cast<uint64_t>(n) * f.m) >> 40);
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, const int16_t* __restrict__ lv,
     const int32_t* __restrict__ r2c, const int32_t* __restrict__ r2off,
-    const int32_t* __restrict__ dmax, int n_r2c, int row_base, Grid g, int ngh, int ngw,
-    int n_groups, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx) {
+    const int32_t* __restrict__ dmax, int n_r2c, int row_base, Grid g, FastDiv div_pf,
+    FastDiv div_nw, int ngw, int n_groups, const int32_t* __restrict__ row_ptr,
+    const int32_t* __restrict__ col_idx) {
   using L = AttnLds<D>;
-  constexpr int KS = D / 16;                  // k-steps of S^T
-  constexpr int DB = D / 32;                  // 32-row blocks of O^T
-  constexpr int GH = QB == 2 ? 2 : 1, G = GH * 2;
+  constexpr int KS = D / 16;  // k-steps of S^T
+  constexpr int DB = D / 32;  // 32-row blocks of O^T
+  constexpr int NONE = 0x7fffffff;
   __shared__ __attribute__((aligned(1024))) char kv0[L::BUF];  // K | V, buffer 0
   __shared__ __attribute__((aligned(1024))) char kv1[L::BUF];  // K | V, buffer 1
   extern __shared__ int32_t r2s[];  // compact radius table (dynamic LDS)
@@ -574,7 +587,8 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_bf16_kernel(
   for (int i = threadIdx.x; i < n_r2c; i += 256) r2s[i] = r2c[i];
   __syncthreads();
 
-  const int groups_per_frame = ngh * ngw;
+  // Group = two horizontally adjacent query tiles of one frame.
+  const int groups_per_frame = g.nh * ngw;
   const int per_head = g.T * groups_per_frame;
   const int bh = gid / per_head;
   const int grem = gid % per_head;
@@ -582,56 +596,58 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_bf16_kernel(
   const int gr = (grem % groups_per_frame) / ngw, gc = grem % ngw;
   const size_t N = static_cast<size_t>(g.T) * g.H * g.W;
 
-  // This wave's query tile and queries (lane % 32 -> tile column, 4 rows per block).
-  const int tr = QB == 2 ? gr * 2 + (wave >> 1) : gr;
-  const int tc = QB == 2 ? gc * 2 + (wave & 1) : gc * 2 + (wave >> 1);
-  const bool tvalid = tr < g.nh && tc < g.nw;
+  // This wave: tile column gc*2 + wave/2, tile rows 4*(wave%2)..+3; lane%32 -> query.
+  const int tc = gc * 2 + (wave >> 1);
+  const bool tvalid = tc < g.nw;
   const int wq = tc * 8 + (col & 7);
-  int hq[QB], toff[QB], tdmax[QB];
-  bool qvalid[QB];
-  size_t nq[QB];
-  bf16x8 qf[QB][KS];
+  const int hq = gr * 8 + 4 * (wave & 1) + (col >> 3);
+  const bool qvalid = tvalid && hq < g.H && wq < g.W;
+  const size_t nq = (static_cast<size_t>(tq) * g.H + (qvalid ? hq : 0)) * g.W + (qvalid ? wq : 0);
+  bf16x8 qf[KS];
+  {
+    const uint16_t* qp = q + (static_cast<size_t>(bh) * N + nq) * D;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row_in_tile = (QB == 2 ? 4 * qb : 4 * (wave & 1)) + (col >> 3);
-    hq[qb] = tr * 8 + row_in_tile;
-    qvalid[qb] = tvalid && hq[qb] < g.H && wq < g.W;
-    const int hh = qvalid[qb] ? hq[qb] : 0, ww = qvalid[qb] ? wq : 0;
-    nq[qb] = (static_cast<size_t>(tq) * g.H + hh) * g.W + ww;
-    const uint16_t* qp = q + (static_cast<size_t>(bh) * N + nq[qb]) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[qb][ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks + 8 * h);
-    const int trow = qvalid[qb] ? lv[static_cast<size_t>(bh) * N + nq[qb]] - row_base : 0;
-    toff[qb] = r2off[trow];
-    tdmax[qb] = qvalid[qb] ? dmax[trow] : -1;
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks + 8 * h);
   }
+  const int trow = qvalid ? lv[static_cast<size_t>(bh) * N + nq] - row_base : 0;
+  const int toff = r2off[trow];
+  const int tdmax = qvalid ? dmax[trow] : -1;
 
-  // Tile lists of the group's query tiles (empty for tiles outside the grid).
-  int ptr[G], endp[G];
+  // Tile lists of the two query tiles, merged on the fly (ascending, unique).
+  // The head of each list is loaded one step ahead of its use.
+  int ptr[2], endp[2], head[2];
 #pragma unroll
-  for (int gi = 0; gi < G; ++gi) {
-    const int rr = QB == 2 ? gr * 2 + (gi >> 1) : gr;
-    const int cc = gc * 2 + (gi & 1);
+  for (int gi = 0; gi < 2; ++gi) {
+    const int cc = gc * 2 + gi;
     ptr[gi] = endp[gi] = 0;
-    if (rr < g.nh && cc < g.nw) {
-      const int64_t row = static_cast<int64_t>(bh) * g.count + (tq * g.nh + rr) * g.nw + cc;
+    if (cc < g.nw) {
+      const int64_t row = static_cast<int64_t>(bh) * g.count + (tq * g.nh + gr) * g.nw + cc;
       ptr[gi] = row_ptr[row];
       endp[gi] = row_ptr[row + 1];
     }
+    head[gi] = ptr[gi] < endp[gi] ? col_idx[ptr[gi]] : NONE;
   }
   auto next_tile = [&]() {
-    int kt = 0x7fffffff;
+    const int kt = min(head[0], head[1]);
 #pragma unroll
-    for (int gi = 0; gi < G; ++gi)
-      if (ptr[gi] < endp[gi]) kt = min(kt, col_idx[ptr[gi]]);
-#pragma unroll
-    for (int gi = 0; gi < G; ++gi)
-      if (ptr[gi] < endp[gi] && col_idx[ptr[gi]] == kt) ++ptr[gi];
+    for (int gi = 0; gi < 2; ++gi)
+      if (head[gi] == kt && kt != NONE) {
+        ++ptr[gi];
+        head[gi] = ptr[gi] < endp[gi] ? col_idx[ptr[gi]] : NONE;
+      }
     return kt;
   };
 
   const uint16_t* kbase = k + static_cast<size_t>(bh) * N * D;
   const uint16_t* vbase = v + static_cast<size_t>(bh) * N * D;
+  struct TileGeo {
+    int tk, kr0, kc0;
+  };
+  auto decode = [&](int kt) {
+    const int tk = fdiv(kt, div_pf), krem = kt - tk * g.per_frame;
+    const int trr = fdiv(krem, div_nw);
+    return TileGeo{tk, trr * 8, (krem - trr * g.nw) * 8};
+  };
 
   // Streams key tile kt into buffer buf.  DMA segment s (1 KB) receives lane
   // l's 16 bytes at s*1KB + 16*l; the lane fetches the (key row, chunk) that
@@ -639,7 +655,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_bf16_kernel(
   // Every wave issues the same number of DMA loads per tile (a wave without a
   // segment of its own repeats the last one, writing identical bytes), so the
   // loop's memory counters follow a fixed pattern.
-  auto issue_part = [&](const uint16_t* base, char* dst, int stride, int nseg, int kr0, int kc0, int tk) {
+  auto issue_part = [&](const uint16_t* base, char* dst, int stride, int nseg, const TileGeo& t) {
 #pragma unroll
     for (int i = 0; i < (L::VSEG + 3) / 4; ++i) {
       if (4 * i >= nseg) break;  // compile-time after unrolling (nseg is KSEG or VSEG)
@@ -648,188 +664,180 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_bf16_kernel(
       const int kk = ob / stride;
       int c = (ob % stride) / 16;
       c = c < D / 8 ? c : 0;
-      const int kr = min(kr0 + (kk >> 3), g.H - 1), kc = min(kc0 + (kk & 7), g.W - 1);
-      const size_t off = ((static_cast<size_t>(tk) * g.H + kr) * g.W + kc) * D + c * 8;
+      const int kr = min(t.kr0 + (kk >> 3), g.H - 1), kc = min(t.kc0 + (kk & 7), g.W - 1);
+      const size_t off = ((static_cast<size_t>(t.tk) * g.H + kr) * g.W + kc) * D + c * 8;
       lds_dma16(base + off, __builtin_amdgcn_readfirstlane(
                                 static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
                                     (__attribute__((address_space(3))) char*)(dst))) + seg * 1024));
     }
   };
   auto issue = [&](int kt, char* buf) {
-    const int tk = kt / g.per_frame, krem = kt % g.per_frame;
-    const int kr0 = (krem / g.nw) * 8, kc0 = (krem % g.nw) * 8;
-    issue_part(kbase, buf, L::KSTR, L::KSEG, kr0, kc0, tk);
-    issue_part(vbase, buf + L::KSEG * 1024, L::VSTR, L::VSEG, kr0, kc0, tk);
+    const TileGeo t = decode(kt);
+    issue_part(kbase, buf, L::KSTR, L::KSEG, t);
+    issue_part(vbase, buf + L::KSEG * 1024, L::VSTR, L::VSEG, t);
   };
 
-  f32x16 oacc[QB][DB];
-  float mref[QB], lsum[QB];
+  f32x16 oacc[DB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    mref[qb] = TRA_NEG_INF;
-    lsum[qb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[qb][db] = (f32x16){0.f};
-  }
+  for (int db = 0; db < DB; ++db) oacc[db] = (f32x16){0.f};
+  float mref = TRA_NEG_INF, lsum = 0.f;
   const float c1 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
   // Per-lane LDS byte bases; every read below adds a compile-time offset.
   const int g4 = lane >> 4, r4 = (lane & 15) >> 2, j4 = lane & 3;
   const int kread = col * L::KSTR + h * 16;
   const int vread = (4 * (g4 >> 1) + r4) * L::VSTR + (16 * (g4 & 1) + 4 * j4) * 2;
+  const int partner = (lane ^ 32) << 2;  // ds_bpermute address of the other half
 
-  auto compute = [&](int kt, const char* buf) {
-    const int tk = kt / g.per_frame, krem = kt % g.per_frame;
-    const int kr0 = (krem / g.nw) * 8, kc0 = (krem % g.nw) * 8;
-    const int delta = tk > tq ? tk - tq : tq - tk;
-    int thr[QB];
+  // S^T block blk (keys 32*blk..+31 of the tile x this wave's 32 queries).
+  auto scores = [&](const char* buf, int blk) {
+    f32x16 acc = (f32x16){0.f};
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int t = r2s[toff[qb] + min(delta, max(tdmax[qb], 0))];
-      thr[qb] = delta <= tdmax[qb] ? t : -1;
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(buf + kread + 32 * blk * L::KSTR + 32 * ks);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], acc, 0, 0, 0);
     }
-    // Exact mask: key (kr0 + 4*blk + a, kc0 + 4*h + b) sits in register i = 4a + b.
-    int dw2[4];
+    return acc;
+  };
+  // Online-softmax bookkeeping for one block of scores; returns P^T as the two
+  // 16-key B operands of the PV product.
+  auto softmax = [&](f32x16& sacc, bf16x8* pf) {
+    float mx = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int kc = kc0 + 4 * h + b, dw = wq - kc;
-      dw2[b] = kc < g.W ? dw * dw : 0x3fffffff;
+    for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sacc[i]), sacc[i + 1]);
+    mx = fmaxf(mx, sacc[15]);
+    // Lazy rescale: the reference (shared by both lanes of a query) moves only
+    // when a score exceeds it by more than 2^8, so probabilities stay <= 256
+    // between rescales.  The test is per lane; only a rescale exchanges the
+    // two half-wave maxima.
+    if (__any(mx * c1 > mref + 8.f)) {
+      mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(mx))));
+      const float mn = fmaxf(mref, mx * c1);
+      const float alpha = mref == TRA_NEG_INF ? 0.f : __builtin_amdgcn_exp2f(mref - mn);
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      mref = mn;
     }
-    const int mindw = min(min(dw2[0], dw2[1]), min(dw2[2], dw2[3]));
-    const int maxdw = max(max(dw2[0], dw2[1]), max(dw2[2], dw2[3]));
-    int remr[QB][2][4];
-    bool doq[QB][2], fullq[QB][2];
+    const float msub = mref == TRA_NEG_INF ? 0.f : mref;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+    for (int j = 0; j < 2; ++j) {
+      uint32_t pk[4];
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int kr = kr0 + 4 * blk + a, dh = hq[qb] - kr;
-          remr[qb][blk][a] = (kr < g.H && thr[qb] >= 0) ? thr[qb] - dh * dh : -1;
-        }
-        const int mxr = max(max(remr[qb][blk][0], remr[qb][blk][1]), max(remr[qb][blk][2], remr[qb][blk][3]));
-        const int mnr = min(min(remr[qb][blk][0], remr[qb][blk][1]), min(remr[qb][blk][2], remr[qb][blk][3]));
-        doq[qb][blk] = __any(mxr >= mindw);
-        fullq[qb][blk] = __all(mnr >= maxdw);
+      for (int x = 0; x < 4; ++x) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[8 * j + 2 * x], c1, -msub));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[8 * j + 2 * x + 1], c1, -msub));
+        lsum += p0;
+        lsum += p1;
+        pk[x] = pack_bf16x2(p0, p1);
       }
-
+      pf[j] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    }
+  };
+  // O^T += V^T P^T for block blk.
+  auto pv = [&](const char* buf, int blk, const bf16x8* pf) {
+    const char* vb = buf + L::KSEG * 1024 + vread;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      bool any = false;
+    for (int j = 0; j < 2; ++j) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) any = any || doq[qb][blk];
-      if (!any) continue;
-      f32x16 sacc[QB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sacc[qb] = (f32x16){0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 af = *reinterpret_cast<const bf16x8*>(buf + kread + 32 * blk * L::KSTR + 32 * ks);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          if (doq[qb][blk]) sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[qb][ks], sacc[qb], 0, 0, 0);
-      }
-      bf16x8 pf[QB][2];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        if (!doq[qb][blk]) continue;
-        if (!fullq[qb][blk]) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (dw2[i & 3] > remr[qb][blk][i >> 2]) sacc[qb][i] = TRA_NEG_INF;
-        }
-        float mx = sacc[qb][0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[qb][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mcand = mx * c1;
-        // Lazy rescale: the reference moves only when a score exceeds it by
-        // more than 2^8, so probabilities stay <= 256 between rescales.
-        if (__any(mcand > mref[qb] + 8.f)) {
-          const float mn = fmaxf(mref[qb], mcand);
-          const float alpha = mref[qb] == TRA_NEG_INF ? 0.f : __builtin_amdgcn_exp2f(mref[qb] - mn);
-          lsum[qb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha;
-          mref[qb] = mn;
-        }
-        const float msub = mref[qb] == TRA_NEG_INF ? 0.f : mref[qb];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          uint32_t pk[4];
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[qb][8 * j + 2 * x], c1, -msub));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[qb][8 * j + 2 * x + 1], c1, -msub));
-            lsum[qb] += p0 + p1;
-            pk[x] = pack_bf16x2(p0, p1);
-          }
-          pf[qb][j] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-        }
-      }
-      const char* vb = buf + L::KSEG * 1024 + vread;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const uint2 lo = lds_read_tr_b(vb + (32 * blk + 16 * j) * L::VSTR + 64 * db);
-          const uint2 hi = lds_read_tr_b(vb + (32 * blk + 16 * j + 8) * L::VSTR + 64 * db);
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            if (doq[qb][blk]) oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][j], oacc[qb][db], 0, 0, 0);
-        }
+      for (int db = 0; db < DB; ++db) {
+        const uint2 lo = lds_read_tr_b(vb + (32 * blk + 16 * j) * L::VSTR + 64 * db);
+        const uint2 hi = lds_read_tr_b(vb + (32 * blk + 16 * j + 8) * L::VSTR + 64 * db);
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[j], oacc[db], 0, 0, 0);
       }
     }
   };
 
-  // Loads complete in order: waiting until at most this wave's DMA loads of
-  // the next tile are outstanding leaves the current tile complete.
-  constexpr int LOADS_NEXT = (L::KSEG + 3) / 4 + (L::VSEG + 3) / 4;
-  // Two-stage pipeline with one DMA site per buffer: kv0 receives tile A while
-  // kv1's tile B is consumed, then kv1 receives the next B while A is consumed.
-  constexpr int NONE = 0x7fffffff;
-  int kt_a = next_tile(), kt_b = NONE;
-  while (true) {
-    if (kt_a != NONE) issue(kt_a, kv0);
-    if (kt_b != NONE) {
-      if (kt_a != NONE) wait_vmcnt<LOADS_NEXT>();
-      else wait_vmcnt<0>();
-      lds_barrier();
-      compute(kt_b, kv1);
-      lds_barrier();
+  auto compute = [&](int kt, const char* buf) {
+    const TileGeo t = decode(kt);
+    const int delta = t.tk > tq ? t.tk - tq : tq - t.tk;
+    const int tv = r2s[toff + min(delta, max(tdmax, 0))];
+    const int thr = delta <= tdmax ? tv : -1;
+    // Exact mask: key (kr0 + 4*blk + a, kc0 + 4*h + b) sits in register i = 4a + b.
+    const bool interior = t.kr0 + 8 <= g.H && t.kc0 + 8 <= g.W;  // wave-uniform
+    const int dwa = wq - t.kc0 - 4 * h;
+    int dw2[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      dw2[b] = __mul24(dwa - b, dwa - b);
+      if (!interior && t.kc0 + 4 * h + b >= g.W) dw2[b] = 0x3fffffff;
     }
-    if (kt_a == NONE) break;
-    kt_b = next_tile();
-    if (kt_b != NONE) {
-      issue(kt_b, kv1);
-      wait_vmcnt<LOADS_NEXT>();
-    } else {
-      wait_vmcnt<0>();
+    const int mindw = min(min(dw2[0], dw2[1]), min(dw2[2], dw2[3]));
+    const int maxdw = max(max(dw2[0], dw2[1]), max(dw2[2], dw2[3]));
+    int remr[2][4];
+    bool doq[2], fullq[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int dha = hq - t.kr0 - 4 * blk;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        remr[blk][a] = thr - __mul24(dha - a, dha - a);
+        if (!interior && t.kr0 + 4 * blk + a >= g.H) remr[blk][a] = -1;
+      }
+      if (thr < 0) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) remr[blk][a] = -1;
+      }
+      const int mxr = max(max(remr[blk][0], remr[blk][1]), max(remr[blk][2], remr[blk][3]));
+      const int mnr = min(min(remr[blk][0], remr[blk][1]), min(remr[blk][2], remr[blk][3]));
+      doq[blk] = __any(mxr >= mindw);
+      fullq[blk] = __all(mnr >= maxdw);
     }
+    // Both halves' score MFMAs are issued before either softmax, so the vector
+    // work on one half overlaps the matrix work on the other.
+    f32x16 sc[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+      if (doq[blk]) sc[blk] = scores(buf, blk);
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      if (!doq[blk]) continue;
+      if (!fullq[blk]) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (dw2[i & 3] > remr[blk][i >> 2]) sc[blk][i] = TRA_NEG_INF;
+      }
+      bf16x8 pf[2];
+      softmax(sc[blk], pf);
+      pv(buf, blk, pf);
+    }
+  };
+
+  // One barrier per key tile.  At the barrier of tile e every wave has its
+  // own DMA loads of tile e complete (the only ones outstanding) and has
+  // finished computing tile e-1, so the data of e is visible and the other
+  // buffer is free: tile e+1 is then streamed into it while e is consumed.
+  int kt = next_tile();
+  if (kt != NONE) issue(kt, kv0);
+  while (kt != NONE) {
+    wait_vmcnt<0>();
     lds_barrier();
-    compute(kt_a, kv0);
+    int kn = next_tile();
+    if (kn != NONE) issue(kn, kv1);
+    compute(kt, kv0);
+    kt = kn;
+    if (kt == NONE) break;
+    wait_vmcnt<0>();
     lds_barrier();
-    kt_a = next_tile();
+    kn = next_tile();
+    if (kn != NONE) issue(kn, kv0);
+    compute(kt, kv1);
+    kt = kn;
   }
 
+  const float ltot = lsum + __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(lsum)));
+  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  if (qvalid) {
+    uint16_t* op = o + (static_cast<size_t>(bh) * N + nq) * D;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float ltot = lsum[qb] + __shfl_xor(lsum[qb], 32);
-    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    if (qvalid[qb]) {
-      uint16_t* op = o + (static_cast<size_t>(bh) * N + nq[qb]) * D;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int d0 = 32 * db + 8 * a + 4 * h;
-          const uint2 out4 =
-              make_uint2(pack_bf16x2(oacc[qb][db][4 * a] * inv, oacc[qb][db][4 * a + 1] * inv),
-                         pack_bf16x2(oacc[qb][db][4 * a + 2] * inv, oacc[qb][db][4 * a + 3] * inv));
-          *reinterpret_cast<uint2*>(op + d0) = out4;
-        }
-    }
+      for (int a = 0; a < 4; ++a) {
+        const int d0 = 32 * db + 8 * a + 4 * h;
+        const uint2 out4 = make_uint2(pack_bf16x2(oacc[db][4 * a] * inv, oacc[db][4 * a + 1] * inv),
+                                      pack_bf16x2(oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv));
+        *reinterpret_cast<uint2*>(op + d0) = out4;
+      }
   }
 }
 
@@ -1043,16 +1051,6 @@ size_t attention_lds_bytes(int d, int n_r2c) {
   return kv + static_cast<size_t>(n_r2c) * sizeof(int32_t);
 }
 
-// Query blocks of 32 per wave in the bf16 attention kernel (1 or 2); the
-// environment variable TRA_ATTN_QB selects one for tuning, default 1.
-static int attention_query_blocks() {
-  static const int qb = [] {
-    const char* e = getenv("TRA_ATTN_QB");
-    return (e && e[0] == '2') ? 2 : 1;
-  }();
-  return qb;
-}
-
 hipError_t launch_attention(int dtype, int d, const void* q, const void* k, const void* v,
                             void* o, const int16_t* lv, const RadiusTable& tab, int row_base,
                             int BH, const Grid& tiles, const int32_t* row_ptr,
@@ -1064,21 +1062,18 @@ hipError_t launch_attention(int dtype, int d, const void* q, const void* k, cons
     const auto* kk = static_cast<const uint16_t*>(k);
     const auto* vv = static_cast<const uint16_t*>(v);
     auto* oo = static_cast<uint16_t*>(o);
-    const int qb = attention_query_blocks();
-    const int ngh = qb == 2 ? (tiles.nh + 1) / 2 : tiles.nh, ngw = (tiles.nw + 1) / 2;
-    const int64_t groups = static_cast<int64_t>(BH) * tiles.T * ngh * ngw;
+    const int ngw = (tiles.nw + 1) / 2;
+    const int64_t groups = static_cast<int64_t>(BH) * tiles.T * tiles.nh * ngw;
     const unsigned grid = static_cast<unsigned>((groups + 7) / 8 * 8);
     const int ng = static_cast<int>(groups);
     const size_t lds_tab = static_cast<size_t>(tab.n_r2c) * sizeof(int32_t);
-#define TRA_ATTN(DD, QQ)                                                                        \
-  attn_bf16_kernel<DD, QQ><<<grid, 256, lds_tab, s>>>(qq, kk, vv, oo, lv, tab.r2c, tab.r2off, tab.dmax, \
-                                                 tab.n_r2c, row_base, tiles, ngh, ngw, ng, row_ptr, \
-                                                 col_idx)
-    if (d == 128) {
-      if (qb == 2) TRA_ATTN(128, 2); else TRA_ATTN(128, 1);
-    } else {
-      if (qb == 2) TRA_ATTN(64, 2); else TRA_ATTN(64, 1);
-    }
+    const FastDiv dpf = make_fastdiv(tiles.per_frame), dnw = make_fastdiv(tiles.nw);
+#define TRA_ATTN(DD)                                                                          \
+  attn_bf16_kernel<DD><<<grid, 256, lds_tab, s>>>(qq, kk, vv, oo, lv, tab.r2c, tab.r2off, tab.dmax, \
+                                                  tab.n_r2c, row_base, tiles, dpf, dnw, ngw, ng,     \
+                                                  row_ptr, col_idx)
+    if (d == 128) TRA_ATTN(128);
+    else TRA_ATTN(64);
 #undef TRA_ATTN
   } else {
     const auto* qq = static_cast<const float*>(q);
