@@ -525,6 +525,15 @@ __device__ __forceinline__ void lds_dma16(const void* gaddr, uint32_t lds_base) 
                : "memory", "m0");
 }
 
+// The same DMA addressed as a wave-uniform 64-bit base plus a per-lane 32-bit
+// byte offset (no vector address arithmetic at the call site).
+__device__ __forceinline__ void lds_dma16_so(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   // s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left unconstrained)
@@ -654,27 +663,64 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   // the padded layout puts there (pad chunks re-fetch the row's first chunk).
   // Every wave issues the same number of DMA loads per tile (a wave without a
   // segment of its own repeats the last one, writing identical bytes), so the
-  // loop's memory counters follow a fixed pattern.
-  auto issue_part = [&](const uint16_t* base, char* dst, int stride, int nseg, const TileGeo& t) {
+  // loop's memory counters follow a fixed pattern.  A lane's byte offset from
+  // the tile's first key is fixed per segment; it is computed once here and
+  // the interior tiles' loads need no address arithmetic.
+  constexpr int NK = (L::KSEG + 3) / 4, NV = (L::VSEG + 3) / 4;
+  struct SegLane {
+    int kr, kc, c;  // key row / column within the tile, 16-byte chunk
+  };
+  auto seg_lane = [&](int stride, int nseg, int i) {
+    const int seg = min(wave + 4 * i, nseg - 1);
+    const int ob = seg * 1024 + lane * 16;
+    const int kk = ob / stride;
+    const int c = (ob % stride) / 16;
+    return SegLane{kk >> 3, kk & 7, c < D / 8 ? c : 0};
+  };
+  uint32_t koff[NK], voff[NV];
 #pragma unroll
-    for (int i = 0; i < (L::VSEG + 3) / 4; ++i) {
-      if (4 * i >= nseg) break;  // compile-time after unrolling (nseg is KSEG or VSEG)
-      const int seg = min(wave + 4 * i, nseg - 1);
-      const int ob = seg * 1024 + lane * 16;
-      const int kk = ob / stride;
-      int c = (ob % stride) / 16;
-      c = c < D / 8 ? c : 0;
-      const int kr = min(t.kr0 + (kk >> 3), g.H - 1), kc = min(t.kc0 + (kk & 7), g.W - 1);
-      const size_t off = ((static_cast<size_t>(t.tk) * g.H + kr) * g.W + kc) * D + c * 8;
-      lds_dma16(base + off, __builtin_amdgcn_readfirstlane(
-                                static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-                                    (__attribute__((address_space(3))) char*)(dst))) + seg * 1024));
-    }
+  for (int i = 0; i < NK; ++i) {
+    const SegLane sl = seg_lane(L::KSTR, L::KSEG, i);
+    koff[i] = static_cast<uint32_t>((sl.kr * g.W + sl.kc) * D * 2 + sl.c * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const SegLane sl = seg_lane(L::VSTR, L::VSEG, i);
+    voff[i] = static_cast<uint32_t>((sl.kr * g.W + sl.kc) * D * 2 + sl.c * 16);
+  }
+  auto lds_seg = [&](char* dst, int nseg, int i) {
+    return __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(dst))) +
+        min(wave + 4 * i, nseg - 1) * 1024);
   };
   auto issue = [&](int kt, char* buf) {
     const TileGeo t = decode(kt);
-    issue_part(kbase, buf, L::KSTR, L::KSEG, t);
-    issue_part(vbase, buf + L::KSEG * 1024, L::VSTR, L::VSEG, t);
+    char* vbuf = buf + L::KSEG * 1024;
+    if (t.kr0 + 8 <= g.H && t.kc0 + 8 <= g.W) {
+      const size_t tile_off = ((static_cast<size_t>(t.tk) * g.H + t.kr0) * g.W + t.kc0) * D;
+      const uint16_t* kb = kbase + tile_off;
+      const uint16_t* vb = vbase + tile_off;
+#pragma unroll
+      for (int i = 0; i < NK; ++i) lds_dma16_so(kb, koff[i], lds_seg(buf, L::KSEG, i));
+#pragma unroll
+      for (int i = 0; i < NV; ++i) lds_dma16_so(vb, voff[i], lds_seg(vbuf, L::VSEG, i));
+    } else {
+      // Ragged tile at the bottom/right edge: clamp rows and columns.
+#pragma unroll
+      for (int i = 0; i < NK; ++i) {
+        const SegLane sl = seg_lane(L::KSTR, L::KSEG, i);
+        const int kr = min(t.kr0 + sl.kr, g.H - 1), kc = min(t.kc0 + sl.kc, g.W - 1);
+        lds_dma16(kbase + ((static_cast<size_t>(t.tk) * g.H + kr) * g.W + kc) * D + sl.c * 8,
+                  lds_seg(buf, L::KSEG, i));
+      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const SegLane sl = seg_lane(L::VSTR, L::VSEG, i);
+        const int kr = min(t.kr0 + sl.kr, g.H - 1), kc = min(t.kc0 + sl.kc, g.W - 1);
+        lds_dma16(vbase + ((static_cast<size_t>(t.tk) * g.H + kr) * g.W + kc) * D + sl.c * 8,
+                  lds_seg(vbuf, L::VSEG, i));
+      }
+    }
   };
 
   f32x16 oacc[DB];
