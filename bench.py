@@ -34,6 +34,21 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBPS = 8000.0
 
 
+def measured_traffic():
+    """HBM-side bytes per attention launch from the committed rocprofv3 byte
+    counters (calibrated against a plain copy), or None when the kernel source
+    has changed since they were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "attention_traffic.json")))
+        src = open(os.path.join(ROOT, "sparse_self_attention_amd", "csrc", "tra_kernels.hip"), "rb").read()
+    except OSError:
+        return None
+    if hashlib.sha256(src).hexdigest() != rec.get("kernel_source_sha256"):
+        return None
+    return rec["bytes_read_per_launch"] + rec["bytes_written_per_launch"]
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -186,7 +201,8 @@ def main():
                  "gbps": plan_bytes / (plan_ms * 1e-3) / 1e9,
                  "frac_hbm_peak": plan_bytes / (plan_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+                     "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": measured_traffic() if cfg.name == WORKLOAD else None},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
