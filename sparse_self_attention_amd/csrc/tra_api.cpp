@@ -69,6 +69,9 @@ tra_status check_params(const tra_shape* s, const tra_params* p, Table* tab) {
   if (p->pool_h < 1 || p->pool_w < 1) return fail(TRA_ERR_INVALID_ARG, "pool_h and pool_w must be >= 1");
   if (p->tile_h != 8 || p->tile_w != 8)
     return fail(TRA_ERR_INVALID_ARG, "the device kernels use 8x8 tiles (tile_h = tile_w = 8)");
+  if (s->dtype == TRA_BF16 &&
+      tra::pair_list_words(tra::make_grid(s->T, s->H, s->W, 8, 8)) > tra::kMaxPairListWords)
+    return fail(TRA_ERR_SHAPE, "bf16 attention supports at most 393216 key tiles (8x8) per head");
   if (!std::isfinite(p->radius_override) || p->radius_override >= 32768.0)
     return fail(TRA_ERR_INVALID_ARG, "radius_override must be finite and below 32768");
   const int T = s->T;
@@ -149,6 +152,9 @@ struct tra_plan {
   int32_t* row_ptr = nullptr;
   int32_t* col_idx = nullptr;
   int64_t col_cap = 0;
+  int32_t* pair_list = nullptr;  // bf16 only: merged lists of query-tile pairs, 2 int32 per entry
+  int64_t pair_cap = 0;          // entries
+  int32_t* pair_len = nullptr;
   int64_t* totals = nullptr;      // device: nnz, longest row, overflow flag
   int64_t* totals_host = nullptr; // pinned
   int64_t nnz = 0;
@@ -160,7 +166,7 @@ namespace {
 void release(tra_plan* p) {
   if (!p) return;
   void* bufs[] = {p->kbar, p->H, p->lv, p->r2, p->dmax, p->r2c, p->r2off, p->pool_w,
-                  p->counts, p->row_ptr, p->col_idx, p->totals};
+                  p->counts, p->row_ptr, p->col_idx, p->pair_list, p->pair_len, p->totals};
   for (void* b : bufs)
     if (b) (void)hipFree(b);
   if (p->totals_host) (void)hipHostFree(p->totals_host);
@@ -196,6 +202,16 @@ tra_status build(tra_plan* p, const void* q, const void* k, hipStream_t st) {
   }
   TRA_HIP(tra::launch_csr_fill(p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, p->row_ptr,
                                p->col_idx, st));
+  if (s.dtype == TRA_BF16) {
+    if (p->nnz > p->pair_cap) {
+      if (p->pair_list) TRA_HIP(hipFree(p->pair_list));
+      p->pair_list = nullptr;
+      p->pair_cap = 0;
+      TRA_HIP(hipMalloc(&p->pair_list, p->col_cap * 2 * sizeof(int32_t)));
+      p->pair_cap = p->col_cap;
+    }
+    TRA_HIP(tra::launch_pair_lists(p->row_ptr, p->col_idx, p->BH, p->tiles, p->pair_list, p->pair_len, st));
+  }
   return TRA_OK;
 }
 
@@ -274,6 +290,10 @@ tra_status tra_plan_create(const tra_shape* shape, const tra_params* params, con
   TRA_HIP_P(hipMalloc(&p->counts, p->n_rows * sizeof(int32_t)));
   TRA_HIP_P(hipMalloc(&p->row_ptr, (p->n_rows + 1) * sizeof(int32_t)));
   TRA_HIP_P(hipMalloc(&p->totals, 4 * sizeof(int64_t)));
+  if (shape->dtype == TRA_BF16) {
+    const int64_t n_pairs = static_cast<int64_t>(p->BH) * p->tiles.T * p->tiles.nh * ((p->tiles.nw + 1) / 2);
+    TRA_HIP_P(hipMalloc(&p->pair_len, n_pairs * sizeof(int32_t)));
+  }
   TRA_HIP_P(hipHostMalloc(&p->totals_host, 4 * sizeof(int64_t)));
   if (params->radius_override >= 0.0)
     TRA_HIP_P(hipMemsetAsync(p->kbar, 0, static_cast<size_t>(p->BH) * p->pool.count * shape->head_dim * es, hs));
@@ -309,7 +329,7 @@ tra_status tra_attention(const tra_plan* plan, const void* q, const void* k, con
                              static_cast<int>(plan->table.r2c.size()), s.T};
   TRA_HIP(tra::launch_attention(s.dtype, s.head_dim, q, k, v, o, plan->lv, tab, plan->row_base,
                                 plan->BH, plan->tiles, plan->row_ptr, plan->col_idx,
-                                static_cast<hipStream_t>(stream)));
+                                plan->pair_list, plan->pair_len, static_cast<hipStream_t>(stream)));
   return TRA_OK;
 }
 

@@ -62,7 +62,18 @@ hipError_t launch_csr_fill(const int16_t* lv, const int32_t* r2, const int32_t* 
 hipError_t launch_attention(int dtype, int d, const void* q, const void* k, const void* v,
                             void* o, const int16_t* lv, const RadiusTable& tab, int row_base,
                             int BH, const Grid& tiles, const int32_t* row_ptr,
-                            const int32_t* col_idx, hipStream_t s);
+                            const int32_t* col_idx, const int32_t* pair_list,
+                            const int32_t* pair_len, hipStream_t s);
+// Merged tile lists of horizontally adjacent query-tile pairs (the bf16
+// attention kernel's unit of work): entries of two int32 each, pair p's list
+// at pair_list + 2 * row_ptr[first row of p], length pair_len[p].  The
+// buffer needs 2 * nnz entries of int32.
+hipError_t launch_pair_lists(const int32_t* row_ptr, const int32_t* col_idx, int BH,
+                             const Grid& tiles, int32_t* pair_list, int32_t* pair_len,
+                             hipStream_t s);
+// LDS words of the pair-list bitmap (one bit per key tile of a head).
+int pair_list_words(const Grid& tiles);
+constexpr int kMaxPairListWords = 12288;  // 48 KB of LDS
 // Dynamic LDS the bf16 attention kernel needs for its staged K/V buffers
 // plus a compact radius table of n_r2c entries; 0 if it exceeds the device limit.
 size_t attention_lds_bytes(int d, int n_r2c);

@@ -445,6 +445,64 @@ __global__ __launch_bounds__(256) void csr_kernel(const int16_t* __restrict__ lv
   if (!FILL && lane == 0) counts[row] = count;
 }
 
+// Union of the tile lists of two horizontally adjacent query tiles, the unit
+// of work of the bf16 attention kernel.  Every non-empty column run of a query
+// tile's list contains the tile's own column, so per (frame, tile row) the
+// union of the two runs is again one run; the union is formed here once per
+// plan with a bitmap over the head's key tiles in LDS, then written out in
+// ascending order as (frame | ragged << 31, row0 | col0 << 16), where ragged
+// marks a tile cut by the bottom or right edge of the grid.  Pair p's list
+// goes where its first tile's CSR row starts (the two rows are adjacent and
+// the union is no longer than both), its length to pair_len[p].
+// One workgroup per pair; nwords = ceil(tiles per head / 32) words of LDS.
+__global__ __launch_bounds__(256) void pair_kernel(const int32_t* __restrict__ row_ptr,
+                                                  const int32_t* __restrict__ col_idx, Grid g,
+                                                  int ngw, int per_head, int nwords,
+                                                  int2* __restrict__ out,
+                                                  int32_t* __restrict__ out_len) {
+  extern __shared__ uint32_t bits[];
+  __shared__ int part[256];
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x / per_head, pair = blockIdx.x % per_head;
+  const int gc = pair % ngw, fr = pair / ngw;  // fr = frame * nh + tile row
+  const int64_t row = static_cast<int64_t>(bh) * g.count + static_cast<int64_t>(fr) * g.nw + 2 * gc;
+  const int beg = row_ptr[row];
+  const int end = row_ptr[row + (2 * gc + 1 < g.nw ? 2 : 1)];
+  for (int w = tid; w < nwords; w += 256) bits[w] = 0u;
+  __syncthreads();
+  for (int e = beg + tid; e < end; e += 256) {
+    const int t = col_idx[e];
+    atomicOr(&bits[t >> 5], 1u << (t & 31));
+  }
+  __syncthreads();
+  const int per = (nwords + 255) / 256;
+  const int w0 = min(nwords, tid * per), w1 = min(nwords, w0 + per);
+  int cnt = 0;
+  for (int w = w0; w < w1; ++w) cnt += __popc(bits[w]);
+  part[tid] = cnt;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int pos = beg + part[tid] - cnt;
+  for (int w = w0; w < w1; ++w) {
+    uint32_t m = bits[w];
+    while (m) {
+      const int t = w * 32 + __builtin_ctz(m);
+      m &= m - 1u;
+      const int tk = t / g.per_frame, rem = t - tk * g.per_frame;
+      const int tr = rem / g.nw, tc = rem - tr * g.nw;
+      const int kr0 = tr * g.th, kc0 = tc * g.tw;
+      const bool ragged = kr0 + g.th > g.H || kc0 + g.tw > g.W;
+      out[pos++] = make_int2(tk | (ragged ? static_cast<int>(0x80000000u) : 0), kr0 | (kc0 << 16));
+    }
+  }
+  if (tid == 255) out_len[blockIdx.x] = part[255];
+}
+
 // Exclusive scan of per-row counts.  One workgroup of 1024 threads.
 // totals[0] = nnz, totals[1] = longest row, totals[2] = 1 if nnz >= 2^31.
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ counts,
@@ -528,6 +586,14 @@ __device__ __forceinline__ void lds_dma16(const void* gaddr, uint32_t lds_base) 
 // The same DMA addressed as a wave-uniform 64-bit base plus a per-lane 32-bit
 // byte offset (no vector address arithmetic at the call site).
 __device__ __forceinline__ void lds_dma16_so(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  // The base is wave-uniform by construction; readfirstlane lets the compiler
+  // keep it in SGPRs (a no-op when it already is there).
+  // (readfirstlane yields int: each half goes through uint32_t so that the
+  // low half is zero-extended, never sign-extended.)
+  const uint64_t b = reinterpret_cast<uint64_t>(sbase);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b))));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b >> 32))));
+  sbase = reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(sbase), "s"(lds_base)
@@ -555,27 +621,14 @@ template <int D> struct AttnLds {
   static_assert(64 * KSTR % 1024 == 0 && 64 * VSTR % 1024 == 0, "tile must be whole segments");
 };
 
-// Division by a constant divisor d (1 <= d < 2^16) for 0 <= n < 2^24:
-// floor(n / d) = (n * m) >> 40 with m = ceil(2^40 / d).
-struct FastDiv {
-  uint64_t m;
-  int d;
-};
-__host__ __device__ inline FastDiv make_fastdiv(int d) {
-  return FastDiv{((uint64_t(1) << 40) + static_cast<uint64_t>(d) - 1) / static_cast<uint64_t>(d), d};
-}
-__device__ __forceinline__ int fdiv(int n, const FastDiv& f) {
-  return static_cast<int>((static_cast<uint64_t>(n) * f.m) >> 40);
-}
-
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, const int16_t* __restrict__ lv,
     const int32_t* __restrict__ r2c, const int32_t* __restrict__ r2off,
-    const int32_t* __restrict__ dmax, int n_r2c, int row_base, Grid g, FastDiv div_pf,
-    FastDiv div_nw, int ngw, int n_groups, const int32_t* __restrict__ row_ptr,
-    const int32_t* __restrict__ col_idx) {
+    const int32_t* __restrict__ dmax, int n_r2c, int row_base, Grid g, int ngw, int n_groups,
+    const int32_t* __restrict__ row_ptr, const int2* __restrict__ pair_list,
+    const int32_t* __restrict__ pair_len) {
   using L = AttnLds<D>;
   constexpr int KS = D / 16;  // k-steps of S^T
   constexpr int DB = D / 32;  // 32-row blocks of O^T
@@ -622,41 +675,34 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   const int toff = r2off[trow];
   const int tdmax = qvalid ? dmax[trow] : -1;
 
-  // Tile lists of the two query tiles, merged on the fly (ascending, unique).
-  // The head of each list is loaded one step ahead of its use.
-  int ptr[2], endp[2], head[2];
-#pragma unroll
-  for (int gi = 0; gi < 2; ++gi) {
-    const int cc = gc * 2 + gi;
-    ptr[gi] = endp[gi] = 0;
-    if (cc < g.nw) {
-      const int64_t row = static_cast<int64_t>(bh) * g.count + (tq * g.nh + gr) * g.nw + cc;
-      ptr[gi] = row_ptr[row];
-      endp[gi] = row_ptr[row + 1];
+  // The union of the two query tiles' tile lists, ascending, prepared by the
+  // plan: entry (frame | ragged << 31, row0 | col0 << 16).  It is read through
+  // 64-entry windows held in VGPRs (lane i holds entry 64*w + i) and taken out
+  // with v_readlane; the window after the current one is loaded when the
+  // current one is entered, long before its first use.  (Vector loads keep the
+  // list out of the LDS wait counter: a scalar load in flight would hold up
+  // every LDS wait.)
+  const int n_tiles = pair_len[gid];
+  const int2* lst = pair_list + row_ptr[static_cast<int64_t>(bh) * g.count + (tq * g.nh + gr) * g.nw + gc * 2];
+  int2 cur = lane < n_tiles ? lst[lane] : make_int2(0, 0);
+  int2 nxt = 64 + lane < n_tiles ? lst[64 + lane] : make_int2(0, 0);
+  struct TileGeo {
+    int tk, kr0, kc0;
+    bool ragged;
+  };
+  // Entry j (entries are read in order, each once).
+  auto entry = [&](int j) {
+    if ((j & 63) == 0 && j > 0) {
+      cur = nxt;
+      nxt = j + 64 + lane < n_tiles ? lst[j + 64 + lane] : make_int2(0, 0);
     }
-    head[gi] = ptr[gi] < endp[gi] ? col_idx[ptr[gi]] : NONE;
-  }
-  auto next_tile = [&]() {
-    const int kt = min(head[0], head[1]);
-#pragma unroll
-    for (int gi = 0; gi < 2; ++gi)
-      if (head[gi] == kt && kt != NONE) {
-        ++ptr[gi];
-        head[gi] = ptr[gi] < endp[gi] ? col_idx[ptr[gi]] : NONE;
-      }
-    return kt;
+    const int ex = __builtin_amdgcn_readlane(cur.x, j & 63);
+    const int ey = __builtin_amdgcn_readlane(cur.y, j & 63);
+    return TileGeo{ex & 0x7fffffff, ey & 0xffff, ey >> 16, ex < 0};
   };
 
   const uint16_t* kbase = k + static_cast<size_t>(bh) * N * D;
   const uint16_t* vbase = v + static_cast<size_t>(bh) * N * D;
-  struct TileGeo {
-    int tk, kr0, kc0;
-  };
-  auto decode = [&](int kt) {
-    const int tk = fdiv(kt, div_pf), krem = kt - tk * g.per_frame;
-    const int trr = fdiv(krem, div_nw);
-    return TileGeo{tk, trr * 8, (krem - trr * g.nw) * 8};
-  };
 
   // Streams key tile kt into buffer buf.  DMA segment s (1 KB) receives lane
   // l's 16 bytes at s*1KB + 16*l; the lane fetches the (key row, chunk) that
@@ -693,10 +739,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
         static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(dst))) +
         min(wave + 4 * i, nseg - 1) * 1024);
   };
-  auto issue = [&](int kt, char* buf) {
-    const TileGeo t = decode(kt);
+  auto issue = [&](const TileGeo& t, char* buf) {
     char* vbuf = buf + L::KSEG * 1024;
-    if (t.kr0 + 8 <= g.H && t.kc0 + 8 <= g.W) {
+    if (!t.ragged) {
       const size_t tile_off = ((static_cast<size_t>(t.tk) * g.H + t.kr0) * g.W + t.kc0) * D;
       const uint16_t* kb = kbase + tile_off;
       const uint16_t* vb = vbase + tile_off;
@@ -745,26 +790,45 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     return acc;
   };
   // Online-softmax bookkeeping for one block of scores; returns P^T as the two
-  // 16-key B operands of the PV product.
-  auto softmax = [&](f32x16& sacc, bf16x8* pf) {
+  // 16-key B operands of the PV product.  When `partial`, msk[x] holds the
+  // radius mask of elements 2x, 2x+1 as two 16-bit halves (all ones = keep);
+  // it is applied to the packed bf16 probabilities, and the running sum adds
+  // the same bf16 values the product uses.
+  //
+  // Lazy rescale: the reference (shared by both lanes of a query) moves only
+  // when a score exceeds it by more than 2^8, so probabilities stay <= 256
+  // between moves.  The cheap test looks at the unmasked scores; when it
+  // fires, the exact masked maximum decides whether the reference moves.
+  auto softmax = [&](f32x16& sacc, bf16x8* pf, const uint32_t* msk, bool partial) {
     float mx = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
 #pragma unroll
     for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sacc[i]), sacc[i + 1]);
     mx = fmaxf(mx, sacc[15]);
-    // Lazy rescale: the reference (shared by both lanes of a query) moves only
-    // when a score exceeds it by more than 2^8, so probabilities stay <= 256
-    // between rescales.  The test is per lane; only a rescale exchanges the
-    // two half-wave maxima.
     if (__any(mx * c1 > mref + 8.f)) {
-      mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(mx))));
-      const float mn = fmaxf(mref, mx * c1);
-      const float alpha = mref == TRA_NEG_INF ? 0.f : __builtin_amdgcn_exp2f(mref - mn);
-      lsum *= alpha;
+      if (partial) {
+        mx = TRA_NEG_INF;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-      mref = mn;
+        for (int i = 0; i < 16; ++i) {
+          const int keep = (i & 1) ? static_cast<int>(msk[i >> 1]) >> 16
+                                   : static_cast<int>(msk[i >> 1] << 16) >> 16;
+          mx = fmaxf(mx, __int_as_float((__float_as_int(sacc[i]) & keep) |
+                                        (__float_as_int(TRA_NEG_INF) & ~keep)));
+        }
+      }
+      mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(mx))));
+      if (__any(mx * c1 > mref + 8.f)) {
+        const float mn = fmaxf(mref, mx * c1);
+        const float alpha = mref == TRA_NEG_INF ? 0.f : __builtin_amdgcn_exp2f(mref - mn);
+        lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+        mref = mn;
+      }
     }
+    // With no kept key seen yet the reference is -inf: the probabilities of
+    // this block are then all masked, and any value works.
     const float msub = mref == TRA_NEG_INF ? 0.f : mref;
+    const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       uint32_t pk[4];
@@ -772,9 +836,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
       for (int x = 0; x < 4; ++x) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[8 * j + 2 * x], c1, -msub));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[8 * j + 2 * x + 1], c1, -msub));
-        lsum += p0;
-        lsum += p1;
         pk[x] = pack_bf16x2(p0, p1);
+        if (partial) pk[x] &= msk[4 * j + x];
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[x]), ones, lsum, false);
       }
       pf[j] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
     }
@@ -794,40 +858,46 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     }
   };
 
-  auto compute = [&](int kt, const char* buf) {
-    const TileGeo t = decode(kt);
+  // Radius mask.  Key (kr0 + 4*blk + a, kc0 + 4*h + b) sits in register
+  // i = 4a + b of block blk; it is kept iff dw2[b] < rr[4*blk + a], with
+  // dw2[b] = (w_q - w_k)^2 and rr = R2 + 1 - (h_q - h_k)^2 (R2 = -1 for an
+  // inactive frame).  Keys outside the grid get sentinels that fail the test:
+  // rr <= 2^30 (radius tables stay below 2^30), so the differences below
+  // stay inside int32.
+  constexpr int COL_OUT = 0x40000001, ROW_OUT = -1;
+  // When `more`, the LDS DMA of the next tile (tn into nbuf) is issued once
+  // the score MFMAs are in flight, so that the matrix unit works while the
+  // DMA instructions wait for the address unit (a wave's DMA issue otherwise
+  // stalls behind its workgroup's burst).
+  auto compute = [&](const TileGeo& t, const char* buf, bool more, const TileGeo& tn, char* nbuf) {
     const int delta = t.tk > tq ? t.tk - tq : tq - t.tk;
     const int tv = r2s[toff + min(delta, max(tdmax, 0))];
-    const int thr = delta <= tdmax ? tv : -1;
-    // Exact mask: key (kr0 + 4*blk + a, kc0 + 4*h + b) sits in register i = 4a + b.
-    const bool interior = t.kr0 + 8 <= g.H && t.kc0 + 8 <= g.W;  // wave-uniform
+    const int thr1 = delta <= tdmax ? tv + 1 : 0;
     const int dwa = wq - t.kc0 - 4 * h;
-    int dw2[4];
+    const int dha = hq - t.kr0;
+    int dw2[4], rr[8];
+    dw2[0] = __mul24(dwa, dwa);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      dw2[b] = __mul24(dwa - b, dwa - b);
-      if (!interior && t.kc0 + 4 * h + b >= g.W) dw2[b] = 0x3fffffff;
+    for (int b = 1; b < 4; ++b) dw2[b] = dw2[b - 1] - 2 * dwa + (2 * b - 1);
+    rr[0] = thr1 - __mul24(dha, dha);
+#pragma unroll
+    for (int a = 1; a < 8; ++a) rr[a] = rr[a - 1] + 2 * dha - (2 * a - 1);
+    if (t.ragged) {  // tile at the bottom/right edge of the grid (wave-uniform)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        if (t.kc0 + 4 * h + b >= g.W) dw2[b] = COL_OUT;
+#pragma unroll
+      for (int a = 0; a < 8; ++a)
+        if (t.kr0 + a >= g.H) rr[a] = ROW_OUT;
     }
     const int mindw = min(min(dw2[0], dw2[1]), min(dw2[2], dw2[3]));
     const int maxdw = max(max(dw2[0], dw2[1]), max(dw2[2], dw2[3]));
-    int remr[2][4];
     bool doq[2], fullq[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      const int dha = hq - t.kr0 - 4 * blk;
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        remr[blk][a] = thr - __mul24(dha - a, dha - a);
-        if (!interior && t.kr0 + 4 * blk + a >= g.H) remr[blk][a] = -1;
-      }
-      if (thr < 0) {
-#pragma unroll
-        for (int a = 0; a < 4; ++a) remr[blk][a] = -1;
-      }
-      const int mxr = max(max(remr[blk][0], remr[blk][1]), max(remr[blk][2], remr[blk][3]));
-      const int mnr = min(min(remr[blk][0], remr[blk][1]), min(remr[blk][2], remr[blk][3]));
-      doq[blk] = __any(mxr >= mindw);
-      fullq[blk] = __all(mnr >= maxdw);
+      const int* r = rr + 4 * blk;
+      doq[blk] = __any(mindw < max(max(r[0], r[1]), max(r[2], r[3])));
+      fullq[blk] = __all(maxdw < min(min(r[0], r[1]), min(r[2], r[3])));
     }
     // Both halves' score MFMAs are issued before either softmax, so the vector
     // work on one half overlaps the matrix work on the other.
@@ -835,16 +905,23 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
       if (doq[blk]) sc[blk] = scores(buf, blk);
+    if (more) issue(tn, nbuf);
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       if (!doq[blk]) continue;
-      if (!fullq[blk]) {
+      uint32_t msk[8];
+      const bool partial = !fullq[blk];
+      if (partial) {
+        // Sign bytes of the two differences -> 16-bit keep masks.
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (dw2[i & 3] > remr[blk][i >> 2]) sc[blk][i] = TRA_NEG_INF;
+        for (int x = 0; x < 8; ++x) {
+          const int ra = rr[4 * blk + (x >> 1)];
+          const int t0 = dw2[2 * (x & 1)] - ra, t1 = dw2[2 * (x & 1) + 1] - ra;
+          msk[x] = __builtin_amdgcn_perm(static_cast<uint32_t>(t1), static_cast<uint32_t>(t0), 0x0B0B0909u);
+        }
       }
       bf16x8 pf[2];
-      softmax(sc[blk], pf);
+      softmax(sc[blk], pf, msk, partial);
       pv(buf, blk, pf);
     }
   };
@@ -853,22 +930,26 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   // own DMA loads of tile e complete (the only ones outstanding) and has
   // finished computing tile e-1, so the data of e is visible and the other
   // buffer is free: tile e+1 is then streamed into it while e is consumed.
-  int kt = next_tile();
-  if (kt != NONE) issue(kt, kv0);
-  while (kt != NONE) {
-    wait_vmcnt<0>();
-    lds_barrier();
-    int kn = next_tile();
-    if (kn != NONE) issue(kn, kv1);
-    compute(kt, kv0);
-    kt = kn;
-    if (kt == NONE) break;
-    wait_vmcnt<0>();
-    lds_barrier();
-    kn = next_tile();
-    if (kn != NONE) issue(kn, kv0);
-    compute(kt, kv1);
-    kt = kn;
+  if (n_tiles > 0) {
+    TileGeo tc = entry(0), tn;
+    issue(tc, kv0);
+    int e = 0;
+    while (true) {
+      wait_vmcnt<0>();
+      lds_barrier();
+      const bool more0 = e + 1 < n_tiles;
+      if (more0) tn = entry(e + 1);
+      compute(tc, kv0, more0, tn, kv1);
+      if (++e == n_tiles) break;
+      tc = tn;
+      wait_vmcnt<0>();
+      lds_barrier();
+      const bool more1 = e + 1 < n_tiles;
+      if (more1) tn = entry(e + 1);
+      compute(tc, kv1, more1, tn, kv0);
+      if (++e == n_tiles) break;
+      tc = tn;
+    }
   }
 
   const float ltot = lsum + __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(lsum)));
@@ -1097,10 +1178,25 @@ size_t attention_lds_bytes(int d, int n_r2c) {
   return kv + static_cast<size_t>(n_r2c) * sizeof(int32_t);
 }
 
+int pair_list_words(const Grid& tiles) { return (tiles.count + 31) / 32; }
+
+hipError_t launch_pair_lists(const int32_t* row_ptr, const int32_t* col_idx, int BH,
+                             const Grid& tiles, int32_t* pair_list, int32_t* pair_len,
+                             hipStream_t s) {
+  const int ngw = (tiles.nw + 1) / 2;
+  const int per_head = tiles.T * tiles.nh * ngw;
+  const int nwords = pair_list_words(tiles);
+  const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(BH) * per_head);
+  pair_kernel<<<grid, 256, static_cast<size_t>(nwords) * 4, s>>>(
+      row_ptr, col_idx, tiles, ngw, per_head, nwords, reinterpret_cast<int2*>(pair_list), pair_len);
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(int dtype, int d, const void* q, const void* k, const void* v,
                             void* o, const int16_t* lv, const RadiusTable& tab, int row_base,
                             int BH, const Grid& tiles, const int32_t* row_ptr,
-                            const int32_t* col_idx, hipStream_t s) {
+                            const int32_t* col_idx, const int32_t* pair_list,
+                            const int32_t* pair_len, hipStream_t s) {
   const int32_t* r2 = tab.r2;
   const unsigned rows = static_cast<unsigned>(BH) * tiles.count;
   if (dtype == 1) {
@@ -1113,11 +1209,10 @@ hipError_t launch_attention(int dtype, int d, const void* q, const void* k, cons
     const unsigned grid = static_cast<unsigned>((groups + 7) / 8 * 8);
     const int ng = static_cast<int>(groups);
     const size_t lds_tab = static_cast<size_t>(tab.n_r2c) * sizeof(int32_t);
-    const FastDiv dpf = make_fastdiv(tiles.per_frame), dnw = make_fastdiv(tiles.nw);
 #define TRA_ATTN(DD)                                                                          \
   attn_bf16_kernel<DD><<<grid, 256, lds_tab, s>>>(qq, kk, vv, oo, lv, tab.r2c, tab.r2off, tab.dmax, \
-                                                  tab.n_r2c, row_base, tiles, dpf, dnw, ngw, ng,     \
-                                                  row_ptr, col_idx)
+                                                  tab.n_r2c, row_base, tiles, ngw, ng, row_ptr,      \
+                                                  reinterpret_cast<const int2*>(pair_list), pair_len)
     if (d == 128) TRA_ATTN(128);
     else TRA_ATTN(64);
 #undef TRA_ATTN
