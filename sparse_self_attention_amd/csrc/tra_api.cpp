@@ -72,6 +72,9 @@ tra_status check_params(const tra_shape* s, const tra_params* p, Table* tab) {
   if (s->dtype == TRA_BF16 &&
       tra::pair_list_words(tra::make_grid(s->T, s->H, s->W, 8, 8)) > tra::kMaxPairListWords)
     return fail(TRA_ERR_SHAPE, "bf16 attention supports at most 393216 key tiles (8x8) per head");
+  if (s->dtype == TRA_BF16 &&
+      static_cast<int64_t>(s->T) * s->H * s->W * s->head_dim * 2 >= (int64_t(1) << 31))
+    return fail(TRA_ERR_SHAPE, "bf16 attention needs T*H*W*head_dim*2 (bytes of one head) below 2^31");
   if (!std::isfinite(p->radius_override) || p->radius_override >= 32768.0)
     return fail(TRA_ERR_INVALID_ARG, "radius_override must be finite and below 32768");
   const int T = s->T;

@@ -570,33 +570,30 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// 16-byte global -> LDS DMA (global_load_lds_dwordx4): lane l's 16 bytes land
-// at LDS byte address lds_base + 16*l (lds_base wave-uniform, through M0).
-// Issued from inline assembly so that the compiler's wait-count insertion does
-// not treat every later LDS read as dependent on it; the kernel orders the
-// hand-off itself with wait_vmcnt + lds_barrier.  The instruction has no
-// register results; one wait state separates the M0 write from its use.
-__device__ __forceinline__ void lds_dma16(const void* gaddr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(gaddr), "s"(lds_base)
-               : "memory", "m0");
+// 16-byte global -> LDS DMA (buffer_load_dwordx4 ... lds): lane l's 16 bytes
+// land at LDS byte address lds_base + 16*l (lds_base wave-uniform, through
+// M0).  Issued from inline assembly so that the compiler's wait-count
+// insertion does not treat every later LDS read as dependent on it; the kernel
+// orders the hand-off itself with wait_vmcnt + lds_barrier.  The instruction
+// has no register results; one wait state separates the M0 write from its use.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+// Raw buffer resource over [base, base + bytes): reads at offsets >= bytes
+// return zero.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a)));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  r[3] = 0x00020000;
+  return r;
 }
-
-// The same DMA addressed as a wave-uniform 64-bit base plus a per-lane 32-bit
-// byte offset (no vector address arithmetic at the call site).
-__device__ __forceinline__ void lds_dma16_so(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  // The base is wave-uniform by construction; readfirstlane lets the compiler
-  // keep it in SGPRs (a no-op when it already is there).
-  // (readfirstlane yields int: each half goes through uint32_t so that the
-  // low half is zero-extended, never sign-extended.)
-  const uint64_t b = reinterpret_cast<uint64_t>(sbase);
-  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b))));
-  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b >> 32))));
-  sbase = reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+// Lane l's 16 bytes at byte offset `off` of the resource (range-checked per
+// lane) go to LDS lds_base + 16*l.
+__device__ __forceinline__ void lds_dma16_buf(i32x4 rsrc, uint32_t off, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "v"(voff), "s"(sbase), "s"(lds_base)
+               : "v"(off), "s"(rsrc), "s"(lds_base)
                : "memory", "m0");
 }
 
@@ -701,17 +698,21 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     return TileGeo{ex & 0x7fffffff, ey & 0xffff, ey >> 16, ex < 0};
   };
 
-  const uint16_t* kbase = k + static_cast<size_t>(bh) * N * D;
-  const uint16_t* vbase = v + static_cast<size_t>(bh) * N * D;
+  // One buffer resource per head for K and V: every tile, edge tiles
+  // included, is loaded with the interior address pattern.  A key position
+  // outside the grid then reads a neighbouring token of the same head (or
+  // zero past the head's end); such keys are always masked.
+  const i32x4 krsrc = make_rsrc(k + static_cast<size_t>(bh) * N * D, static_cast<uint32_t>(N * D * 2));
+  const i32x4 vrsrc = make_rsrc(v + static_cast<size_t>(bh) * N * D, static_cast<uint32_t>(N * D * 2));
 
-  // Streams key tile kt into buffer buf.  DMA segment s (1 KB) receives lane
+  // Streams key tile t into buffer buf.  DMA segment s (1 KB) receives lane
   // l's 16 bytes at s*1KB + 16*l; the lane fetches the (key row, chunk) that
   // the padded layout puts there (pad chunks re-fetch the row's first chunk).
   // Every wave issues the same number of DMA loads per tile (a wave without a
   // segment of its own repeats the last one, writing identical bytes), so the
   // loop's memory counters follow a fixed pattern.  A lane's byte offset from
-  // the tile's first key is fixed per segment; it is computed once here and
-  // the interior tiles' loads need no address arithmetic.
+  // the tile's first key is fixed per segment; it is computed once here, and a
+  // load adds it to the tile's offset.
   constexpr int NK = (L::KSEG + 3) / 4, NV = (L::VSEG + 3) / 4;
   struct SegLane {
     int kr, kc, c;  // key row / column within the tile, 16-byte chunk
@@ -741,31 +742,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   };
   auto issue = [&](const TileGeo& t, char* buf) {
     char* vbuf = buf + L::KSEG * 1024;
-    if (!t.ragged) {
-      const size_t tile_off = ((static_cast<size_t>(t.tk) * g.H + t.kr0) * g.W + t.kc0) * D;
-      const uint16_t* kb = kbase + tile_off;
-      const uint16_t* vb = vbase + tile_off;
+    const uint32_t tile_bytes = static_cast<uint32_t>((t.tk * g.H + t.kr0) * g.W + t.kc0) * (D * 2u);
 #pragma unroll
-      for (int i = 0; i < NK; ++i) lds_dma16_so(kb, koff[i], lds_seg(buf, L::KSEG, i));
+    for (int i = 0; i < NK; ++i) lds_dma16_buf(krsrc, tile_bytes + koff[i], lds_seg(buf, L::KSEG, i));
 #pragma unroll
-      for (int i = 0; i < NV; ++i) lds_dma16_so(vb, voff[i], lds_seg(vbuf, L::VSEG, i));
-    } else {
-      // Ragged tile at the bottom/right edge: clamp rows and columns.
-#pragma unroll
-      for (int i = 0; i < NK; ++i) {
-        const SegLane sl = seg_lane(L::KSTR, L::KSEG, i);
-        const int kr = min(t.kr0 + sl.kr, g.H - 1), kc = min(t.kc0 + sl.kc, g.W - 1);
-        lds_dma16(kbase + ((static_cast<size_t>(t.tk) * g.H + kr) * g.W + kc) * D + sl.c * 8,
-                  lds_seg(buf, L::KSEG, i));
-      }
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const SegLane sl = seg_lane(L::VSTR, L::VSEG, i);
-        const int kr = min(t.kr0 + sl.kr, g.H - 1), kc = min(t.kc0 + sl.kc, g.W - 1);
-        lds_dma16(vbase + ((static_cast<size_t>(t.tk) * g.H + kr) * g.W + kc) * D + sl.c * 8,
-                  lds_seg(vbuf, L::VSEG, i));
-      }
-    }
+    for (int i = 0; i < NV; ++i) lds_dma16_buf(vrsrc, tile_bytes + voff[i], lds_seg(vbuf, L::VSEG, i));
   };
 
   f32x16 oacc[DB];
@@ -789,46 +770,31 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     }
     return acc;
   };
-  // Online-softmax bookkeeping for one block of scores; returns P^T as the two
-  // 16-key B operands of the PV product.  When `partial`, msk[x] holds the
-  // radius mask of elements 2x, 2x+1 as two 16-bit halves (all ones = keep);
-  // it is applied to the packed bf16 probabilities, and the running sum adds
-  // the same bf16 values the product uses.
+  // Online softmax of one 32-key block.  msk[x] holds the radius mask of
+  // elements 2x, 2x+1 as two 16-bit halves (all ones = keep); it is applied
+  // to the packed bf16 probabilities, and the running sum adds the same bf16
+  // values the PV product uses.
   //
   // Lazy rescale: the reference (shared by both lanes of a query) moves only
   // when a score exceeds it by more than 2^8, so probabilities stay <= 256
-  // between moves.  The cheap test looks at the unmasked scores; when it
-  // fires, the exact masked maximum decides whether the reference moves.
-  auto softmax = [&](f32x16& sacc, bf16x8* pf, const uint32_t* msk, bool partial) {
+  // between moves.  The probabilities are formed against the current
+  // reference first; the cheap test on the unmasked maximum then decides
+  // (rarely) to move the reference by the exact masked maximum and form them
+  // again.
+  auto rowmax = [&](const f32x16& sacc) {
     float mx = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
 #pragma unroll
     for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sacc[i]), sacc[i + 1]);
-    mx = fmaxf(mx, sacc[15]);
-    if (__any(mx * c1 > mref + 8.f)) {
-      if (partial) {
-        mx = TRA_NEG_INF;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int keep = (i & 1) ? static_cast<int>(msk[i >> 1]) >> 16
-                                   : static_cast<int>(msk[i >> 1] << 16) >> 16;
-          mx = fmaxf(mx, __int_as_float((__float_as_int(sacc[i]) & keep) |
-                                        (__float_as_int(TRA_NEG_INF) & ~keep)));
-        }
-      }
-      mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(mx))));
-      if (__any(mx * c1 > mref + 8.f)) {
-        const float mn = fmaxf(mref, mx * c1);
-        const float alpha = mref == TRA_NEG_INF ? 0.f : __builtin_amdgcn_exp2f(mref - mn);
-        lsum *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-        mref = mn;
-      }
-    }
-    // With no kept key seen yet the reference is -inf: the probabilities of
-    // this block are then all masked, and any value works.
+    return fmaxf(mx, sacc[15]);
+  };
+  // P^T as the two 16-key B operands of the PV product; returns the block's
+  // contribution to the running sum.
+  auto probs = [&](const f32x16& sacc, const uint32_t* msk, bf16x8* pf) {
+    // With no kept key seen yet the reference is -inf: this block's
+    // probabilities are then all masked, and any value works.
     const float msub = mref == TRA_NEG_INF ? 0.f : mref;
     const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+    float ls[2] = {0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       uint32_t pk[4];
@@ -836,12 +802,43 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
       for (int x = 0; x < 4; ++x) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[8 * j + 2 * x], c1, -msub));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[8 * j + 2 * x + 1], c1, -msub));
-        pk[x] = pack_bf16x2(p0, p1);
-        if (partial) pk[x] &= msk[4 * j + x];
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[x]), ones, lsum, false);
+        pk[x] = pack_bf16x2(p0, p1) & msk[4 * j + x];
+        ls[j] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[x]), ones, ls[j], false);
       }
       pf[j] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
     }
+    return ls[0] + ls[1];
+  };
+  // Moves the reference to the exact masked maximum of the block when that
+  // exceeds it by more than 2^8 (rare path).
+  auto move_ref = [&](const f32x16& sacc, const uint32_t* msk) {
+    float mx = TRA_NEG_INF;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int keep = (i & 1) ? static_cast<int>(msk[i >> 1]) >> 16
+                               : static_cast<int>(msk[i >> 1] << 16) >> 16;
+      mx = fmaxf(mx, __int_as_float((__float_as_int(sacc[i]) & keep) |
+                                    (__float_as_int(TRA_NEG_INF) & ~keep)));
+    }
+    mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(mx))));
+    if (__any(mx * c1 > mref + 8.f)) {
+      const float mn = fmaxf(mref, mx * c1);
+      const float alpha = mref == TRA_NEG_INF ? 0.f : __builtin_amdgcn_exp2f(mref - mn);
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      mref = mn;
+    }
+  };
+  // softmax step of one block: returns P^T in pf and updates the running sum.
+  auto softmax = [&](const f32x16& sacc, const uint32_t* msk, bf16x8* pf) {
+    const float mx = rowmax(sacc);
+    float ls = probs(sacc, msk, pf);
+    if (__any(mx * c1 > mref + 8.f)) {
+      move_ref(sacc, msk);
+      ls = probs(sacc, msk, pf);
+    }
+    lsum += ls;
   };
   // O^T += V^T P^T for block blk.
   auto pv = [&](const char* buf, int blk, const bf16x8* pf) {
@@ -867,8 +864,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   constexpr int COL_OUT = 0x40000001, ROW_OUT = -1;
   // When `more`, the LDS DMA of the next tile (tn into nbuf) is issued once
   // the score MFMAs are in flight, so that the matrix unit works while the
-  // DMA instructions wait for the address unit (a wave's DMA issue otherwise
-  // stalls behind its workgroup's burst).
+  // DMA instructions wait to issue.
   auto compute = [&](const TileGeo& t, const char* buf, bool more, const TileGeo& tn, char* nbuf) {
     const int delta = t.tk > tq ? t.tk - tq : tq - t.tk;
     const int tv = r2s[toff + min(delta, max(tdmax, 0))];
@@ -891,38 +887,46 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
         if (t.kr0 + a >= g.H) rr[a] = ROW_OUT;
     }
     const int mindw = min(min(dw2[0], dw2[1]), min(dw2[2], dw2[3]));
-    const int maxdw = max(max(dw2[0], dw2[1]), max(dw2[2], dw2[3]));
-    bool doq[2], fullq[2];
+    bool doq[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int* r = rr + 4 * blk;
       doq[blk] = __any(mindw < max(max(r[0], r[1]), max(r[2], r[3])));
-      fullq[blk] = __all(maxdw < min(min(r[0], r[1]), min(r[2], r[3])));
     }
-    // Both halves' score MFMAs are issued before either softmax, so the vector
-    // work on one half overlaps the matrix work on the other.
-    f32x16 sc[2];
+    // Sign bytes of the two differences -> 16-bit keep masks of block blk.
+    auto masks = [&](int blk, uint32_t* msk) {
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-      if (doq[blk]) sc[blk] = scores(buf, blk);
-    if (more) issue(tn, nbuf);
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      if (!doq[blk]) continue;
-      uint32_t msk[8];
-      const bool partial = !fullq[blk];
-      if (partial) {
-        // Sign bytes of the two differences -> 16-bit keep masks.
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const int ra = rr[4 * blk + (x >> 1)];
-          const int t0 = dw2[2 * (x & 1)] - ra, t1 = dw2[2 * (x & 1) + 1] - ra;
-          msk[x] = __builtin_amdgcn_perm(static_cast<uint32_t>(t1), static_cast<uint32_t>(t0), 0x0B0B0909u);
-        }
+      for (int x = 0; x < 8; ++x) {
+        const int ra = rr[4 * blk + (x >> 1)];
+        const int t0 = dw2[2 * (x & 1)] - ra, t1 = dw2[2 * (x & 1) + 1] - ra;
+        msk[x] = __builtin_amdgcn_perm(static_cast<uint32_t>(t1), static_cast<uint32_t>(t0), 0x0B0B0909u);
       }
+    };
+    if (doq[0] && doq[1]) {
+      // Both blocks: the vector work of one block overlaps the matrix work of
+      // the other.
+      uint32_t m0[8], m1[8];
+      const f32x16 s0 = scores(buf, 0);
+      masks(0, m0);
+      const f32x16 s1 = scores(buf, 1);
+      if (more) issue(tn, nbuf);
+      bf16x8 pf0[2], pf1[2];
+      softmax(s0, m0, pf0);
+      pv(buf, 0, pf0);
+      masks(1, m1);
+      softmax(s1, m1, pf1);
+      pv(buf, 1, pf1);
+    } else if (doq[0] || doq[1]) {
+      const int blk = doq[0] ? 0 : 1;
+      uint32_t m[8];
+      const f32x16 s0 = scores(buf, blk);
+      masks(blk, m);
+      if (more) issue(tn, nbuf);
       bf16x8 pf[2];
-      softmax(sc[blk], pf, msk, partial);
+      softmax(s0, m, pf);
       pv(buf, blk, pf);
+    } else if (more) {
+      issue(tn, nbuf);
     }
   };
 
