@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -69,9 +70,6 @@ tra_status check_params(const tra_shape* s, const tra_params* p, Table* tab) {
   if (p->pool_h < 1 || p->pool_w < 1) return fail(TRA_ERR_INVALID_ARG, "pool_h and pool_w must be >= 1");
   if (p->tile_h != 8 || p->tile_w != 8)
     return fail(TRA_ERR_INVALID_ARG, "the device kernels use 8x8 tiles (tile_h = tile_w = 8)");
-  if (s->dtype == TRA_BF16 &&
-      tra::pair_list_words(tra::make_grid(s->T, s->H, s->W, 8, 8)) > tra::kMaxPairListWords)
-    return fail(TRA_ERR_SHAPE, "bf16 attention supports at most 393216 key tiles (8x8) per head");
   if (s->dtype == TRA_BF16 &&
       static_cast<int64_t>(s->T) * s->H * s->W * s->head_dim * 2 >= (int64_t(1) << 31))
     return fail(TRA_ERR_SHAPE, "bf16 attention needs T*H*W*head_dim*2 (bytes of one head) below 2^31");
@@ -155,6 +153,9 @@ struct tra_plan {
   int32_t* row_ptr = nullptr;
   int32_t* col_idx = nullptr;
   int64_t col_cap = 0;
+  int DM = 0;                    // largest active frame distance of the radius table
+  int32_t* runs = nullptr;       // per query tile: key-tile column runs per (frame, tile row)
+  int32_t* rowwin = nullptr;     // per query tile: first frame | frames << 16
   int32_t* pair_list = nullptr;  // bf16 only: merged lists of query-tile pairs, 2 int32 per entry
   int64_t pair_cap = 0;          // entries
   int32_t* pair_len = nullptr;
@@ -169,7 +170,7 @@ namespace {
 void release(tra_plan* p) {
   if (!p) return;
   void* bufs[] = {p->kbar, p->H, p->lv, p->r2, p->dmax, p->r2c, p->r2off, p->pool_w,
-                  p->counts, p->row_ptr, p->col_idx, p->pair_list, p->pair_len, p->totals};
+                  p->counts, p->row_ptr, p->col_idx, p->runs, p->rowwin, p->pair_list, p->pair_len, p->totals};
   for (void* b : bufs)
     if (b) (void)hipFree(b);
   if (p->totals_host) (void)hipHostFree(p->totals_host);
@@ -188,7 +189,8 @@ tra_status build(tra_plan* p, const void* q, const void* k, hipStream_t st) {
   } else {
     TRA_HIP(tra::launch_fill_levels(p->lv, p->H, p->n_queries, st));
   }
-  TRA_HIP(tra::launch_csr_count(p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, p->counts, st));
+  TRA_HIP(tra::launch_csr_runs(p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, p->DM, p->counts,
+                               p->runs, p->rowwin, st));
   TRA_HIP(tra::launch_scan(p->counts, p->n_rows, p->row_ptr, p->totals, st));
   TRA_HIP(hipMemcpyAsync(p->totals_host, p->totals, 3 * sizeof(int64_t), hipMemcpyDeviceToHost, st));
   TRA_HIP(hipStreamSynchronize(st));
@@ -203,8 +205,7 @@ tra_status build(tra_plan* p, const void* q, const void* k, hipStream_t st) {
     TRA_HIP(hipMalloc(&p->col_idx, cap * sizeof(int32_t)));
     p->col_cap = cap;
   }
-  TRA_HIP(tra::launch_csr_fill(p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, p->row_ptr,
-                               p->col_idx, st));
+  TRA_HIP(tra::launch_csr_expand(p->BH, p->tiles, p->DM, p->runs, p->rowwin, p->row_ptr, p->col_idx, st));
   if (s.dtype == TRA_BF16) {
     if (p->nnz > p->pair_cap) {
       if (p->pair_list) TRA_HIP(hipFree(p->pair_list));
@@ -213,7 +214,8 @@ tra_status build(tra_plan* p, const void* q, const void* k, hipStream_t st) {
       TRA_HIP(hipMalloc(&p->pair_list, p->col_cap * 2 * sizeof(int32_t)));
       p->pair_cap = p->col_cap;
     }
-    TRA_HIP(tra::launch_pair_lists(p->row_ptr, p->col_idx, p->BH, p->tiles, p->pair_list, p->pair_len, st));
+    TRA_HIP(tra::launch_pair_lists(p->BH, p->tiles, p->DM, p->runs, p->rowwin, p->row_ptr, p->pair_list,
+                                   p->pair_len, st));
   }
   return TRA_OK;
 }
@@ -293,6 +295,13 @@ tra_status tra_plan_create(const tra_shape* shape, const tra_params* params, con
   TRA_HIP_P(hipMalloc(&p->counts, p->n_rows * sizeof(int32_t)));
   TRA_HIP_P(hipMalloc(&p->row_ptr, (p->n_rows + 1) * sizeof(int32_t)));
   TRA_HIP_P(hipMalloc(&p->totals, 4 * sizeof(int64_t)));
+  for (int32_t dm : p->table.dmax) p->DM = std::max(p->DM, static_cast<int>(dm));
+  {
+    const int64_t run_entries = p->n_rows * (2 * p->DM + 1) * p->tiles.nh;
+    if (run_entries > (int64_t(1) << 32)) return fin(fail(TRA_ERR_SHAPE, "tile-list run buffer too large"));
+    TRA_HIP_P(hipMalloc(&p->runs, run_entries * sizeof(int32_t)));
+    TRA_HIP_P(hipMalloc(&p->rowwin, p->n_rows * sizeof(int32_t)));
+  }
   if (shape->dtype == TRA_BF16) {
     const int64_t n_pairs = static_cast<int64_t>(p->BH) * p->tiles.T * p->tiles.nh * ((p->tiles.nw + 1) / 2);
     TRA_HIP_P(hipMalloc(&p->pair_len, n_pairs * sizeof(int32_t)));

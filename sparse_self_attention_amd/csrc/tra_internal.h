@@ -51,29 +51,30 @@ hipError_t launch_entropy(int dtype, int d, const void* q, const void* kbar, con
                           int BH, int N, int n_pool, const EntropyArgs& ea, float* H_out,
                           int16_t* lv_out, hipStream_t s);
 hipError_t launch_fill_levels(int16_t* lv, float* H, int64_t n, hipStream_t s);
-hipError_t launch_csr_count(const int16_t* lv, const int32_t* r2, const int32_t* dmax, int T,
-                            int row_base, int BH, const Grid& tiles, int32_t* counts,
-                            hipStream_t s);
+// Tile lists: per query tile the runs of key-tile columns per (frame, tile
+// row) plus the count and the frame window (csr_runs), the scan of the counts,
+// and the expansion of the runs into col_idx.  DM is the largest active frame
+// distance of the radius table; runs holds n_rows * (2*DM + 1) * nh int32.
+hipError_t launch_csr_runs(const int16_t* lv, const int32_t* r2, const int32_t* dmax, int T,
+                           int row_base, int BH, const Grid& tiles, int DM, int32_t* counts,
+                           int32_t* runs, int32_t* rowwin, hipStream_t s);
 hipError_t launch_scan(const int32_t* counts, int64_t n_rows, int32_t* row_ptr,
                        int64_t* totals, hipStream_t s);
-hipError_t launch_csr_fill(const int16_t* lv, const int32_t* r2, const int32_t* dmax, int T,
-                           int row_base, int BH, const Grid& tiles, const int32_t* row_ptr,
-                           int32_t* col_idx, hipStream_t s);
+hipError_t launch_csr_expand(int BH, const Grid& tiles, int DM, const int32_t* runs,
+                             const int32_t* rowwin, const int32_t* row_ptr, int32_t* col_idx,
+                             hipStream_t s);
 hipError_t launch_attention(int dtype, int d, const void* q, const void* k, const void* v,
                             void* o, const int16_t* lv, const RadiusTable& tab, int row_base,
                             int BH, const Grid& tiles, const int32_t* row_ptr,
                             const int32_t* col_idx, const int32_t* pair_list,
                             const int32_t* pair_len, hipStream_t s);
 // Merged tile lists of horizontally adjacent query-tile pairs (the bf16
-// attention kernel's unit of work): entries of two int32 each, pair p's list
-// at pair_list + 2 * row_ptr[first row of p], length pair_len[p].  The
-// buffer needs 2 * nnz entries of int32.
-hipError_t launch_pair_lists(const int32_t* row_ptr, const int32_t* col_idx, int BH,
-                             const Grid& tiles, int32_t* pair_list, int32_t* pair_len,
-                             hipStream_t s);
-// LDS words of the pair-list bitmap (one bit per key tile of a head).
-int pair_list_words(const Grid& tiles);
-constexpr int kMaxPairListWords = 12288;  // 48 KB of LDS
+// attention kernel's unit of work), from the runs: entries of two int32 each,
+// pair p's list at pair_list + 2 * row_ptr[first row of p], length
+// pair_len[p].  The buffer needs 2 * nnz int32.
+hipError_t launch_pair_lists(int BH, const Grid& tiles, int DM, const int32_t* runs,
+                             const int32_t* rowwin, const int32_t* row_ptr, int32_t* pair_list,
+                             int32_t* pair_len, hipStream_t s);
 // Dynamic LDS the bf16 attention kernel needs for its staged K/V buffers
 // plus a compact radius table of n_r2c entries; 0 if it exceeds the device limit.
 size_t attention_lds_bytes(int d, int n_r2c);

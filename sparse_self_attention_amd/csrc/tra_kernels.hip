@@ -12,8 +12,10 @@
 //                         fp32 online log-sum-exp with an entropy moment, fp64
 //                         epilogue, quantised budget level (reads Q)
 //   entropy_f32_kernel    the same for fp32 inputs with fp64 dot products
-//   csr_kernel<FILL>      per query tile: union over its 64 queries of the disk
-//                         footprints, as key-tile runs (count pass, fill pass)
+//   csr_runs_kernel       per query tile: union over its 64 queries of the disk
+//                         footprints, as key-tile runs per frame and tile row
+//   csr_expand_kernel     runs -> CSR column indices
+//   pair_kernel           runs of two adjacent query tiles -> their merged list
 //   scan_kernel           exclusive scan of the per-tile counts
 //   attn_bf16_kernel      block-sparse flash attention: S^T = K Q^T and
 //                         O^T += V^T P^T on 32x32x16 bf16 MFMA, K/V tiles staged
@@ -42,9 +44,12 @@ __device__ __forceinline__ float bf16_to_float(uint16_t b) {
 
 // Integer square root floor(sqrt(x)) for 0 <= x < 2^31.
 __device__ __forceinline__ int isqrt_i(int x) {
-  long long r = static_cast<long long>(sqrtf(static_cast<float>(x)));
-  r -= (r * r > x);
-  r += ((r + 1) * (r + 1) <= x);
+  // r <= 46341 here, so r*r and (r+1)*(r+1) stay below 2^31 + 2^17 and are
+  // compared as unsigned 32-bit values.
+  unsigned r = static_cast<unsigned>(sqrtf(static_cast<float>(x)));
+  const unsigned ux = static_cast<unsigned>(x);
+  r -= (r * r > ux);
+  r += ((r + 1) * (r + 1) <= ux);
   return static_cast<int>(r);
 }
 
@@ -82,24 +87,34 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
-// Wave-wide min / max (64 lanes): DPP inside rows of 16, then lane swaps.
-__device__ __forceinline__ int wave_min(int v) {
-  v = min(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
-  v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
-  v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false));  // row_ror:4
-  v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false));  // row_ror:8
-  v = min(v, __shfl_xor(v, 16));
-  v = min(v, __shfl_xor(v, 32));
-  return v;
+// Wave-wide min / max with a wave-uniform result: DPP inside rows of 16, then
+// the four row results combined through readlane.
+__device__ __forceinline__ int wave_min_u(int v) {
+  v = min(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false));
+  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
-__device__ __forceinline__ int wave_max(int v) {
+__device__ __forceinline__ int wave_max_u(int v) {
   v = max(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
   v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
   v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false));
   v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false));
-  v = max(v, __shfl_xor(v, 16));
-  v = max(v, __shfl_xor(v, 32));
-  return v;
+  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+// Exclusive prefix sum over the wave's lanes; *total receives the wave sum.
+__device__ __forceinline__ int wave_excl_scan(int v, int lane, int* total) {
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  *total = __builtin_amdgcn_readlane(x, 63);
+  return x - v;
 }
 
 // ---------------------------------------------------------------------------
@@ -205,7 +220,7 @@ __device__ __forceinline__ void entropy_store(double Hd, const EntropyArgs& ea, 
 // Pooled keys stream through LDS in chunks of 32 rows; each chunk gives a
 // 32(keys) x 32(queries) score block per MFMA column block, lane = query.
 template <int D>
-__global__ __launch_bounds__(256) void entropy_bf16_kernel(
+__global__ __launch_bounds__(512) void entropy_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kbar,
     const float* __restrict__ pool_w, int N, int NP, EntropyArgs ea, float* __restrict__ Hout,
     int16_t* __restrict__ lvout) {
@@ -216,25 +231,23 @@ __global__ __launch_bounds__(256) void entropy_bf16_kernel(
   const int bh = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, col = lane & 31;
-  const int qbase = blockIdx.x * 256 + wave * 64;
-
-  bf16x8 qf[2][KS];
+  // Eight waves of 32 queries (lane % 32 = query; both lanes of a query hold
+  // half of its pooled keys).
+  const int n = blockIdx.x * 256 + wave * 32 + col;
+  bf16x8 qf[KS];
+  {
+    const uint16_t* p = q + (static_cast<size_t>(bh) * N + min(n, N - 1)) * D;
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int n = min(qbase + cb * 32 + col, N - 1);
-    const uint16_t* p = q + (static_cast<size_t>(bh) * N + n) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[cb][ks] = *reinterpret_cast<const bf16x8*>(p + 16 * ks + 8 * h);
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(p + 16 * ks + 8 * h);
   }
   const uint16_t* kb = kbar + static_cast<size_t>(bh) * NP * D;
   const float c1 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
-  float m[2] = {TRA_NEG_INF, TRA_NEG_INF}, A[2] = {0.f, 0.f}, Bm[2] = {0.f, 0.f};
+  float m = TRA_NEG_INF, A = 0.f, Bm = 0.f;
 
   const int nchunks = (NP + 31) / 32;
   for (int ci = 0; ci < nchunks; ++ci) {
     __syncthreads();
-    for (int idx = threadIdx.x; idx < 32 * NCH; idx += 256) {
+    for (int idx = threadIdx.x; idx < 32 * NCH; idx += 512) {
       const int r = idx / NCH, c = idx % NCH;
       const int rowi = ci * 32 + r;
       uint4 v = make_uint4(0, 0, 0, 0);
@@ -246,77 +259,66 @@ __global__ __launch_bounds__(256) void entropy_bf16_kernel(
       w_lds[threadIdx.x] = rowi < NP ? pool_w[rowi] : 0.f;
     }
     __syncthreads();
-    bf16x8 af[KS];
+    f32x16 acc = {0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      af[ks] = *reinterpret_cast<const bf16x8*>(&kb_lds[col * D + (((2 * ks + h) ^ swz<NCH>(col)) << 3)]);
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(&kb_lds[col * D + (((2 * ks + h) ^ swz<NCH>(col)) << 3)]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], acc, 0, 0, 0);
+    }
     float w[16];
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const float4 w4 = *reinterpret_cast<const float4*>(&w_lds[8 * a + 4 * h]);
       w[4 * a + 0] = w4.x; w[4 * a + 1] = w4.y; w[4 * a + 2] = w4.z; w[4 * a + 3] = w4.w;
     }
-    const bool partial = (ci + 1) * 32 > NP;
+    if ((ci + 1) * 32 > NP) {
+      // Padded rows: weight 0 and a finite sentinel score, so that they add
+      // exactly 0 to both sums (an infinite score would make 0 * inf = NaN).
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      f32x16 acc = {0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qf[cb][ks], acc, 0, 0, 0);
-      if (partial) {
-        // Padded rows: weight 0 and a finite sentinel score, so that they add
-        // exactly 0 to both sums (an infinite score would make 0 * inf = NaN).
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = 8 * (i >> 2) + 4 * h + (i & 3);
-          if (ci * 32 + r >= NP) acc[i] = -3.0e38f;
-        }
-      }
-      float mx = acc[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, acc[i]);
-      const float mnew = fmaxf(m[cb], mx * c1);
-      if (mnew != TRA_NEG_INF) {
-        float sA = 0.f, sB = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float t = fmaf(acc[i], c1, -mnew);
-          const float e = __builtin_amdgcn_exp2f(t) * w[i];
-          sA += e;
-          sB = fmaf(e, t, sB);
-        }
-        if (A[cb] > 0.f) {
-          const float alpha = __builtin_amdgcn_exp2f(m[cb] - mnew);
-          Bm[cb] = alpha * fmaf(m[cb] - mnew, A[cb], Bm[cb]) + sB;
-          A[cb] = fmaf(A[cb], alpha, sA);
-        } else {
-          Bm[cb] = sB;
-          A[cb] = sA;
-        }
-        m[cb] = mnew;
+      for (int i = 0; i < 16; ++i) {
+        const int r = 8 * (i >> 2) + 4 * h + (i & 3);
+        if (ci * 32 + r >= NP) acc[i] = -3.0e38f;
       }
     }
+    float mx = fmaxf(fmaxf(acc[0], acc[1]), acc[2]);
+#pragma unroll
+    for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, acc[i]), acc[i + 1]);
+    mx = fmaxf(mx, acc[15]);
+    const float mnew = fmaxf(m, mx * c1);
+    float sA = 0.f, sB = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float t = fmaf(acc[i], c1, -mnew);
+      const float e = __builtin_amdgcn_exp2f(t) * w[i];
+      sA += e;
+      sB = fmaf(e, t, sB);
+    }
+    if (A > 0.f) {
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      Bm = alpha * fmaf(m - mnew, A, Bm) + sB;
+      A = fmaf(A, alpha, sA);
+    } else {
+      Bm = sB;
+      A = sA;
+    }
+    m = mnew;
   }
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const float mp = __shfl_xor(m[cb], 32), Ap = __shfl_xor(A[cb], 32), Bp = __shfl_xor(Bm[cb], 32);
-    const int n = qbase + cb * 32 + col;
-    if (h == 0 && n < N) {
-      const double M = fmax(static_cast<double>(m[cb]), static_cast<double>(mp));
-      double At = 0.0, Bt = 0.0;
-      if (A[cb] > 0.f) {
-        const double s0 = exp2(static_cast<double>(m[cb]) - M);
-        At += s0 * A[cb];
-        Bt += s0 * (static_cast<double>(Bm[cb]) + (static_cast<double>(m[cb]) - M) * A[cb]);
-      }
-      if (Ap > 0.f) {
-        const double s1 = exp2(static_cast<double>(mp) - M);
-        At += s1 * Ap;
-        Bt += s1 * (static_cast<double>(Bp) + (static_cast<double>(mp) - M) * Ap);
-      }
-      const double Hd = log(At) - 0.6931471805599453 * Bt / At;
-      entropy_store(Hd, ea, static_cast<size_t>(bh) * N + n, Hout, lvout);
+  const float mp = __shfl_xor(m, 32), Ap = __shfl_xor(A, 32), Bp = __shfl_xor(Bm, 32);
+  if (h == 0 && n < N) {
+    const double M = fmax(static_cast<double>(m), static_cast<double>(mp));
+    double At = 0.0, Bt = 0.0;
+    if (A > 0.f) {
+      const double s0 = exp2(static_cast<double>(m) - M);
+      At += s0 * A;
+      Bt += s0 * (static_cast<double>(Bm) + (static_cast<double>(m) - M) * A);
     }
+    if (Ap > 0.f) {
+      const double s1 = exp2(static_cast<double>(mp) - M);
+      At += s1 * Ap;
+      Bt += s1 * (static_cast<double>(Bp) + (static_cast<double>(mp) - M) * Ap);
+    }
+    const double Hd = log(At) - 0.6931471805599453 * Bt / At;
+    entropy_store(Hd, ea, static_cast<size_t>(bh) * N + n, Hout, lvout);
   }
 }
 
@@ -378,21 +380,29 @@ __global__ void fill_levels_kernel(int16_t* lv, float* H, int64_t n) {
 }
 
 // ---------------------------------------------------------------------------
-// Tile lists.  One wave per query tile, lane = query (tile-local row-major).
-// For every key frame within the wave's largest active temporal distance and
-// every key-tile row the disks reach, each lane's footprint is a run of key-tile
-// columns that contains the query tile's own column, so the union over the
-// wave is the run [min lo, max hi].
-// grid (ceil(tiles.count/4), BH), 256 threads.
+// Tile lists.
+//
+// Step 1 (csr_runs_kernel): one wave per query tile, lane = query (tile-local
+// row-major).  For every key frame within the wave's largest active temporal
+// distance and every key-tile row the disks reach, a query's footprint is the
+// column interval [w - a, w + a], a = isqrt(R2 - dh^2), as a run of key-tile
+// columns that contains the query tile's own column; the union over the wave
+// is therefore the run [min lo, max hi].  The kernel writes the row's count,
+// its frame window (first frame | frames << 16) and the runs
+// (LO | HI << 16, empty = HI < LO) at runs + row * RS, RS = (2*DM + 1) * nh,
+// frame-major, tile rows in order.  grid (ceil(tiles.count/4), BH).
+// Step 2: scan of the counts (scan_kernel).
+// Step 3 (csr_expand_kernel): one wave per row expands the runs into col_idx.
 // ---------------------------------------------------------------------------
-template <bool FILL>
-__global__ __launch_bounds__(256) void csr_kernel(const int16_t* __restrict__ lv,
-                                                 const int32_t* __restrict__ r2,
-                                                 const int32_t* __restrict__ dmax, int T,
-                                                 int row_base, Grid g, int tw_shift,
-                                                 int32_t* __restrict__ counts,
-                                                 const int32_t* __restrict__ row_ptr,
-                                                 int32_t* __restrict__ col_idx) {
+constexpr int32_t RUN_EMPTY = 0xffff;  // LO = 0xffff, HI = 0
+
+__global__ __launch_bounds__(256) void csr_runs_kernel(const int16_t* __restrict__ lv,
+                                                      const int32_t* __restrict__ r2,
+                                                      const int32_t* __restrict__ dmax, int T,
+                                                      int row_base, Grid g, int tw_shift, int DM,
+                                                      int32_t* __restrict__ counts,
+                                                      int32_t* __restrict__ runs,
+                                                      int32_t* __restrict__ rowwin) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tile = blockIdx.x * 4 + wave;
   if (tile >= g.count) return;  // wave-uniform
@@ -408,138 +418,205 @@ __global__ __launch_bounds__(256) void csr_kernel(const int16_t* __restrict__ lv
     trow = lv[static_cast<size_t>(bh) * N + (static_cast<size_t>(tq) * g.H + hq) * g.W + wq] - row_base;
     dm = dmax[trow];
   }
-  const int dmw = wave_max(dm);
-  int count = 0;
-  int out = FILL ? row_ptr[row] : 0;
+  const int dmw = wave_max_u(dm);
   const int t_lo = max(0, tq - dmw), t_hi = min(T - 1, tq + dmw);
+  int32_t* rrow = runs + row * static_cast<int64_t>((2 * DM + 1) * g.nh);
+  int count = 0;
   for (int tk = t_lo; tk <= t_hi; ++tk) {
     const int delta = tk > tq ? tk - tq : tq - tk;
     const int thr = (valid && delta <= dm) ? r2[trow * T + delta] : -1;
     const int rad = thr >= 0 ? isqrt_i(thr) : -1;
     const int top = thr >= 0 ? max(0, hq - rad) : 0x7fffffff;
     const int bot = thr >= 0 ? min(g.H - 1, hq + rad) : -1;
-    const int TOP = wave_min(top), BOT = wave_max(bot);
-    if (BOT < TOP) continue;
-    for (int tr = TOP / g.th; tr <= BOT / g.th; ++tr) {
-      const int r0 = tr * g.th, r1 = min(g.H, r0 + g.th) - 1;
-      const int dh = max(0, max(r0 - hq, hq - r1));
-      const int remv = thr - dh * dh;
-      int lo = 0x7fffffff, hi = -1;
-      if (thr >= 0 && remv >= 0) {
-        const int a = isqrt_i(remv);
-        lo = max(0, wq - a) >> tw_shift;
-        hi = min(g.W - 1, wq + a) >> tw_shift;
-      }
-      const int LO = wave_min(lo), HI = wave_max(hi);
-      if (HI >= LO) {
-        if constexpr (FILL) {
-          const int base = (tk * g.nh + tr) * g.nw;
-          for (int c = LO + lane; c <= HI; c += 64) col_idx[out + (c - LO)] = base + c;
-          out += HI - LO + 1;
-        } else {
+    const int TOP = wave_min_u(top), BOT = wave_max_u(bot);
+    const int tr_first = BOT < TOP ? g.nh : TOP / g.th, tr_last = BOT < TOP ? -1 : BOT / g.th;
+    // Tile rows in chunks of 64: lane j keeps the run of row (chunk + j).
+    for (int trc = 0; trc < g.nh; trc += 64) {
+      int32_t myrun = RUN_EMPTY;
+      const int tr_end = min(trc + 63, tr_last);
+      for (int tr = max(trc, tr_first); tr <= tr_end; ++tr) {
+        const int r0 = tr * g.th, r1 = min(g.H, r0 + g.th) - 1;
+        const int dh = max(0, max(r0 - hq, hq - r1));
+        const int remv = thr - dh * dh;
+        int lo = 0x7fffffff, hi = -1;
+        if (thr >= 0 && remv >= 0) {
+          const int a = isqrt_i(remv);
+          lo = max(0, wq - a) >> tw_shift;
+          hi = min(g.W - 1, wq + a) >> tw_shift;
+        }
+        const int LO = wave_min_u(lo), HI = wave_max_u(hi);
+        if (HI >= LO) {
           count += HI - LO + 1;
+          if (lane == tr - trc) myrun = LO | (HI << 16);
         }
       }
+      if (trc + lane < g.nh) rrow[(tk - t_lo) * g.nh + trc + lane] = myrun;
     }
   }
-  if (!FILL && lane == 0) counts[row] = count;
+  if (lane == 0) {
+    counts[row] = count;
+    rowwin[row] = t_lo | (max(0, t_hi - t_lo + 1) << 16);
+  }
+}
+
+// Step 3: expand the runs of each row into col_idx (ascending tile index).
+// One wave per row, runs taken 64 at a time.
+__global__ __launch_bounds__(256) void csr_expand_kernel(Grid g, int DM, int64_t n_rows,
+                                                        const int32_t* __restrict__ runs,
+                                                        const int32_t* __restrict__ rowwin,
+                                                        const int32_t* __restrict__ row_ptr,
+                                                        int32_t* __restrict__ col_idx) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= n_rows) return;  // wave-uniform
+  const int32_t* rrow = runs + row * static_cast<int64_t>((2 * DM + 1) * g.nh);
+  const int win = rowwin[row];
+  const int t_lo = win & 0xffff, nruns = (win >> 16) * g.nh;
+  int out = row_ptr[row];
+  for (int j0 = 0; j0 < nruns; j0 += 64) {
+    const int j = j0 + lane;
+    const int run = j < nruns ? rrow[j] : RUN_EMPTY;
+    const int LO = run & 0xffff, HI = run >> 16;
+    const int len = HI >= LO ? HI - LO + 1 : 0;
+    int total;
+    const int excl = wave_excl_scan(len, lane, &total);
+    const int base = ((t_lo + j / g.nh) * g.nh + j % g.nh) * g.nw + LO;
+    for (int c = 0; c < len; ++c) col_idx[out + excl + c] = base + c;
+    out += total;
+  }
 }
 
 // Union of the tile lists of two horizontally adjacent query tiles, the unit
-// of work of the bf16 attention kernel.  Every non-empty column run of a query
-// tile's list contains the tile's own column, so per (frame, tile row) the
-// union of the two runs is again one run; the union is formed here once per
-// plan with a bitmap over the head's key tiles in LDS, then written out in
-// ascending order as (frame | ragged << 31, row0 | col0 << 16), where ragged
-// marks a tile cut by the bottom or right edge of the grid.  Pair p's list
-// goes where its first tile's CSR row starts (the two rows are adjacent and
-// the union is no longer than both), its length to pair_len[p].
-// One workgroup per pair; nwords = ceil(tiles per head / 32) words of LDS.
-__global__ __launch_bounds__(256) void pair_kernel(const int32_t* __restrict__ row_ptr,
-                                                  const int32_t* __restrict__ col_idx, Grid g,
-                                                  int ngw, int per_head, int nwords,
-                                                  int2* __restrict__ out,
+// of work of the bf16 attention kernel, from the runs of their two rows: per
+// (frame, tile row) the union of two runs is again a run (each contains its
+// own tile's column, and the two columns are adjacent).  Entries in ascending
+// order as (frame | ragged << 31, row0 | col0 << 16), where ragged marks a
+// tile cut by the bottom or right edge of the grid.  Pair p's list goes where
+// its first tile's CSR row starts (the two rows are adjacent and the union is
+// no longer than both), its length to pair_len[p].  One wave per pair.
+__global__ __launch_bounds__(256) void pair_kernel(Grid g, int DM, int ngw, int64_t n_pairs,
+                                                  const int32_t* __restrict__ runs,
+                                                  const int32_t* __restrict__ rowwin,
+                                                  const int32_t* __restrict__ row_ptr,
+                                                  int2* __restrict__ out_list,
                                                   int32_t* __restrict__ out_len) {
-  extern __shared__ uint32_t bits[];
-  __shared__ int part[256];
-  const int tid = threadIdx.x;
-  const int bh = blockIdx.x / per_head, pair = blockIdx.x % per_head;
-  const int gc = pair % ngw, fr = pair / ngw;  // fr = frame * nh + tile row
-  const int64_t row = static_cast<int64_t>(bh) * g.count + static_cast<int64_t>(fr) * g.nw + 2 * gc;
-  const int beg = row_ptr[row];
-  const int end = row_ptr[row + (2 * gc + 1 < g.nw ? 2 : 1)];
-  for (int w = tid; w < nwords; w += 256) bits[w] = 0u;
-  __syncthreads();
-  for (int e = beg + tid; e < end; e += 256) {
-    const int t = col_idx[e];
-    atomicOr(&bits[t >> 5], 1u << (t & 31));
+  const int lane = threadIdx.x & 63;
+  const int64_t pid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (pid >= n_pairs) return;  // wave-uniform
+  const int64_t per_head = static_cast<int64_t>(g.T) * g.nh * ngw;
+  const int64_t bh = pid / per_head;
+  const int prem = static_cast<int>(pid % per_head);
+  const int gc = prem % ngw, fr = prem / ngw;  // fr = frame * nh + tile row
+  const int64_t RS = static_cast<int64_t>((2 * DM + 1) * g.nh);
+  const int64_t rowa = bh * g.count + static_cast<int64_t>(fr) * g.nw + 2 * gc;
+  const bool has_b = 2 * gc + 1 < g.nw;
+  const int wa = rowwin[rowa], wb = has_b ? rowwin[rowa + 1] : 0;
+  const int loa = wa & 0xffff, nfa = wa >> 16, lob = wb & 0xffff, nfb = wb >> 16;
+  int t_lo = 0x7fffffff, t_hi = -1;
+  if (nfa > 0) {
+    t_lo = loa;
+    t_hi = loa + nfa - 1;
   }
-  __syncthreads();
-  const int per = (nwords + 255) / 256;
-  const int w0 = min(nwords, tid * per), w1 = min(nwords, w0 + per);
-  int cnt = 0;
-  for (int w = w0; w < w1; ++w) cnt += __popc(bits[w]);
-  part[tid] = cnt;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  if (nfb > 0) {
+    t_lo = min(t_lo, lob);
+    t_hi = max(t_hi, lob + nfb - 1);
   }
-  int pos = beg + part[tid] - cnt;
-  for (int w = w0; w < w1; ++w) {
-    uint32_t m = bits[w];
-    while (m) {
-      const int t = w * 32 + __builtin_ctz(m);
-      m &= m - 1u;
-      const int tk = t / g.per_frame, rem = t - tk * g.per_frame;
-      const int tr = rem / g.nw, tc = rem - tr * g.nw;
-      const int kr0 = tr * g.th, kc0 = tc * g.tw;
-      const bool ragged = kr0 + g.th > g.H || kc0 + g.tw > g.W;
-      out[pos++] = make_int2(tk | (ragged ? static_cast<int>(0x80000000u) : 0), kr0 | (kc0 << 16));
+  const int nruns = t_hi >= t_lo ? (t_hi - t_lo + 1) * g.nh : 0;
+  const int64_t beg = row_ptr[rowa];
+  int64_t out = beg;
+  for (int j0 = 0; j0 < nruns; j0 += 64) {
+    const int j = j0 + lane;
+    const int tk = t_lo + j / g.nh, ktr = j % g.nh;
+    int LO = 0xffff, HI = 0;
+    if (j < nruns) {
+      if (tk >= loa && tk < loa + nfa) {
+        const int r = runs[rowa * RS + (tk - loa) * g.nh + ktr];
+        LO = min(LO, r & 0xffff);
+        HI = max(HI, r >> 16);
+      }
+      if (tk >= lob && tk < lob + nfb) {
+        const int r = runs[(rowa + 1) * RS + (tk - lob) * g.nh + ktr];
+        LO = min(LO, r & 0xffff);
+        HI = max(HI, r >> 16);
+      }
     }
+    const int len = HI >= LO ? HI - LO + 1 : 0;
+    int total;
+    const int excl = wave_excl_scan(len, lane, &total);
+    const int kr0 = ktr * g.th;
+    const bool row_cut = kr0 + g.th > g.H;
+    for (int c = 0; c < len; ++c) {
+      const int kc0 = (LO + c) * g.tw;
+      const bool ragged = row_cut || kc0 + g.tw > g.W;
+      out_list[out + excl + c] = make_int2(tk | (ragged ? static_cast<int>(0x80000000u) : 0), kr0 | (kc0 << 16));
+    }
+    out += total;
   }
-  if (tid == 255) out_len[blockIdx.x] = part[255];
+  if (lane == 0) out_len[pid] = static_cast<int32_t>(out - beg);
 }
 
-// Exclusive scan of per-row counts.  One workgroup of 1024 threads.
-// totals[0] = nnz, totals[1] = longest row, totals[2] = 1 if nnz >= 2^31.
+// Exclusive scan of per-row counts.  One workgroup of 1024 threads walks the
+// counts in tiles of 4096 (4 per thread, 16-byte loads): a thread's partial
+// sums, a wave scan of the thread totals, a scan of the 16 wave totals, and a
+// 64-bit carry across tiles.  totals[0] = nnz, totals[1] = longest row,
+// totals[2] = 1 if nnz >= 2^31 (row_ptr then holds wrapped values).
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ counts,
                                                    int64_t n, int32_t* __restrict__ row_ptr,
                                                    int64_t* __restrict__ totals) {
-  __shared__ long long part[1024];
-  __shared__ int pmax[1024];
-  const int tid = threadIdx.x;
-  const int64_t per = (n + 1023) / 1024;
-  const int64_t b = tid * per, e = min(n, b + per);
-  long long s = 0;
+  __shared__ long long wsum[16];
+  __shared__ int wmax[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  long long carry = 0;
   int mx = 0;
-  for (int64_t i = b; i < e; ++i) {
-    s += counts[i];
-    mx = max(mx, counts[i]);
+  for (int64_t base = 0; base < n; base += 4096) {
+    const int64_t i0 = base + 4 * tid;
+    int c[4];
+    if (i0 + 3 < n && (reinterpret_cast<uintptr_t>(counts + i0) & 15) == 0) {
+      const int4 v = *reinterpret_cast<const int4*>(counts + i0);
+      c[0] = v.x; c[1] = v.y; c[2] = v.z; c[3] = v.w;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) c[k] = i0 + k < n ? counts[i0 + k] : 0;
+    }
+    const int t = c[0] + c[1] + c[2] + c[3];
+    mx = max(mx, max(max(c[0], c[1]), max(c[2], c[3])));
+    // Inclusive wave scan of the thread totals (64-bit: a tile can exceed 2^31).
+    long long x = t;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const long long y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    long long wpre = 0, tile = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      const long long ws = wsum[w];
+      wpre += w < wave ? ws : 0;
+      tile += ws;
+    }
+    long long run = carry + wpre + (x - t);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (i0 + k < n) row_ptr[i0 + k] = static_cast<int32_t>(run);
+      run += c[k];
+    }
+    carry += tile;
+    __syncthreads();
   }
-  part[tid] = s;
-  pmax[tid] = mx;
+  // Longest row: wave max, then across waves.
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off));
+  if (lane == 0) wmax[wave] = mx;
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    long long v = tid >= off ? part[tid - off] : 0;
-    int vm = tid >= off ? pmax[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    pmax[tid] = max(pmax[tid], vm);
-    __syncthreads();
-  }
-  long long run = part[tid] - s;  // exclusive prefix of this thread's chunk
-  for (int64_t i = b; i < e; ++i) {
-    row_ptr[i] = static_cast<int32_t>(run);
-    run += counts[i];
-  }
-  if (tid == 1023) {
-    row_ptr[n] = static_cast<int32_t>(part[1023]);
-    totals[0] = part[1023];
-    totals[1] = pmax[1023];
-    totals[2] = part[1023] >= 0x7fffffffLL ? 1 : 0;
+  if (tid == 0) {
+    int m = 0;
+    for (int w = 0; w < 16; ++w) m = max(m, wmax[w]);
+    row_ptr[n] = static_cast<int32_t>(carry);
+    totals[0] = carry;
+    totals[1] = m;
+    totals[2] = carry >= 0x7fffffffLL ? 1 : 0;
   }
 }
 
@@ -1131,8 +1208,9 @@ hipError_t launch_entropy(int dtype, int d, const void* q, const void* kbar, con
   if (dtype == 1) {
     const auto* qq = static_cast<const uint16_t*>(q);
     const auto* kb = static_cast<const uint16_t*>(kbar);
-    if (d == 128) entropy_bf16_kernel<128><<<grid, block, 0, s>>>(qq, kb, pool_w, N, n_pool, ea, H_out, lv_out);
-    else entropy_bf16_kernel<64><<<grid, block, 0, s>>>(qq, kb, pool_w, N, n_pool, ea, H_out, lv_out);
+    const dim3 block16(512);  // eight waves of 32 queries
+    if (d == 128) entropy_bf16_kernel<128><<<grid, block16, 0, s>>>(qq, kb, pool_w, N, n_pool, ea, H_out, lv_out);
+    else entropy_bf16_kernel<64><<<grid, block16, 0, s>>>(qq, kb, pool_w, N, n_pool, ea, H_out, lv_out);
   } else {
     const auto* qq = static_cast<const float*>(q);
     const auto* kb = static_cast<const float*>(kbar);
@@ -1153,12 +1231,12 @@ static int log2i(int x) {
   return s;
 }
 
-hipError_t launch_csr_count(const int16_t* lv, const int32_t* r2, const int32_t* dmax, int T,
-                            int row_base, int BH, const Grid& tiles, int32_t* counts,
-                            hipStream_t s) {
+hipError_t launch_csr_runs(const int16_t* lv, const int32_t* r2, const int32_t* dmax, int T,
+                           int row_base, int BH, const Grid& tiles, int DM, int32_t* counts,
+                           int32_t* runs, int32_t* rowwin, hipStream_t s) {
   const dim3 grid((tiles.count + 3) / 4, BH), block(256);
-  csr_kernel<false><<<grid, block, 0, s>>>(lv, r2, dmax, T, row_base, tiles, log2i(tiles.tw),
-                                           counts, nullptr, nullptr);
+  csr_runs_kernel<<<grid, block, 0, s>>>(lv, r2, dmax, T, row_base, tiles, log2i(tiles.tw), DM,
+                                         counts, runs, rowwin);
   return hipGetLastError();
 }
 
@@ -1168,12 +1246,12 @@ hipError_t launch_scan(const int32_t* counts, int64_t n_rows, int32_t* row_ptr, 
   return hipGetLastError();
 }
 
-hipError_t launch_csr_fill(const int16_t* lv, const int32_t* r2, const int32_t* dmax, int T,
-                           int row_base, int BH, const Grid& tiles, const int32_t* row_ptr,
-                           int32_t* col_idx, hipStream_t s) {
-  const dim3 grid((tiles.count + 3) / 4, BH), block(256);
-  csr_kernel<true><<<grid, block, 0, s>>>(lv, r2, dmax, T, row_base, tiles, log2i(tiles.tw),
-                                          nullptr, row_ptr, col_idx);
+hipError_t launch_csr_expand(int BH, const Grid& tiles, int DM, const int32_t* runs,
+                             const int32_t* rowwin, const int32_t* row_ptr, int32_t* col_idx,
+                             hipStream_t s) {
+  const int64_t n_rows = static_cast<int64_t>(BH) * tiles.count;
+  csr_expand_kernel<<<static_cast<unsigned>((n_rows + 3) / 4), 256, 0, s>>>(tiles, DM, n_rows, runs, rowwin,
+                                                                           row_ptr, col_idx);
   return hipGetLastError();
 }
 
@@ -1182,17 +1260,13 @@ size_t attention_lds_bytes(int d, int n_r2c) {
   return kv + static_cast<size_t>(n_r2c) * sizeof(int32_t);
 }
 
-int pair_list_words(const Grid& tiles) { return (tiles.count + 31) / 32; }
-
-hipError_t launch_pair_lists(const int32_t* row_ptr, const int32_t* col_idx, int BH,
-                             const Grid& tiles, int32_t* pair_list, int32_t* pair_len,
-                             hipStream_t s) {
+hipError_t launch_pair_lists(int BH, const Grid& tiles, int DM, const int32_t* runs,
+                             const int32_t* rowwin, const int32_t* row_ptr, int32_t* pair_list,
+                             int32_t* pair_len, hipStream_t s) {
   const int ngw = (tiles.nw + 1) / 2;
-  const int per_head = tiles.T * tiles.nh * ngw;
-  const int nwords = pair_list_words(tiles);
-  const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(BH) * per_head);
-  pair_kernel<<<grid, 256, static_cast<size_t>(nwords) * 4, s>>>(
-      row_ptr, col_idx, tiles, ngw, per_head, nwords, reinterpret_cast<int2*>(pair_list), pair_len);
+  const int64_t n_pairs = static_cast<int64_t>(BH) * tiles.T * tiles.nh * ngw;
+  pair_kernel<<<static_cast<unsigned>((n_pairs + 3) / 4), 256, 0, s>>>(
+      tiles, DM, ngw, n_pairs, runs, rowwin, row_ptr, reinterpret_cast<int2*>(pair_list), pair_len);
   return hipGetLastError();
 }
 
