@@ -117,6 +117,55 @@ __device__ __forceinline__ int wave_excl_scan(int v, int lane, int* total) {
   return x - v;
 }
 
+// Workgroup barrier for LDS hand-offs: this wave's LDS reads are complete
+// (lgkmcnt(0)) before it arrives.  Unlike __syncthreads() it carries no
+// release fence, so it does not wait for this wave's outstanding DMA loads into
+// the other buffer; those are ordered by wait_vmcnt before the next barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 16-byte global -> LDS DMA (buffer_load_dwordx4 ... lds): lane l's 16 bytes
+// land at LDS byte address lds_base + 16*l (lds_base wave-uniform, through
+// M0).  Issued from inline assembly so that the compiler's wait-count
+// insertion does not treat every later LDS read as dependent on it; the kernel
+// orders the hand-off itself with wait_vmcnt + lds_barrier.  The instruction
+// has no register results; one wait state separates the M0 write from its use.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+// Raw buffer resource over [base, base + bytes): reads at offsets >= bytes
+// return zero.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a)));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  r[3] = 0x00020000;
+  return r;
+}
+// Lane l's 16 bytes at byte offset `off` of the resource (range-checked per
+// lane) go to LDS lds_base + 16*l.
+__device__ __forceinline__ void lds_dma16_buf(i32x4 rsrc, uint32_t off, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(off), "s"(rsrc), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// The same with 4 bytes per lane (lane l's dword goes to lds_base + 4*l).
+__device__ __forceinline__ void lds_dma4_buf(i32x4 rsrc, uint32_t off, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(off), "s"(rsrc), "s"(lds_base)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  // s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left unconstrained)
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
 // ---------------------------------------------------------------------------
 // Rounding of an exact mean to the input dtype (one rounding, nearest-even).
 // S is the exact sum (float64), n the count.  q = S/n is correctly rounded in
@@ -226,10 +275,11 @@ __global__ __launch_bounds__(512) void entropy_bf16_kernel(
     int16_t* __restrict__ lvout) {
   constexpr int NCH = D / 8;
   constexpr int KS = D / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t kb_lds[32 * D];
-  __shared__ __attribute__((aligned(16))) float w_lds[32];
+  __shared__ __attribute__((aligned(1024))) uint16_t kb_lds[2][32 * D];
+  __shared__ __attribute__((aligned(256))) float w_lds[2][64];
   const int bh = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5, col = lane & 31;
   // Eight waves of 32 queries (lane % 32 = query; both lanes of a query hold
   // half of its pooled keys).
@@ -240,35 +290,50 @@ __global__ __launch_bounds__(512) void entropy_bf16_kernel(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(p + 16 * ks + 8 * h);
   }
-  const uint16_t* kb = kbar + static_cast<size_t>(bh) * NP * D;
   const float c1 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
   float m = TRA_NEG_INF, A = 0.f, Bm = 0.f;
 
+  // Pooled keys stream in chunks of 32 rows (one 1 KB DMA segment per wave,
+  // the chunk's weights through wave 0), one chunk ahead of use, through
+  // range-checked buffer resources: rows past NP read as zero (weight 0).
+  // Lane l of segment s fills LDS bytes s*1KB + 16*l of the chunk, that is
+  // row r and physical 16-byte chunk pc of the swizzled layout below; it
+  // fetches the logical chunk pc ^ swz(r) of that row.
+  constexpr int SEGS = 32 * D * 2 / 1024;  // 1 KB segments per chunk
+  const i32x4 krs = make_rsrc(kbar + static_cast<size_t>(bh) * NP * D, static_cast<uint32_t>(NP * D * 2));
+  const i32x4 wrs = make_rsrc(pool_w, static_cast<uint32_t>(NP * 4));
+  const int sbyte = wave * 1024 + lane * 16;
+  const int srow = sbyte / (2 * D), spc = (sbyte % (2 * D)) / 16;
+  const uint32_t soff = static_cast<uint32_t>(srow * 2 * D + ((spc ^ swz<NCH>(srow)) * 16));
+  const uint32_t kb_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(&kb_lds[0][0])));
+  const uint32_t w_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(&w_lds[0][0])));
+  auto stream = [&](int ci) {
+    const int b = ci & 1;
+    if (wave < SEGS)
+      lds_dma16_buf(krs, static_cast<uint32_t>(ci) * 32 * D * 2 + soff,
+                    __builtin_amdgcn_readfirstlane(kb_base + b * 32 * D * 2 + wave * 1024));
+    if (wave == 0)
+      lds_dma4_buf(wrs, static_cast<uint32_t>(ci) * 32 * 4 + lane * 4,
+                   __builtin_amdgcn_readfirstlane(w_base + b * 64 * 4));
+  };
   const int nchunks = (NP + 31) / 32;
+  stream(0);
   for (int ci = 0; ci < nchunks; ++ci) {
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < 32 * NCH; idx += 512) {
-      const int r = idx / NCH, c = idx % NCH;
-      const int rowi = ci * 32 + r;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (rowi < NP) v = *reinterpret_cast<const uint4*>(kb + static_cast<size_t>(rowi) * D + c * 8);
-      *reinterpret_cast<uint4*>(&kb_lds[r * D + ((c ^ swz<NCH>(r)) << 3)]) = v;
-    }
-    if (threadIdx.x < 32) {
-      const int rowi = ci * 32 + threadIdx.x;
-      w_lds[threadIdx.x] = rowi < NP ? pool_w[rowi] : 0.f;
-    }
-    __syncthreads();
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (ci + 1 < nchunks) stream(ci + 1);
+    const uint16_t* kc = kb_lds[ci & 1];
+    const float* wc = w_lds[ci & 1];
     f32x16 acc = {0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 af = *reinterpret_cast<const bf16x8*>(&kb_lds[col * D + (((2 * ks + h) ^ swz<NCH>(col)) << 3)]);
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(&kc[col * D + (((2 * ks + h) ^ swz<NCH>(col)) << 3)]);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], acc, 0, 0, 0);
     }
     float w[16];
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      const float4 w4 = *reinterpret_cast<const float4*>(&w_lds[8 * a + 4 * h]);
+      const float4 w4 = *reinterpret_cast<const float4*>(&wc[8 * a + 4 * h]);
       w[4 * a + 0] = w4.x; w[4 * a + 1] = w4.y; w[4 * a + 2] = w4.z; w[4 * a + 3] = w4.w;
     }
     if ((ci + 1) * 32 > NP) {
@@ -639,47 +704,6 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
 // 32-key block in register i of a lane, which is exactly the k-slot order of
 // the next MFMA's B operand, so P never leaves registers.
 // ---------------------------------------------------------------------------
-// Workgroup barrier for LDS hand-offs: this wave's LDS reads are complete
-// (lgkmcnt(0)) before it arrives.  Unlike __syncthreads() it carries no
-// release fence, so it does not wait for this wave's outstanding DMA loads into
-// the other buffer; those are ordered by wait_vmcnt before the next barrier.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// 16-byte global -> LDS DMA (buffer_load_dwordx4 ... lds): lane l's 16 bytes
-// land at LDS byte address lds_base + 16*l (lds_base wave-uniform, through
-// M0).  Issued from inline assembly so that the compiler's wait-count
-// insertion does not treat every later LDS read as dependent on it; the kernel
-// orders the hand-off itself with wait_vmcnt + lds_barrier.  The instruction
-// has no register results; one wait state separates the M0 write from its use.
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-// Raw buffer resource over [base, base + bytes): reads at offsets >= bytes
-// return zero.
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a)));
-  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xffffu));
-  r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
-  r[3] = 0x00020000;
-  return r;
-}
-// Lane l's 16 bytes at byte offset `off` of the resource (range-checked per
-// lane) go to LDS lds_base + 16*l.
-__device__ __forceinline__ void lds_dma16_buf(i32x4 rsrc, uint32_t off, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(off), "s"(rsrc), "s"(lds_base)
-               : "memory", "m0");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  // s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left unconstrained)
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-
 // LDS row strides (bytes) of the staged K and V tiles.  K rows are read as
 // 16-byte MFMA operands by 16 lanes at a time (same chunk, 16 consecutive rows):
 // a stride of 4 banks mod 64 spreads them over all banks.  V rows are read with
