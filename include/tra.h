@@ -28,7 +28,9 @@
  *     last failure on the calling thread.
  *   - Supported on the device: dtype TRA_BF16 with head_dim 64 or 128 (bf16
  *     matrix cores), dtype TRA_F32 with head_dim 64 or 128 (fp32 vector path),
- *     8 x 8 tiles (tile_h = tile_w = 8).
+ *     8 x 8 tiles (tile_h = tile_w = 8).  T, H, W <= 32767;
+ *     B*heads*T*H*W < 2^31; for TRA_BF16 one head's K (T*H*W*head_dim*2 bytes)
+ *     below 2^31.  Larger shapes fail with TRA_ERR_SHAPE.
  */
 #ifndef TRA_H
 #define TRA_H

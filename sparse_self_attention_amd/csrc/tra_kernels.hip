@@ -688,15 +688,15 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
 // ---------------------------------------------------------------------------
 // Block-sparse attention, bf16, 8x8 tiles.
 //
-// Work decomposition.  A workgroup of 4 waves owns a group of G = 2*QB
-// neighbouring query tiles of one frame (QB = 1: a 1x2 pair, QB = 2: a 2x2
-// square) and walks the ascending union of their tile lists, merged on the fly
-// from the CSR rows.  Each key tile is fetched once per workgroup into one of
-// two LDS buffers with global_load_lds_dwordx4, so the next tile streams in
-// while the current one is consumed, and all 4 waves use it.  A wave owns QB
-// blocks of 32 queries (lane % 32 = query) and skips a 32-key half of a tile
-// whenever none of its queries retains a key there: tiles that only a
-// neighbouring query tile needs cost loads but no matrix work.
+// Work decomposition.  A workgroup of 4 waves owns two horizontally adjacent
+// query tiles of one frame and walks the ascending union of their tile lists,
+// prepared by the plan (pair_kernel).  Each key tile is streamed once per
+// workgroup into one of two LDS buffers by range-checked buffer DMA
+// (buffer_load_dwordx4 ... lds), so the next tile streams in while the
+// current one is consumed, and all 4 waves use it.  A wave owns 32 queries
+// (lane % 32 = query) and skips a 32-key half of a tile whenever none of its
+// queries retains a key there: tiles that only the neighbouring query tile
+// needs cost loads but no matrix work.
 //
 //   S^T (keys x queries) = K Q^T :  A = K rows from LDS, B = Q^T in registers
 //   O^T (d x queries)   += V^T P^T : A = V^T via ds_read_b64_tr_b16, B = P^T

@@ -67,11 +67,18 @@ def _validate(**kw):
     (dict(a=math.inf), "TRA_ERR_INVALID_ARG"),
     (dict(radius_override=1e9), "TRA_ERR_INVALID_ARG"),
     (dict(budget_max=1e12), "TRA_ERR_INVALID_ARG"),
+    # one bf16 head of K would span 2^31 bytes or more (32-bit buffer offsets)
+    (dict(grid=(2, 32767, 256), heads=1), "TRA_ERR_SHAPE"),
 ])
 def test_validation_rejects(kw, code):
     with pytest.raises(tra.TraError) as ei:
         _validate(**kw)
     assert ei.value.name == code
+
+
+def test_validation_accepts_large_fp32_head():
+    # the per-head byte limit applies to the bf16 path only
+    _validate(grid=(2, 32767, 256), heads=1, dtype=torch.float32)
 
 
 def test_validation_accepts_every_workload():
