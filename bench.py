@@ -170,6 +170,35 @@ def main():
     attn_ms = float(np.mean(attn_ms_all))
     log(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step, plan {plan_ms:.3f} ms, attention {attn_ms:.3f} ms/call")
 
+    # Cold caches: before each of a few extra calls, 512 MiB are written so that
+    # neither the L2s nor the 256 MB last-level cache hold Q, K, V or the plan.
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold_plan, cold_attn = [], []
+    for i in range(3):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        flush.fill_(i + 1)
+        ev[0].record(stream)
+        plan.rebuild(qs[0], ks[0])
+        ev[1].record(stream)
+        flush.fill_(i + 7)
+        ev[2].record(stream)
+        tra.attention(qs[-1], ks[-1], v, plan, out=outs[-1])
+        ev[3].record(stream)
+        torch.cuda.synchronize()
+        cold_plan.append(ev[0].elapsed_time(ev[1]))
+        cold_attn.append(ev[2].elapsed_time(ev[3]))
+    del flush
+    # Drift of the reused plan: queries whose level a re-plan from the inputs of
+    # the last call would change.
+    drift = plan.drift(qs[-1], ks[-1])
+    log(f"[bench] cold: plan {np.median(cold_plan):.3f} ms, attention {np.median(cold_attn):.3f} ms; "
+        f"plan drift at call {calls}: {drift} queries")
+
+    def pct(xs):
+        return {"p10": float(np.percentile(xs, 10)), "p50": float(np.percentile(xs, 50)),
+                "p90": float(np.percentile(xs, 90))}
+
+    plan_ms_all = [r["p0"].elapsed_time(r["p1"]) for r in recs]
     value = calls * flops_call / (ms_step * 1e-3) / 1e12
     achieved = flops_call / (attn_ms * 1e-3) / 1e12
     elem = 2 if cfg.dtype == "bf16" else 4
@@ -194,7 +223,13 @@ def main():
                    "retained_density": retained / (cfg.heads * cfg.N ** 2),
                    "tile_efficiency": retained / listed},
         "ms_per_call": {"attention": attn_ms, "plan": plan_ms, "step_per_call": ms_step / calls},
+        "timing_ms": {"attention": pct(attn_ms_all), "plan": pct(plan_ms_all),
+                      "cold_attention_median": float(np.median(cold_attn)),
+                      "cold_plan_median": float(np.median(cold_plan))},
+        "plan_drift": {"call": calls, "changed_levels": drift,
+                       "fraction": drift / (cfg.batch * cfg.heads * cfg.N)},
         "attention": {"retained_tflops": achieved, "frac_bf16_peak": achieved / PEAK_BF16_TFLOPS,
+                      "listed_flops_per_call": 4.0 * cfg.head_dim * listed,
                       "listed_pair_tflops": 4.0 * cfg.head_dim * listed / (attn_ms * 1e-3) / 1e12,
                       "retained_flops_per_call": flops_call},
         "plan": {"ms": plan_ms, "algorithmic_bytes": plan_bytes,

@@ -179,6 +179,18 @@ tra_status tra_plan_export(const tra_plan* plan, int16_t* levels, float* entropy
  */
 tra_status tra_plan_stats(const tra_plan* plan, int64_t* retained, int64_t* listed, void* stream);
 
+/*
+ * Plan drift (plans are reused across denoising steps, [TRA] section 2
+ * "Reutilisation Inter-Etapes"): the number of queries whose budget level
+ * would change if the plan were rebuilt from q and k.  Runs the pooling and
+ * entropy steps on q and k into temporary device memory (allocated and freed
+ * by this call) and compares the levels with the plan's; the plan is not
+ * modified.  Under radius_override every level is -1 and the drift is 0.
+ * Synchronises `stream`.
+ */
+tra_status tra_plan_drift(const tra_plan* plan, const void* q, const void* k, int64_t* changed,
+                          void* stream);
+
 void tra_plan_destroy(tra_plan* plan);
 
 const char* tra_status_string(tra_status s);

@@ -59,6 +59,7 @@ _SIGS = {
     "tra_plan_export": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P]),
     "tra_plan_stats": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int64),
                                       ctypes.POINTER(ctypes.c_int64), _P]),
+    "tra_plan_drift": (ctypes.c_int, [_P, _P, _P, ctypes.POINTER(ctypes.c_int64), _P]),
     "tra_plan_destroy": (None, [_P]),
     "tra_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "tra_last_error": (ctypes.c_char_p, []),
@@ -220,6 +221,16 @@ class Plan:
         _check(load_library().tra_plan_stats(self.handle, ctypes.byref(ret), ctypes.byref(lst),
                                              _stream(self.device)), "tra_plan_stats")
         return ret.value, lst.value
+
+    def drift(self, q, k):
+        """Number of queries whose budget level would change if the plan were
+        rebuilt from (q, k); the plan itself is not modified."""
+        self._check_tensor(q, "q")
+        self._check_tensor(k, "k")
+        n = ctypes.c_int64()
+        _check(load_library().tra_plan_drift(self.handle, _dev_ptr(q, "q"), _dev_ptr(k, "k"), ctypes.byref(n),
+                                             _stream(self.device)), "tra_plan_drift")
+        return n.value
 
     def _check_tensor(self, x, name):
         shape = _shape_of(x, self.grid)

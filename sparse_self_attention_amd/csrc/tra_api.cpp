@@ -414,6 +414,45 @@ tra_status tra_plan_stats(const tra_plan* plan, int64_t* retained, int64_t* list
   return TRA_OK;
 }
 
+tra_status tra_plan_drift(const tra_plan* plan, const void* q, const void* k, int64_t* changed,
+                          void* stream) {
+  if (!plan || !changed) return fail(TRA_ERR_INVALID_ARG, "plan and changed must not be NULL");
+  if (!q || !k) return fail(TRA_ERR_INVALID_ARG, "q and k must be device pointers");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k)) & 15)
+    return fail(TRA_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
+  *changed = 0;
+  if (plan->params.radius_override >= 0.0) return TRA_OK;
+  const tra_shape& s = plan->shape;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const size_t kbar_bytes = static_cast<size_t>(plan->BH) * plan->pool.count * s.head_dim * dtype_size(s.dtype);
+  void* kbar = nullptr;
+  float* H = nullptr;
+  int16_t* lv = nullptr;
+  unsigned long long* dev = nullptr;
+  hipError_t e = hipMalloc(&kbar, kbar_bytes);
+  if (e == hipSuccess) e = hipMalloc(&H, plan->n_queries * sizeof(float));
+  if (e == hipSuccess) e = hipMalloc(&lv, plan->n_queries * sizeof(int16_t));
+  if (e == hipSuccess) e = hipMalloc(&dev, sizeof(unsigned long long));
+  unsigned long long host = 0;
+  if (e == hipSuccess) e = hipMemsetAsync(dev, 0, sizeof(unsigned long long), hs);
+  if (e == hipSuccess) e = tra::launch_pool(s.dtype, s.head_dim, k, kbar, plan->BH, plan->pool, hs);
+  if (e == hipSuccess) {
+    const tra::EntropyArgs ea{plan->params.a, plan->params.c, plan->params.levels_per_nat, plan->table.k_lo,
+                              plan->table.k_hi};
+    e = tra::launch_entropy(s.dtype, s.head_dim, q, kbar, plan->pool_w, plan->BH, static_cast<int>(plan->N),
+                            plan->pool.count, ea, H, lv, hs);
+  }
+  if (e == hipSuccess) e = tra::launch_level_diff(plan->lv, lv, plan->n_queries, dev, hs);
+  if (e == hipSuccess) e = hipMemcpyAsync(&host, dev, sizeof(host), hipMemcpyDeviceToHost, hs);
+  if (e == hipSuccess) e = hipStreamSynchronize(hs);
+  for (void* b : {kbar, static_cast<void*>(H), static_cast<void*>(lv), static_cast<void*>(dev)})
+    if (b) (void)hipFree(b);
+  if (e != hipSuccess)
+    return fail(e == hipErrorOutOfMemory ? TRA_ERR_OOM : TRA_ERR_HIP, std::string("tra_plan_drift: ") + hipGetErrorString(e));
+  *changed = static_cast<int64_t>(host);
+  return TRA_OK;
+}
+
 void tra_plan_destroy(tra_plan* plan) {
   if (!plan) return;
   (void)hipDeviceSynchronize();

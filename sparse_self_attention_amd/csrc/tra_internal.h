@@ -79,6 +79,10 @@ hipError_t launch_pair_lists(int BH, const Grid& tiles, int DM, const int32_t* r
 // plus a compact radius table of n_r2c entries; 0 if it exceeds the device limit.
 size_t attention_lds_bytes(int d, int n_r2c);
 
+// Count of positions where two level arrays differ, added to *out.
+hipError_t launch_level_diff(const int16_t* a, const int16_t* b, int64_t n, unsigned long long* out,
+                             hipStream_t s);
+
 hipError_t launch_stats(const int16_t* lv, const int32_t* r2, int T, int row_base, int BH,
                         const Grid& tiles, const int32_t* row_ptr, const int32_t* col_idx,
                         unsigned long long* out2, hipStream_t s);

@@ -1331,6 +1331,25 @@ hipError_t launch_attention(int dtype, int d, const void* q, const void* k, cons
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void level_diff_kernel(const int16_t* __restrict__ a,
+                                                        const int16_t* __restrict__ b, int64_t n,
+                                                        unsigned long long* __restrict__ out) {
+  unsigned long long cnt = 0;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    cnt += a[i] != b[i];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
+  if ((threadIdx.x & 63) == 0 && cnt) atomicAdd(out, cnt);
+}
+
+hipError_t launch_level_diff(const int16_t* a, const int16_t* b, int64_t n, unsigned long long* out,
+                             hipStream_t s) {
+  const int64_t blocks = (n + 255) / 256;
+  level_diff_kernel<<<static_cast<unsigned>(blocks < 4096 ? blocks : 4096), 256, 0, s>>>(a, b, n, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_stats(const int16_t* lv, const int32_t* r2, int T, int row_base, int BH,
                         const Grid& tiles, const int32_t* row_ptr, const int32_t* col_idx,
                         unsigned long long* out2, hipStream_t s) {

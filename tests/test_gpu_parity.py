@@ -178,3 +178,33 @@ def test_plan_reuse_path(gpu):
         err = np.abs(o[0, h].double().cpu().numpy()[qs] - ref)
         _say("call", call, "head", h, err.max(), err.mean())
         assert err.max() <= 2e-2 and err.mean() <= 2e-3
+
+
+def test_plan_drift(gpu):
+    """Drift of a plan against new (Q, K): zero for its own inputs; for perturbed
+    inputs, the same count as a fresh plan's levels give, and the oracle's count
+    up to queries that sit within the excuse band of a level boundary."""
+    cfg = small_workload(T=3, H=13, W=21, heads=2, c=-0.5, budget_max=819.0)
+    q, k, v = make_inputs(cfg, device=gpu)
+    plan = tra.plan(q, k, grid=(cfg.T, cfg.H, cfg.W), **cfg.params())
+    assert plan.drift(q, k) == 0
+    q2, k2 = perturb(q, 3, 0, rel=0.2), perturb(k, 3, 1, rel=0.2)
+    n = plan.drift(q2, k2)
+    lv1 = plan.export()["levels"].astype(np.int64)
+    lv2 = tra.plan(q2, k2, grid=(cfg.T, cfg.H, cfg.W), **cfg.params()).export()["levels"].astype(np.int64)
+    assert n == int((lv1 != lv2).sum())
+    p = cfg.params()
+    pools = O.Geometry(cfg.T, cfg.H, cfg.W, cfg.pool_h, cfg.pool_w)
+    ref, slack = 0, 0
+    for h in range(cfg.heads):
+        lv_o, exc = [], set()
+        for qq, kk in ((q, k), (q2, k2)):
+            qh, kh = qq[0, h].double().cpu().numpy(), kk[0, h].double().cpu().numpy()
+            Hh = O.entropy(qh, O.pool_keys(kh, pools, cfg.dtype), pools.block_sizes())
+            lv_o.append(O.levels(Hh, p))
+            exc |= set(O.excused_queries(Hh, p).tolist())
+        ref += int((lv_o[0] != lv_o[1]).sum())
+        slack += len(exc)
+    _say("drift", n, "oracle", ref, "excused", slack, "of", cfg.heads * cfg.N)
+    assert n > 0
+    assert abs(n - ref) <= slack
