@@ -42,7 +42,7 @@ __all__ = [
     "Geometry", "pool_keys", "entropy", "explicit_softmax_entropy", "level_range", "levels",
     "frame_sum", "radius_table", "table_margin", "retained_keys", "retained_count",
     "retained_counts", "dense_mask", "query_tile_row", "csr", "attention_rows",
-    "dense_attention", "excused_queries", "round_to_dtype", "plan", "ENTROPY_EXCUSE",
+    "dense_attention", "dense_entropy", "excused_queries", "round_to_dtype", "plan", "ENTROPY_EXCUSE",
 ]
 
 ENTROPY_EXCUSE = 1e-5  # queries this close (nats) to a level boundary may differ
@@ -403,6 +403,28 @@ def dense_attention(q, k, v, mask=None):
     s -= s.max(axis=1, keepdims=True)
     e = np.exp(s)
     return (e / e.sum(axis=1, keepdims=True)) @ v
+
+
+# ----------------------------------------------------------------------------
+# Warm-up variant: the entropy measured on a dense pass
+# ----------------------------------------------------------------------------
+def dense_entropy(q, k):
+    """Entropy of each query's full softmax over all N keys, fp64:
+    H_i = -sum_j p_ij ln p_ij with p_i = softmax_j(q_i.k_j/sqrt(d)).
+
+    The summary page's pipeline ("Le Pipeline TRA", entropy-to-budget step)
+    takes the entropy during dense warm-up steps, on the full attention rather
+    than on pooled keys; levels, radii and tile lists then follow the same
+    steps 4-7 as the pooled estimate.
+    """
+    q, k = (np.asarray(x, dtype=np.float64) for x in (q, k))
+    s = (q @ k.T) / math.sqrt(q.shape[1])
+    s -= s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    p /= p.sum(axis=1, keepdims=True)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        terms = np.where(p > 0, -p * np.log(p), 0.0)
+    return terms.sum(axis=1)
 
 
 # ----------------------------------------------------------------------------

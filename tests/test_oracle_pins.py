@@ -161,6 +161,49 @@ def test_entropy_bounds_on_generated_inputs():
 
 
 # ---------------------------------------------------------------------------
+# Dense (warm-up) entropy
+# ---------------------------------------------------------------------------
+def test_dense_entropy_matches_scipy():
+    from scipy.special import softmax
+    from scipy.stats import entropy as scipy_entropy
+    rng = np.random.default_rng(21)
+    d = 32
+    q = rng.standard_normal((9, d)) * rng.uniform(0.2, 8.0, size=(9, 1))
+    k = rng.standard_normal((150, d))
+    ref = scipy_entropy(softmax(q @ k.T / math.sqrt(d), axis=1), axis=1)
+    assert np.max(np.abs(O.dense_entropy(q, k) - ref)) < 1e-11
+
+
+def test_dense_entropy_is_pooled_entropy_with_one_token_blocks():
+    """With 1x1 pool blocks the pooled-key entropy (log-sum-exp form) is the
+    dense entropy (-sum p ln p form)."""
+    T, H, W, d = 2, 5, 7, 16
+    geom = O.Geometry(T, H, W, 1, 1)
+    rng = np.random.default_rng(22)
+    q = rng.standard_normal((11, d)) * 4.0
+    k = rng.standard_normal((T * H * W, d)).astype(np.float32).astype(np.float64)
+    kbar = O.pool_keys(k, geom, "fp32")
+    assert np.array_equal(kbar, k)
+    assert np.max(np.abs(O.dense_entropy(q, k) - O.entropy(q, kbar, geom.block_sizes()))) < 1e-11
+
+
+def test_dense_entropy_closed_forms():
+    d, n1, n2 = 8, 13, 29
+    rng = np.random.default_rng(23)
+    q = rng.standard_normal((4, d)) * 2.0
+    same = np.tile(rng.standard_normal((1, d)), (n1 + n2, 1))
+    assert np.allclose(O.dense_entropy(q, same), math.log(n1 + n2), atol=1e-12, rtol=0)
+    # n1 copies of key a and n2 of key b: H = h(p) + p ln n1 + (1-p) ln n2, where
+    # p is the total probability of the a copies.
+    ka, kb = rng.standard_normal(d), rng.standard_normal(d)
+    keys = np.vstack([np.tile(ka, (n1, 1)), np.tile(kb, (n2, 1))])
+    za, zb = q @ ka / math.sqrt(d), q @ kb / math.sqrt(d)
+    pa = n1 * np.exp(za) / (n1 * np.exp(za) + n2 * np.exp(zb))
+    expected = -pa * np.log(pa) - (1 - pa) * np.log(1 - pa) + pa * math.log(n1) + (1 - pa) * math.log(n2)
+    assert np.max(np.abs(O.dense_entropy(q, keys) - expected)) < 1e-12
+
+
+# ---------------------------------------------------------------------------
 # Levels
 # ---------------------------------------------------------------------------
 def test_levels_by_search():
