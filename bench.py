@@ -194,6 +194,33 @@ def main():
     log(f"[bench] cold: plan {np.median(cold_plan):.3f} ms, attention {np.median(cold_attn):.3f} ms; "
         f"plan drift at call {calls}: {drift} queries")
 
+    # Dense attention over all keys on the same inputs (the full attention the
+    # sparse path replaces) and the dense warm-up pass that also yields each
+    # query's exact entropy.
+    def time_ms(fn, reps):
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    H_warm = torch.empty((cfg.batch, cfg.heads, cfg.N), dtype=torch.float32, device=dev)
+
+    def dense(with_entropy):
+        tra.dense_attention(q, k, v, grid, out=outs[0], entropy=H_warm if with_entropy else False)
+
+    dense(False)
+    dense(True)
+    torch.cuda.synchronize()
+    dense_ms = time_ms(lambda: dense(False), 3)
+    dense_ent_ms = time_ms(lambda: dense(True), 3)
+    dense_flops = 4.0 * cfg.head_dim * cfg.batch * cfg.heads * float(cfg.N) ** 2
+    log(f"[bench] dense attention {dense_ms:.2f} ms, dense warm-up pass with entropy {dense_ent_ms:.2f} ms")
+
     def pct(xs):
         return {"p10": float(np.percentile(xs, 10)), "p50": float(np.percentile(xs, 50)),
                 "p90": float(np.percentile(xs, 90))}
@@ -226,6 +253,11 @@ def main():
         "timing_ms": {"attention": pct(attn_ms_all), "plan": pct(plan_ms_all),
                       "cold_attention_median": float(np.median(cold_attn)),
                       "cold_plan_median": float(np.median(cold_plan))},
+        "dense": {"ms": dense_ms, "tflops": dense_flops / (dense_ms * 1e-3) / 1e12,
+                  "frac_bf16_peak": dense_flops / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                  "warmup_with_entropy_ms": dense_ent_ms,
+                  "sparse_attention_speedup": dense_ms / attn_ms,
+                  "step_speedup": (calls * dense_ms) / ms_step},
         "plan_drift": {"call": calls, "changed_levels": drift,
                        "fraction": drift / (cfg.batch * cfg.heads * cfg.N)},
         "attention": {"retained_tflops": achieved, "frac_bf16_peak": achieved / PEAK_BF16_TFLOPS,

@@ -14,6 +14,8 @@
  * Two calls form the path:
  *   tra_plan_create  entropy -> budget level -> radius table -> CSR tile lists
  *   tra_attention    block-sparse softmax attention with the exact per-token mask
+ * and a dense warm-up variant measures the entropy on the full attention
+ * (tra_dense_attention, then tra_plan_create_from_entropy).
  * A plan is reusable across calls whose Q/K/V have the plan's shape (the pages'
  * warm-up reuse: entropy is measured once and reused in later denoising steps).
  *
@@ -190,6 +192,36 @@ tra_status tra_plan_stats(const tra_plan* plan, int64_t* retained, int64_t* list
  */
 tra_status tra_plan_drift(const tra_plan* plan, const void* q, const void* k, int64_t* changed,
                           void* stream);
+
+/*
+ * Dense warm-up pass ([TRA] section 2, "Le Pipeline TRA", entropy-to-budget
+ * step: the entropy is measured on the full attention of dense warm-up steps):
+ *   O_i = sum_j softmax_j(q_i . k_j / sqrt(d)) v_j over all N keys of the head,
+ *   H_i = -sum_j p_ij ln p_ij of that same softmax (when entropy != NULL).
+ * q, k, v, o: device [B, heads, N, d] of the shape's dtype (same limits as
+ * tra_plan_create); o must not alias q, k or v.  entropy: device float
+ * [B*heads*N] or NULL (then only O is computed).  bf16 runs on matrix cores
+ * with fp32 softmax and fp64 entropy sums; fp32 inputs use fp64 scores.
+ * Asynchronous on `stream`; allocates nothing.
+ */
+tra_status tra_dense_attention(const tra_shape* shape, const void* q, const void* k, const void* v,
+                               void* o, float* entropy, void* stream);
+
+/*
+ * Build a plan whose budget levels come from given per-query entropies
+ * (device float [B*heads*N], e.g. those of tra_dense_attention) instead of
+ * the pooled-key estimate: k_i = clamped level of entropy[i], then the same
+ * radius table and tile lists as tra_plan_create.  The entropies are copied
+ * into the plan (tra_plan_export returns them); the plan's pooled keys are
+ * zero.  Under radius_override the entropies are ignored.  Synchronises
+ * `stream` once.
+ */
+tra_status tra_plan_create_from_entropy(const tra_shape* shape, const tra_params* params,
+                                        const float* entropy, void* stream, tra_plan** out);
+
+/* tra_plan_rebuild with levels from given entropies (see
+ * tra_plan_create_from_entropy).  Pooled keys keep their last values. */
+tra_status tra_plan_rebuild_from_entropy(tra_plan* plan, const float* entropy, void* stream);
 
 void tra_plan_destroy(tra_plan* plan);
 

@@ -7,6 +7,11 @@ kernels.  PyTorch supplies device memory and the current stream.
     plan = tra.plan(q, k, grid=(T, H, W), **params)   # entropy -> radius -> tile lists
     o    = tra.attention(q, k, v, plan)                 # block-sparse masked attention
 
+Dense warm-up variant (the entropy taken on the full attention):
+
+    o, H = tra.dense_attention(q, k, v, grid=(T, H, W), entropy=True)
+    plan = tra.plan_from_entropy(H, grid=(T, H, W), head_dim=d, dtype=q.dtype, **params)
+
 q, k, v: contiguous [B, heads, T*H*W, d] CUDA tensors (bfloat16 or float32).
 """
 import ctypes
@@ -14,7 +19,8 @@ import os
 
 import torch
 
-__all__ = ["TraError", "Plan", "plan", "attention", "radius_table", "validate", "library_path",
+__all__ = ["TraError", "Plan", "plan", "plan_from_entropy", "attention", "dense_attention", "radius_table",
+           "validate", "library_path",
            "load_library", "DEFAULT_PARAMS", "EXPORTED_SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -60,6 +66,10 @@ _SIGS = {
     "tra_plan_stats": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int64),
                                       ctypes.POINTER(ctypes.c_int64), _P]),
     "tra_plan_drift": (ctypes.c_int, [_P, _P, _P, ctypes.POINTER(ctypes.c_int64), _P]),
+    "tra_plan_create_from_entropy": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.POINTER(_Params), _P, _P,
+                                                    ctypes.POINTER(_P)]),
+    "tra_plan_rebuild_from_entropy": (ctypes.c_int, [_P, _P, _P]),
+    "tra_dense_attention": (ctypes.c_int, [ctypes.POINTER(_Shape), _P, _P, _P, _P, _P, _P]),
     "tra_plan_destroy": (None, [_P]),
     "tra_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "tra_last_error": (ctypes.c_char_p, []),
@@ -232,6 +242,12 @@ class Plan:
                                              _stream(self.device)), "tra_plan_drift")
         return n.value
 
+    def rebuild_from_entropy(self, entropy):
+        """Re-plan from per-query entropies ([B, heads, N] float32 device tensor)."""
+        _check_entropy(entropy, self.shape)
+        _check(load_library().tra_plan_rebuild_from_entropy(self.handle, _dev_ptr(entropy, "entropy"),
+                                                            _stream(self.device)), "tra_plan_rebuild_from_entropy")
+
     def _check_tensor(self, x, name):
         shape = _shape_of(x, self.grid)
         st = load_library().tra_plan_matches(self.handle, ctypes.byref(shape))
@@ -275,3 +291,51 @@ def attention(q, k, v, plan, out=None):
                                         _dev_ptr(v, "v"), _dev_ptr(out, "out"), _stream(q.device)),
            "tra_attention")
     return out
+
+
+def _check_entropy(entropy, shape):
+    N = shape.T * shape.H * shape.W
+    if entropy.dtype != torch.float32 or tuple(entropy.shape) != (shape.B, shape.heads, N):
+        raise ValueError(f"entropy must be a float32 [{shape.B}, {shape.heads}, {N}] tensor")
+
+
+def plan_from_entropy(entropy, grid, head_dim, dtype=torch.bfloat16, **params):
+    """Plan whose budget levels come from given per-query entropies (for example
+    the exact ones of `dense_attention(..., entropy=True)`) instead of pooled keys."""
+    if entropy.dim() != 3:
+        raise ValueError("entropy must be [B, heads, T*H*W]")
+    shape = _make_shape(entropy.shape[0], entropy.shape[1], grid, head_dim, _DTYPES[dtype])
+    _check_entropy(entropy, shape)
+    prm = _make_params(params)
+    h = _P()
+    _check(load_library().tra_plan_create_from_entropy(ctypes.byref(shape), ctypes.byref(prm),
+                                                       _dev_ptr(entropy, "entropy"), _stream(entropy.device),
+                                                       ctypes.byref(h)), "tra_plan_create_from_entropy")
+    return Plan(h, shape, tuple(grid), prm, entropy.device)
+
+
+def dense_attention(q, k, v, grid, out=None, entropy=False):
+    """Dense softmax attention over all keys of each head (the warm-up pass).
+    With entropy=True (or a float32 [B, heads, N] device tensor to fill) also
+    returns each query's exact attention entropy: (out, H)."""
+    shape = _shape_of(q, grid)
+    for x, nm in ((k, "k"), (v, "v")):
+        if x.shape != q.shape or x.dtype != q.dtype:
+            raise ValueError(f"{nm} must match q in shape and dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    if isinstance(entropy, torch.Tensor):
+        H = entropy
+        _check_entropy(H, shape)
+    elif entropy:
+        H = torch.empty((q.shape[0], q.shape[1], q.shape[2]), dtype=torch.float32, device=q.device)
+    else:
+        H = None
+    _check(load_library().tra_dense_attention(ctypes.byref(shape), _dev_ptr(q, "q"), _dev_ptr(k, "k"),
+                                              _dev_ptr(v, "v"), _dev_ptr(out, "out"),
+                                              _dev_ptr(H, "entropy") if H is not None else None,
+                                              _stream(q.device)),
+           "tra_dense_attention")
+    return (out, H) if H is not None else out

@@ -177,15 +177,21 @@ void release(tra_plan* p) {
   delete p;
 }
 
-// Steps entropy -> level -> tile lists into the plan's buffers.
-tra_status build(tra_plan* p, const void* q, const void* k, hipStream_t st) {
+// Steps entropy -> level -> tile lists into the plan's buffers.  The levels
+// come from the pooled-key entropy of (q, k), or, when `Hin` is not NULL, from
+// the given per-query entropies.
+tra_status build(tra_plan* p, const void* q, const void* k, const float* Hin, hipStream_t st) {
   const tra_shape& s = p->shape;
   const int d = s.head_dim;
   if (p->params.radius_override < 0.0) {
-    TRA_HIP(tra::launch_pool(s.dtype, d, k, p->kbar, p->BH, p->pool, st));
     tra::EntropyArgs ea{p->params.a, p->params.c, p->params.levels_per_nat, p->table.k_lo, p->table.k_hi};
-    TRA_HIP(tra::launch_entropy(s.dtype, d, q, p->kbar, p->pool_w, p->BH, static_cast<int>(p->N),
-                                p->pool.count, ea, p->H, p->lv, st));
+    if (Hin) {
+      TRA_HIP(tra::launch_levels_from_entropy(Hin, p->n_queries, ea, p->H, p->lv, st));
+    } else {
+      TRA_HIP(tra::launch_pool(s.dtype, d, k, p->kbar, p->BH, p->pool, st));
+      TRA_HIP(tra::launch_entropy(s.dtype, d, q, p->kbar, p->pool_w, p->BH, static_cast<int>(p->N),
+                                  p->pool.count, ea, p->H, p->lv, st));
+    }
   } else {
     TRA_HIP(tra::launch_fill_levels(p->lv, p->H, p->n_queries, st));
   }
@@ -244,20 +250,14 @@ tra_status tra_radius_table(const tra_shape* shape, const tra_params* params, in
   return TRA_OK;
 }
 
-tra_status tra_plan_create(const tra_shape* shape, const tra_params* params, const void* q,
-                           const void* k, void* stream, tra_plan** out) {
-  if (!out) return fail(TRA_ERR_INVALID_ARG, "out is NULL");
-  *out = nullptr;
-  tra_status st = check_shape(shape);
-  if (st != TRA_OK) return st;
-  Table tab;
-  st = check_params(shape, params, &tab);
-  if (st != TRA_OK) return st;
-  if (!q || !k) return fail(TRA_ERR_INVALID_ARG, "q and k must be device pointers");
-  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k)) & 15)
-    return fail(TRA_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
-  hipStream_t hs = static_cast<hipStream_t>(stream);
+}  // extern "C"
 
+namespace {
+
+// Validated shape and params -> a plan with every buffer allocated and the
+// radius table uploaded, levels and tile lists not yet built.
+tra_status create_plan(const tra_shape* shape, const tra_params* params, Table&& tab, hipStream_t hs,
+                       tra_plan** out) {
   tra_plan* p = new tra_plan();
   p->shape = *shape;
   p->params = *params;
@@ -307,8 +307,6 @@ tra_status tra_plan_create(const tra_shape* shape, const tra_params* params, con
     TRA_HIP_P(hipMalloc(&p->pair_len, n_pairs * sizeof(int32_t)));
   }
   TRA_HIP_P(hipHostMalloc(&p->totals_host, 4 * sizeof(int64_t)));
-  if (params->radius_override >= 0.0)
-    TRA_HIP_P(hipMemsetAsync(p->kbar, 0, static_cast<size_t>(p->BH) * p->pool.count * shape->head_dim * es, hs));
 
   std::vector<float> w(p->pool.count);
   for (int b = 0; b < p->pool.count; ++b) {
@@ -321,10 +319,103 @@ tra_status tra_plan_create(const tra_shape* shape, const tra_params* params, con
   TRA_HIP_P(hipMemcpy(p->pool_w, w.data(), w.size() * sizeof(float), hipMemcpyHostToDevice));
   TRA_HIP_P(hipMemcpy(p->r2c, p->table.r2c.data(), p->table.r2c.size() * sizeof(int32_t), hipMemcpyHostToDevice));
   TRA_HIP_P(hipMemcpy(p->r2off, p->table.r2off.data(), p->table.r2off.size() * sizeof(int32_t), hipMemcpyHostToDevice));
+  // Pooled keys stay zero until a build from (q, k) writes them.
+  TRA_HIP_P(hipMemsetAsync(p->kbar, 0, static_cast<size_t>(p->BH) * p->pool.count * shape->head_dim * es, hs));
 #undef TRA_HIP_P
-  st = build(p, q, k, hs);
-  if (st != TRA_OK) return fin(st);
   *out = p;
+  return TRA_OK;
+}
+
+tra_status check_qk(const void* q, const void* k) {
+  if (!q || !k) return fail(TRA_ERR_INVALID_ARG, "q and k must be device pointers");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k)) & 15)
+    return fail(TRA_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
+  return TRA_OK;
+}
+
+tra_status check_entropy_ptr(const float* H) {
+  if (!H) return fail(TRA_ERR_INVALID_ARG, "entropy must be a device pointer");
+  if (reinterpret_cast<uintptr_t>(H) & 3) return fail(TRA_ERR_INVALID_ARG, "entropy must be 4-byte aligned");
+  return TRA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tra_status tra_plan_create(const tra_shape* shape, const tra_params* params, const void* q,
+                           const void* k, void* stream, tra_plan** out) {
+  if (!out) return fail(TRA_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  tra_status st = check_shape(shape);
+  if (st != TRA_OK) return st;
+  Table tab;
+  st = check_params(shape, params, &tab);
+  if (st != TRA_OK) return st;
+  st = check_qk(q, k);
+  if (st != TRA_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  tra_plan* p = nullptr;
+  st = create_plan(shape, params, std::move(tab), hs, &p);
+  if (st != TRA_OK) return st;
+  st = build(p, q, k, nullptr, hs);
+  if (st != TRA_OK) {
+    release(p);
+    return st;
+  }
+  *out = p;
+  return TRA_OK;
+}
+
+tra_status tra_plan_create_from_entropy(const tra_shape* shape, const tra_params* params,
+                                        const float* entropy, void* stream, tra_plan** out) {
+  if (!out) return fail(TRA_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  tra_status st = check_shape(shape);
+  if (st != TRA_OK) return st;
+  Table tab;
+  st = check_params(shape, params, &tab);
+  if (st != TRA_OK) return st;
+  st = check_entropy_ptr(entropy);
+  if (st != TRA_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  tra_plan* p = nullptr;
+  st = create_plan(shape, params, std::move(tab), hs, &p);
+  if (st != TRA_OK) return st;
+  st = build(p, nullptr, nullptr, entropy, hs);
+  if (st != TRA_OK) {
+    release(p);
+    return st;
+  }
+  *out = p;
+  return TRA_OK;
+}
+
+tra_status tra_plan_rebuild_from_entropy(tra_plan* plan, const float* entropy, void* stream) {
+  if (!plan) return fail(TRA_ERR_INVALID_ARG, "plan is NULL");
+  const tra_status st = check_entropy_ptr(entropy);
+  if (st != TRA_OK) return st;
+  return build(plan, nullptr, nullptr, entropy, static_cast<hipStream_t>(stream));
+}
+
+tra_status tra_dense_attention(const tra_shape* shape, const void* q, const void* k, const void* v,
+                               void* o, float* entropy, void* stream) {
+  tra_status st = check_shape(shape);
+  if (st != TRA_OK) return st;
+  if (shape->dtype == TRA_BF16 &&
+      static_cast<int64_t>(shape->T) * shape->H * shape->W * shape->head_dim * 2 >= (int64_t(1) << 31))
+    return fail(TRA_ERR_SHAPE, "bf16 attention needs T*H*W*head_dim*2 (bytes of one head) below 2^31");
+  if (!q || !k || !v || !o) return fail(TRA_ERR_INVALID_ARG, "q, k, v and o must be device pointers");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) |
+       reinterpret_cast<uintptr_t>(o)) & 15)
+    return fail(TRA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+  if (o == q || o == k || o == v) return fail(TRA_ERR_INVALID_ARG, "o must not alias q, k or v");
+  if (entropy && (reinterpret_cast<uintptr_t>(entropy) & 3))
+    return fail(TRA_ERR_INVALID_ARG, "entropy must be 4-byte aligned");
+  const int BH = shape->B * shape->heads;
+  const int N = shape->T * shape->H * shape->W;
+  TRA_HIP(tra::launch_dense(shape->dtype, shape->head_dim, q, k, v, o, entropy, BH, N,
+                            static_cast<hipStream_t>(stream)));
   return TRA_OK;
 }
 
@@ -347,10 +438,9 @@ tra_status tra_attention(const tra_plan* plan, const void* q, const void* k, con
 
 tra_status tra_plan_rebuild(tra_plan* plan, const void* q, const void* k, void* stream) {
   if (!plan) return fail(TRA_ERR_INVALID_ARG, "plan is NULL");
-  if (!q || !k) return fail(TRA_ERR_INVALID_ARG, "q and k must be device pointers");
-  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k)) & 15)
-    return fail(TRA_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
-  return build(plan, q, k, static_cast<hipStream_t>(stream));
+  const tra_status st = check_qk(q, k);
+  if (st != TRA_OK) return st;
+  return build(plan, q, k, nullptr, static_cast<hipStream_t>(stream));
 }
 
 tra_status tra_plan_matches(const tra_plan* plan, const tra_shape* shape) {

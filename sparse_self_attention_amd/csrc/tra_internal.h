@@ -83,6 +83,15 @@ size_t attention_lds_bytes(int d, int n_r2c);
 hipError_t launch_level_diff(const int16_t* a, const int16_t* b, int64_t n, unsigned long long* out,
                              hipStream_t s);
 
+// Dense warm-up pass (tra_dense.hip): O = softmax(Q K^T / sqrt(d)) V over all N
+// keys of each head and, when H is not NULL, each query's exact attention
+// entropy into H (fp32, B*heads*N).
+hipError_t launch_dense(int dtype, int d, const void* q, const void* k, const void* v, void* o,
+                        float* H, int BH, int N, hipStream_t s);
+// Levels of n queries from given entropies; the entropies are copied to Hout.
+hipError_t launch_levels_from_entropy(const float* Hin, int64_t n, const EntropyArgs& ea, float* Hout,
+                                      int16_t* lv, hipStream_t s);
+
 hipError_t launch_stats(const int16_t* lv, const int32_t* r2, int T, int row_base, int BH,
                         const Grid& tiles, const int32_t* row_ptr, const int32_t* col_idx,
                         unsigned long long* out2, hipStream_t s);

@@ -110,3 +110,52 @@ def test_binding_rejects_host_tensors():
     q = torch.zeros((1, 1, 8 * 8, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         tra.plan(q, q, grid=(1, 8, 8))
+
+
+def _shape(dtype=1, head_dim=128, grid=(2, 8, 8)):
+    T, H, W = grid
+    return tra._Shape(1, 2, T, H, W, head_dim, dtype)
+
+
+def test_dense_attention_rejects_bad_arguments_before_any_device_call():
+    """Argument checks of the dense warm-up entry point run on the host."""
+    lib = tra.load_library()
+    P = ctypes.c_void_p
+    ok = P(4096)  # never dereferenced: every call below fails validation first
+    name = lambda st: lib.tra_status_string(st).decode()
+    assert name(lib.tra_dense_attention(None, ok, ok, ok, P(8192), None, None)) == "TRA_ERR_INVALID_ARG"
+    assert name(lib.tra_dense_attention(ctypes.byref(_shape(head_dim=96)), ok, ok, ok, P(8192), None, None)) \
+        == "TRA_ERR_DTYPE"
+    assert name(lib.tra_dense_attention(ctypes.byref(_shape()), None, ok, ok, P(8192), None, None)) \
+        == "TRA_ERR_INVALID_ARG"
+    assert name(lib.tra_dense_attention(ctypes.byref(_shape()), P(4100), ok, ok, P(8192), None, None)) \
+        == "TRA_ERR_INVALID_ARG"  # misaligned
+    assert name(lib.tra_dense_attention(ctypes.byref(_shape()), ok, ok, ok, ok, None, None)) \
+        == "TRA_ERR_INVALID_ARG"  # o aliases q
+    assert name(lib.tra_dense_attention(ctypes.byref(_shape()), ok, ok, ok, P(8192), P(8194), None)) \
+        == "TRA_ERR_INVALID_ARG"  # misaligned entropy
+
+
+def test_plan_from_entropy_rejects_bad_arguments_before_any_device_call():
+    lib = tra.load_library()
+    out = ctypes.c_void_p()
+    prm = tra._make_params({})
+    name = lambda st: lib.tra_status_string(st).decode()
+    assert name(lib.tra_plan_create_from_entropy(ctypes.byref(_shape()), ctypes.byref(prm), None, None,
+                                                 ctypes.byref(out))) == "TRA_ERR_INVALID_ARG"
+    assert out.value is None
+    bad = tra._make_params({"decay": 0.0})
+    assert name(lib.tra_plan_create_from_entropy(ctypes.byref(_shape()), ctypes.byref(bad),
+                                                 ctypes.c_void_p(4096), None, ctypes.byref(out))) \
+        == "TRA_ERR_INVALID_ARG"
+    assert name(lib.tra_plan_rebuild_from_entropy(None, ctypes.c_void_p(4096), None)) == "TRA_ERR_INVALID_ARG"
+
+
+def test_binding_dense_checks_shapes_on_host():
+    q = torch.zeros((1, 1, 2 * 8 * 8, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        tra.dense_attention(q, q, q, grid=(2, 8, 8))  # host tensors
+    with pytest.raises(ValueError):
+        tra.dense_attention(q, q[..., :32].contiguous(), q, grid=(2, 8, 8))
+    with pytest.raises(ValueError):
+        tra.plan_from_entropy(torch.zeros((1, 1, 5)), grid=(2, 8, 8), head_dim=64)
