@@ -225,6 +225,50 @@ tra_status tra_plan_rebuild_from_entropy(tra_plan* plan, const float* entropy, v
 
 void tra_plan_destroy(tra_plan* plan);
 
+/*
+ * Reuse schedule across denoising steps ([TRA] section 2, "Le Pipeline TRA":
+ * entropy measured during dense warm-up steps, then reused by the sparse
+ * steps that follow, relying on the stability of the entropy across steps).
+ * One call per denoising step, in order; each computes that step's attention
+ * output o from its q, k, v (device [B, heads, N, d] of the shape's dtype):
+ *   step < warmup_steps - 1        TRA_STEP_DENSE: dense attention
+ *   step == warmup_steps - 1       TRA_STEP_DENSE_REPLAN: dense attention with
+ *                                  exact entropies, plan built from them
+ *   later                          TRA_STEP_SPARSE: sparse attention under the
+ *                                  plan, unless a refresh is due, which runs as
+ *                                  TRA_STEP_DENSE_REPLAN instead
+ * A refresh is due after refresh_every sparse steps (0 = never), and on the
+ * step after a sparse step whose drift exceeded drift_threshold * B*heads*N
+ * queries.  Drift (tracked when drift_threshold >= 0) is the number of queries
+ * whose pooled-key budget level differs from the level the pooled estimate
+ * gave on the inputs of the last re-plan step; measuring it costs one pooling
+ * and entropy pass and one stream synchronisation per sparse step.
+ * The schedule owns its plan and buffers; tra_schedule_step returns the
+ * step's mode and drift (-1 if not measured) in *info (may be NULL).
+ */
+typedef struct {
+  int32_t warmup_steps;   /* >= 1 */
+  int32_t refresh_every;  /* >= 0 */
+  double drift_threshold; /* fraction of queries; < 0: no drift tracking */
+} tra_schedule_params;
+
+typedef enum { TRA_STEP_DENSE = 0, TRA_STEP_DENSE_REPLAN = 1, TRA_STEP_SPARSE = 2 } tra_step_mode;
+
+typedef struct {
+  int32_t step, mode; /* mode: tra_step_mode */
+  int64_t drift;
+} tra_step_info;
+
+typedef struct tra_schedule tra_schedule;
+
+tra_status tra_schedule_create(const tra_shape* shape, const tra_params* params, const tra_schedule_params* sp,
+                               tra_schedule** out);
+tra_status tra_schedule_step(tra_schedule* sched, const void* q, const void* k, const void* v, void* o,
+                             void* stream, tra_step_info* info);
+/* The schedule's current plan (borrowed; NULL before the first re-plan step). */
+tra_status tra_schedule_plan(const tra_schedule* sched, const tra_plan** plan);
+void tra_schedule_destroy(tra_schedule* sched);
+
 const char* tra_status_string(tra_status s);
 
 /* Message describing the last failing call on this thread ("" if none). */

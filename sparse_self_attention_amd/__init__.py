@@ -19,7 +19,8 @@ import os
 
 import torch
 
-__all__ = ["TraError", "Plan", "plan", "plan_from_entropy", "attention", "dense_attention", "radius_table",
+__all__ = ["TraError", "Plan", "plan", "plan_from_entropy", "attention", "dense_attention", "Schedule",
+           "STEP_MODES", "radius_table",
            "validate", "library_path",
            "load_library", "DEFAULT_PARAMS", "EXPORTED_SYMBOLS"]
 
@@ -51,6 +52,15 @@ class _Info(ctypes.Structure):
                 ("max_row_len", ctypes.c_int32)]
 
 
+class _SchedParams(ctypes.Structure):
+    _fields_ = [("warmup_steps", ctypes.c_int32), ("refresh_every", ctypes.c_int32),
+                ("drift_threshold", ctypes.c_double)]
+
+
+class _StepInfo(ctypes.Structure):
+    _fields_ = [("step", ctypes.c_int32), ("mode", ctypes.c_int32), ("drift", ctypes.c_int64)]
+
+
 _P = ctypes.c_void_p
 _SIGS = {
     "tra_params_validate": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.POINTER(_Params)]),
@@ -70,6 +80,11 @@ _SIGS = {
                                                     ctypes.POINTER(_P)]),
     "tra_plan_rebuild_from_entropy": (ctypes.c_int, [_P, _P, _P]),
     "tra_dense_attention": (ctypes.c_int, [ctypes.POINTER(_Shape), _P, _P, _P, _P, _P, _P]),
+    "tra_schedule_create": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.POINTER(_Params),
+                                           ctypes.POINTER(_SchedParams), ctypes.POINTER(_P)]),
+    "tra_schedule_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.POINTER(_StepInfo)]),
+    "tra_schedule_plan": (ctypes.c_int, [_P, ctypes.POINTER(_P)]),
+    "tra_schedule_destroy": (None, [_P]),
     "tra_plan_destroy": (None, [_P]),
     "tra_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "tra_last_error": (ctypes.c_char_p, []),
@@ -339,3 +354,63 @@ def dense_attention(q, k, v, grid, out=None, entropy=False):
                                               _stream(q.device)),
            "tra_dense_attention")
     return (out, H) if H is not None else out
+
+
+STEP_MODES = ("dense", "dense_replan", "sparse")
+
+
+class _BorrowedPlan(Plan):
+    """A plan owned by a Schedule (never destroyed from Python)."""
+
+    def destroy(self):
+        self._h = None
+
+
+class Schedule:
+    """Reuse schedule across denoising steps: `warmup_steps` dense steps (the last
+    one measures exact entropies and builds the plan), then sparse steps under
+    that plan; the plan is rebuilt by a dense step every `refresh_every` sparse
+    steps (0 = never) and after a sparse step whose pooled-level drift exceeds
+    `drift_threshold` of the queries (< 0: not tracked)."""
+
+    def __init__(self, q, grid, warmup_steps=1, refresh_every=0, drift_threshold=-1.0, **params):
+        self.shape = _shape_of(q, grid)
+        self.grid = tuple(grid)
+        self.device = q.device
+        self.params = _make_params(params)
+        sp = _SchedParams(int(warmup_steps), int(refresh_every), float(drift_threshold))
+        h = _P()
+        _check(load_library().tra_schedule_create(ctypes.byref(self.shape), ctypes.byref(self.params),
+                                                  ctypes.byref(sp), ctypes.byref(h)), "tra_schedule_create")
+        self._h = h
+
+    def step(self, q, k, v, out=None):
+        """Attention output of the next step and {"step", "mode", "drift"}."""
+        fields = lambda sh: tuple(getattr(sh, f) for f, _ in _Shape._fields_)
+        for x, nm in ((q, "q"), (k, "k"), (v, "v")):
+            if fields(_shape_of(x, self.grid)) != fields(self.shape):
+                raise ValueError(f"{nm} does not match the schedule's shape")
+        if out is None:
+            out = torch.empty_like(q)
+        info = _StepInfo()
+        _check(load_library().tra_schedule_step(self._h, _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                                                _dev_ptr(out, "out"), _stream(q.device), ctypes.byref(info)),
+               "tra_schedule_step")
+        return out, {"step": info.step, "mode": STEP_MODES[info.mode], "drift": info.drift}
+
+    def plan(self):
+        """The schedule's current plan (a borrowed view), or None before the first re-plan."""
+        h = _P()
+        _check(load_library().tra_schedule_plan(self._h, ctypes.byref(h)), "tra_schedule_plan")
+        return None if not h.value else _BorrowedPlan(h, self.shape, self.grid, self.params, self.device)
+
+    def destroy(self):
+        if getattr(self, "_h", None) is not None:
+            load_library().tra_schedule_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass

@@ -549,6 +549,168 @@ void tra_plan_destroy(tra_plan* plan) {
   release(plan);
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Reuse schedule across denoising steps.  Step policy (host side):
+//   step < warmup-1                       dense attention
+//   step == warmup-1, or a refresh is due dense attention + exact entropies,
+//                                         plan (re)built from them
+//   otherwise                             sparse attention under the plan
+// A refresh is due after refresh_every sparse steps, or on the step after a
+// sparse step whose tracked drift exceeded drift_threshold.  Drift tracking
+// compares the pooled-key levels of the current (q, k) with those of the
+// inputs the plan was built from (one pooling + entropy pass per step).
+// ---------------------------------------------------------------------------
+struct tra_schedule {
+  tra_shape shape;
+  tra_params params;
+  tra_schedule_params sp;
+  tra_plan* plan = nullptr;
+  float* Hd = nullptr;        // dense entropies of the last re-plan step
+  void* kbar = nullptr;       // pooled keys (drift tracking)
+  float* Hp = nullptr;        // pooled entropies (drift tracking)
+  int16_t* lv_ref = nullptr;  // pooled levels at the last re-plan
+  int16_t* lv_now = nullptr;
+  unsigned long long* cnt = nullptr;
+  unsigned long long* cnt_host = nullptr;  // pinned
+  int64_t n_queries = 0;
+  int32_t step = 0, since_plan = 0;
+  bool refresh_due = false;
+};
+
+namespace {
+
+void release_schedule(tra_schedule* s) {
+  if (!s) return;
+  if (s->plan) release(s->plan);
+  for (void* b : {static_cast<void*>(s->Hd), s->kbar, static_cast<void*>(s->Hp), static_cast<void*>(s->lv_ref),
+                  static_cast<void*>(s->lv_now), static_cast<void*>(s->cnt)})
+    if (b) (void)hipFree(b);
+  if (s->cnt_host) (void)hipHostFree(s->cnt_host);
+  delete s;
+}
+
+bool tracks_drift(const tra_schedule* s) {
+  return s->sp.drift_threshold >= 0.0 && s->params.radius_override < 0.0;
+}
+
+// Pooled-key levels of (q, k) into lv (the plan's pooling geometry and table).
+hipError_t pooled_levels(tra_schedule* s, const void* q, const void* k, int16_t* lv, hipStream_t hs) {
+  const tra_plan* p = s->plan;
+  hipError_t e = tra::launch_pool(s->shape.dtype, s->shape.head_dim, k, s->kbar, p->BH, p->pool, hs);
+  if (e != hipSuccess) return e;
+  const tra::EntropyArgs ea{p->params.a, p->params.c, p->params.levels_per_nat, p->table.k_lo, p->table.k_hi};
+  return tra::launch_entropy(s->shape.dtype, s->shape.head_dim, q, s->kbar, p->pool_w, p->BH,
+                             static_cast<int>(p->N), p->pool.count, ea, s->Hp, lv, hs);
+}
+
+}  // namespace
+
+extern "C" {
+
+tra_status tra_schedule_create(const tra_shape* shape, const tra_params* params, const tra_schedule_params* sp,
+                               tra_schedule** out) {
+  if (!out) return fail(TRA_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (!sp) return fail(TRA_ERR_INVALID_ARG, "schedule params are NULL");
+  tra_status st = check_shape(shape);
+  if (st != TRA_OK) return st;
+  st = check_params(shape, params, nullptr);
+  if (st != TRA_OK) return st;
+  if (sp->warmup_steps < 1) return fail(TRA_ERR_INVALID_ARG, "warmup_steps must be >= 1");
+  if (sp->refresh_every < 0) return fail(TRA_ERR_INVALID_ARG, "refresh_every must be >= 0");
+  if (!std::isfinite(sp->drift_threshold)) return fail(TRA_ERR_INVALID_ARG, "drift_threshold must be finite");
+  tra_schedule* s = new tra_schedule();
+  s->shape = *shape;
+  s->params = *params;
+  s->sp = *sp;
+  s->n_queries = static_cast<int64_t>(shape->B) * shape->heads * shape->T * shape->H * shape->W;
+  auto fin = [&](hipError_t e) {
+    release_schedule(s);
+    return fail(e == hipErrorOutOfMemory ? TRA_ERR_OOM : TRA_ERR_HIP, std::string("tra_schedule_create: ") +
+                                                                         hipGetErrorString(e));
+  };
+  hipError_t e = hipMalloc(&s->Hd, s->n_queries * sizeof(float));
+  if (e != hipSuccess) return fin(e);
+  if (tracks_drift(s)) {
+    const tra::Grid pool = tra::make_grid(shape->T, shape->H, shape->W, params->pool_h, params->pool_w);
+    const size_t kb = static_cast<size_t>(shape->B) * shape->heads * pool.count * shape->head_dim *
+                      dtype_size(shape->dtype);
+    if ((e = hipMalloc(&s->kbar, kb)) != hipSuccess) return fin(e);
+    if ((e = hipMalloc(&s->Hp, s->n_queries * sizeof(float))) != hipSuccess) return fin(e);
+    if ((e = hipMalloc(&s->lv_ref, s->n_queries * sizeof(int16_t))) != hipSuccess) return fin(e);
+    if ((e = hipMalloc(&s->lv_now, s->n_queries * sizeof(int16_t))) != hipSuccess) return fin(e);
+    if ((e = hipMalloc(&s->cnt, sizeof(unsigned long long))) != hipSuccess) return fin(e);
+    if ((e = hipHostMalloc(&s->cnt_host, sizeof(unsigned long long))) != hipSuccess) return fin(e);
+  }
+  *out = s;
+  return TRA_OK;
+}
+
+tra_status tra_schedule_step(tra_schedule* s, const void* q, const void* k, const void* v, void* o, void* stream,
+                             tra_step_info* info) {
+  if (!s) return fail(TRA_ERR_INVALID_ARG, "schedule is NULL");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const tra_shape& sh = s->shape;
+  int32_t mode;
+  if (s->step < s->sp.warmup_steps - 1) {
+    mode = TRA_STEP_DENSE;
+  } else if (s->step == s->sp.warmup_steps - 1 || s->refresh_due ||
+             (s->sp.refresh_every > 0 && s->since_plan >= s->sp.refresh_every)) {
+    mode = TRA_STEP_DENSE_REPLAN;
+  } else {
+    mode = TRA_STEP_SPARSE;
+  }
+  int64_t drift = -1;
+  if (mode == TRA_STEP_DENSE) {
+    tra_status st = tra_dense_attention(&sh, q, k, v, o, nullptr, stream);
+    if (st != TRA_OK) return st;
+  } else if (mode == TRA_STEP_DENSE_REPLAN) {
+    tra_status st = tra_dense_attention(&sh, q, k, v, o, s->Hd, stream);
+    if (st != TRA_OK) return st;
+    st = s->plan ? tra_plan_rebuild_from_entropy(s->plan, s->Hd, stream)
+                 : tra_plan_create_from_entropy(&sh, &s->params, s->Hd, stream, &s->plan);
+    if (st != TRA_OK) return st;
+    if (tracks_drift(s)) TRA_HIP(pooled_levels(s, q, k, s->lv_ref, hs));
+    s->since_plan = 0;
+    s->refresh_due = false;
+  } else {
+    tra_status st = tra_attention(s->plan, q, k, v, o, stream);
+    if (st != TRA_OK) return st;
+    ++s->since_plan;
+    if (tracks_drift(s)) {
+      TRA_HIP(pooled_levels(s, q, k, s->lv_now, hs));
+      TRA_HIP(hipMemsetAsync(s->cnt, 0, sizeof(unsigned long long), hs));
+      TRA_HIP(tra::launch_level_diff(s->lv_ref, s->lv_now, s->n_queries, s->cnt, hs));
+      TRA_HIP(hipMemcpyAsync(s->cnt_host, s->cnt, sizeof(unsigned long long), hipMemcpyDeviceToHost, hs));
+      TRA_HIP(hipStreamSynchronize(hs));
+      drift = static_cast<int64_t>(*s->cnt_host);
+      if (static_cast<double>(drift) > s->sp.drift_threshold * static_cast<double>(s->n_queries))
+        s->refresh_due = true;
+    }
+  }
+  if (info) {
+    info->step = s->step;
+    info->mode = mode;
+    info->drift = drift;
+  }
+  ++s->step;
+  return TRA_OK;
+}
+
+tra_status tra_schedule_plan(const tra_schedule* s, const tra_plan** plan) {
+  if (!s || !plan) return fail(TRA_ERR_INVALID_ARG, "schedule and plan must not be NULL");
+  *plan = s->plan;
+  return TRA_OK;
+}
+
+void tra_schedule_destroy(tra_schedule* s) {
+  if (!s) return;
+  (void)hipDeviceSynchronize();
+  release_schedule(s);
+}
+
 const char* tra_status_string(tra_status s) {
   switch (s) {
     case TRA_OK: return "TRA_OK";

@@ -159,3 +159,20 @@ def test_binding_dense_checks_shapes_on_host():
         tra.dense_attention(q, q[..., :32].contiguous(), q, grid=(2, 8, 8))
     with pytest.raises(ValueError):
         tra.plan_from_entropy(torch.zeros((1, 1, 5)), grid=(2, 8, 8), head_dim=64)
+
+
+def test_schedule_rejects_bad_arguments_before_any_device_call():
+    lib = tra.load_library()
+    out = ctypes.c_void_p()
+    prm = tra._make_params({})
+    name = lambda st: lib.tra_status_string(st).decode()
+    for sp, code in [(tra._SchedParams(0, 0, -1.0), "TRA_ERR_INVALID_ARG"),
+                     (tra._SchedParams(1, -1, -1.0), "TRA_ERR_INVALID_ARG"),
+                     (tra._SchedParams(1, 0, float("nan")), "TRA_ERR_INVALID_ARG")]:
+        assert name(lib.tra_schedule_create(ctypes.byref(_shape()), ctypes.byref(prm), ctypes.byref(sp),
+                                            ctypes.byref(out))) == code
+        assert out.value is None
+    assert name(lib.tra_schedule_create(ctypes.byref(_shape(head_dim=80)), ctypes.byref(prm),
+                                        ctypes.byref(tra._SchedParams(1, 0, -1.0)), ctypes.byref(out))) \
+        == "TRA_ERR_DTYPE"
+    assert name(lib.tra_schedule_step(None, None, None, None, None, None, None)) == "TRA_ERR_INVALID_ARG"
