@@ -156,10 +156,12 @@ struct tra_plan {
   int DM = 0;                    // largest active frame distance of the radius table
   int32_t* runs = nullptr;       // per query tile: key-tile column runs per (frame, tile row)
   int32_t* rowwin = nullptr;     // per query tile: first frame | frames << 16
-  int32_t* pair_list = nullptr;  // bf16 only: merged lists of query-tile pairs, 2 int32 per entry
-  int64_t pair_cap = 0;          // entries
-  int32_t* pair_len = nullptr;
-  int64_t* totals = nullptr;      // device: nnz, longest row, overflow flag
+  int32_t* glist = nullptr;  // bf16 only: merged tile lists of query-tile groups, 2 int32 per entry
+  int64_t glist_cap = 0;     // entries
+  int32_t* glen = nullptr;   // per group: list length
+  int32_t* gptr = nullptr;   // per group: list offset (exclusive scan of glen)
+  int64_t n_groups = 0;
+  int64_t* totals = nullptr;      // device: nnz, longest row, overflow flag (+4: the same for groups)
   int64_t* totals_host = nullptr; // pinned
   int64_t nnz = 0;
   int32_t max_row_len = 0;
@@ -170,7 +172,7 @@ namespace {
 void release(tra_plan* p) {
   if (!p) return;
   void* bufs[] = {p->kbar, p->H, p->lv, p->r2, p->dmax, p->r2c, p->r2off, p->pool_w,
-                  p->counts, p->row_ptr, p->col_idx, p->runs, p->rowwin, p->pair_list, p->pair_len, p->totals};
+                  p->counts, p->row_ptr, p->col_idx, p->runs, p->rowwin, p->glist, p->glen, p->gptr, p->totals};
   for (void* b : bufs)
     if (b) (void)hipFree(b);
   if (p->totals_host) (void)hipHostFree(p->totals_host);
@@ -213,15 +215,18 @@ tra_status build(tra_plan* p, const void* q, const void* k, const float* Hin, hi
   }
   TRA_HIP(tra::launch_csr_expand(p->BH, p->tiles, p->DM, p->runs, p->rowwin, p->row_ptr, p->col_idx, st));
   if (s.dtype == TRA_BF16) {
-    if (p->nnz > p->pair_cap) {
-      if (p->pair_list) TRA_HIP(hipFree(p->pair_list));
-      p->pair_list = nullptr;
-      p->pair_cap = 0;
-      TRA_HIP(hipMalloc(&p->pair_list, p->col_cap * 2 * sizeof(int32_t)));
-      p->pair_cap = p->col_cap;
+    if (p->nnz > p->glist_cap) {
+      if (p->glist) TRA_HIP(hipFree(p->glist));
+      p->glist = nullptr;
+      p->glist_cap = 0;
+      TRA_HIP(hipMalloc(&p->glist, p->col_cap * 2 * sizeof(int32_t)));
+      p->glist_cap = p->col_cap;
     }
-    TRA_HIP(tra::launch_pair_lists(p->BH, p->tiles, p->DM, p->runs, p->rowwin, p->row_ptr, p->pair_list,
-                                   p->pair_len, st));
+    TRA_HIP(tra::launch_group_lists(false, p->BH, p->tiles, p->DM, p->runs, p->rowwin, nullptr, nullptr,
+                                    p->glen, st));
+    TRA_HIP(tra::launch_scan(p->glen, p->n_groups, p->gptr, p->totals + 4, st));
+    TRA_HIP(tra::launch_group_lists(true, p->BH, p->tiles, p->DM, p->runs, p->rowwin, p->gptr, p->glist,
+                                    p->glen, st));
   }
   return TRA_OK;
 }
@@ -294,7 +299,7 @@ tra_status create_plan(const tra_shape* shape, const tra_params* params, Table&&
   TRA_HIP_P(hipMalloc(&p->pool_w, static_cast<size_t>(p->pool.count) * sizeof(float)));
   TRA_HIP_P(hipMalloc(&p->counts, p->n_rows * sizeof(int32_t)));
   TRA_HIP_P(hipMalloc(&p->row_ptr, (p->n_rows + 1) * sizeof(int32_t)));
-  TRA_HIP_P(hipMalloc(&p->totals, 4 * sizeof(int64_t)));
+  TRA_HIP_P(hipMalloc(&p->totals, 8 * sizeof(int64_t)));
   for (int32_t dm : p->table.dmax) p->DM = std::max(p->DM, static_cast<int>(dm));
   {
     const int64_t run_entries = p->n_rows * (2 * p->DM + 1) * p->tiles.nh;
@@ -303,8 +308,9 @@ tra_status create_plan(const tra_shape* shape, const tra_params* params, Table&&
     TRA_HIP_P(hipMalloc(&p->rowwin, p->n_rows * sizeof(int32_t)));
   }
   if (shape->dtype == TRA_BF16) {
-    const int64_t n_pairs = static_cast<int64_t>(p->BH) * p->tiles.T * p->tiles.nh * ((p->tiles.nw + 1) / 2);
-    TRA_HIP_P(hipMalloc(&p->pair_len, n_pairs * sizeof(int32_t)));
+    p->n_groups = tra::group_count(p->BH, p->tiles);
+    TRA_HIP_P(hipMalloc(&p->glen, p->n_groups * sizeof(int32_t)));
+    TRA_HIP_P(hipMalloc(&p->gptr, (p->n_groups + 1) * sizeof(int32_t)));
   }
   TRA_HIP_P(hipHostMalloc(&p->totals_host, 4 * sizeof(int64_t)));
 
@@ -432,7 +438,7 @@ tra_status tra_attention(const tra_plan* plan, const void* q, const void* k, con
                              static_cast<int>(plan->table.r2c.size()), s.T};
   TRA_HIP(tra::launch_attention(s.dtype, s.head_dim, q, k, v, o, plan->lv, tab, plan->row_base,
                                 plan->BH, plan->tiles, plan->row_ptr, plan->col_idx,
-                                plan->pair_list, plan->pair_len, static_cast<hipStream_t>(stream)));
+                                plan->gptr, plan->glist, plan->glen, static_cast<hipStream_t>(stream)));
   return TRA_OK;
 }
 

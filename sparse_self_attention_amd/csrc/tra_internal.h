@@ -66,15 +66,26 @@ hipError_t launch_csr_expand(int BH, const Grid& tiles, int DM, const int32_t* r
 hipError_t launch_attention(int dtype, int d, const void* q, const void* k, const void* v,
                             void* o, const int16_t* lv, const RadiusTable& tab, int row_base,
                             int BH, const Grid& tiles, const int32_t* row_ptr,
-                            const int32_t* col_idx, const int32_t* pair_list,
-                            const int32_t* pair_len, hipStream_t s);
-// Merged tile lists of horizontally adjacent query-tile pairs (the bf16
-// attention kernel's unit of work), from the runs: entries of two int32 each,
-// pair p's list at pair_list + 2 * row_ptr[first row of p], length
-// pair_len[p].  The buffer needs 2 * nnz int32.
-hipError_t launch_pair_lists(int BH, const Grid& tiles, int DM, const int32_t* runs,
-                             const int32_t* rowwin, const int32_t* row_ptr, int32_t* pair_list,
-                             int32_t* pair_len, hipStream_t s);
+                            const int32_t* col_idx, const int32_t* gptr, const int32_t* glist,
+                            const int32_t* glen, hipStream_t s);
+// Work unit of the bf16 attention kernel: a group of GROUP_ROWS x 2 query
+// tiles of one frame, run by one workgroup of ATTN_THREADS threads (two waves
+// per query tile).
+#ifndef TRA_GROUP_ROWS
+#define TRA_GROUP_ROWS 2
+#endif
+constexpr int GROUP_ROWS = TRA_GROUP_ROWS;
+constexpr int ATTN_THREADS = 256 * GROUP_ROWS;
+inline int64_t group_count(int BH, const Grid& tiles) {
+  return static_cast<int64_t>(BH) * tiles.T * ((tiles.nh + GROUP_ROWS - 1) / GROUP_ROWS) * ((tiles.nw + 1) / 2);
+}
+// Merged tile lists of the groups, from the runs: with fill = false the length
+// of each group's list to glen; with fill = true the entries (two int32 each)
+// at glist + 2 * gptr[group] (gptr: exclusive scan of the lengths).  The sum
+// of the lengths is at most nnz.
+hipError_t launch_group_lists(bool fill, int BH, const Grid& tiles, int DM, const int32_t* runs,
+                              const int32_t* rowwin, const int32_t* gptr, int32_t* glist, int32_t* glen,
+                              hipStream_t s);
 // Dynamic LDS the bf16 attention kernel needs for its staged K/V buffers
 // plus a compact radius table of n_r2c entries; 0 if it exceeds the device limit.
 size_t attention_lds_bytes(int d, int n_r2c);

@@ -15,7 +15,7 @@
 //   csr_runs_kernel       per query tile: union over its 64 queries of the disk
 //                         footprints, as key-tile runs per frame and tile row
 //   csr_expand_kernel     runs -> CSR column indices
-//   pair_kernel           runs of two adjacent query tiles -> their merged list
+//   group_list_kernel     runs of a group of adjacent query tiles -> their merged list
 //   scan_kernel           exclusive scan of the per-tile counts
 //   attn_bf16_kernel      block-sparse flash attention: S^T = K Q^T and
 //                         O^T += V^T P^T on 32x32x16 bf16 MFMA, K/V tiles staged
@@ -415,73 +415,76 @@ __global__ __launch_bounds__(256) void csr_expand_kernel(Grid g, int DM, int64_t
   }
 }
 
-// Union of the tile lists of two horizontally adjacent query tiles, the unit
-// of work of the bf16 attention kernel, from the runs of their two rows: per
-// (frame, tile row) the union of two runs is again a run (each contains its
-// own tile's column, and the two columns are adjacent).  Entries in ascending
-// order as (frame | ragged << 31, row0 | col0 << 16), where ragged marks a
-// tile cut by the bottom or right edge of the grid.  Pair p's list goes where
-// its first tile's CSR row starts (the two rows are adjacent and the union is
-// no longer than both), its length to pair_len[p].  One wave per pair.
-__global__ __launch_bounds__(256) void pair_kernel(Grid g, int DM, int ngw, int64_t n_pairs,
-                                                  const int32_t* __restrict__ runs,
-                                                  const int32_t* __restrict__ rowwin,
-                                                  const int32_t* __restrict__ row_ptr,
-                                                  int2* __restrict__ out_list,
-                                                  int32_t* __restrict__ out_len) {
+// Union of the tile lists of a group of GROUP_ROWS x 2 query tiles of one
+// frame (the unit of work of the bf16 attention kernel), from the runs of
+// their rows: per (frame, tile row) the union of the runs is again a run
+// (each nonempty run contains its own query tile's column, and the group's
+// columns are adjacent).  Entries in ascending order as
+// (frame | ragged << 31, row0 | col0 << 16), where ragged marks a tile cut by
+// the bottom or right edge of the grid.  FILL = false: the union's length to
+// glen[gid]; FILL = true: the entries from glist + gptr[gid].  One wave per group.
+template <bool FILL>
+__global__ __launch_bounds__(256) void group_list_kernel(Grid g, int DM, int ngh, int ngw, int64_t n_groups,
+                                                        const int32_t* __restrict__ runs,
+                                                        const int32_t* __restrict__ rowwin,
+                                                        const int32_t* __restrict__ gptr,
+                                                        int2* __restrict__ glist, int32_t* __restrict__ glen) {
   const int lane = threadIdx.x & 63;
-  const int64_t pid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (pid >= n_pairs) return;  // wave-uniform
-  const int64_t per_head = static_cast<int64_t>(g.T) * g.nh * ngw;
-  const int64_t bh = pid / per_head;
-  const int prem = static_cast<int>(pid % per_head);
-  const int gc = prem % ngw, fr = prem / ngw;  // fr = frame * nh + tile row
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (gid >= n_groups) return;  // wave-uniform
+  const int64_t per_head = static_cast<int64_t>(g.T) * ngh * ngw;
+  const int64_t bh = gid / per_head;
+  const int grem = static_cast<int>(gid % per_head);
+  const int gc = grem % ngw, gr = (grem / ngw) % ngh, tq = grem / (ngw * ngh);
   const int64_t RS = static_cast<int64_t>((2 * DM + 1) * g.nh);
-  const int64_t rowa = bh * g.count + static_cast<int64_t>(fr) * g.nw + 2 * gc;
-  const bool has_b = 2 * gc + 1 < g.nw;
-  const int wa = rowwin[rowa], wb = has_b ? rowwin[rowa + 1] : 0;
-  const int loa = wa & 0xffff, nfa = wa >> 16, lob = wb & 0xffff, nfb = wb >> 16;
+  constexpr int NR = 2 * GROUP_ROWS;
+  int64_t rows[NR];
+  int wlo[NR], wn[NR];
   int t_lo = 0x7fffffff, t_hi = -1;
-  if (nfa > 0) {
-    t_lo = loa;
-    t_hi = loa + nfa - 1;
-  }
-  if (nfb > 0) {
-    t_lo = min(t_lo, lob);
-    t_hi = max(t_hi, lob + nfb - 1);
+#pragma unroll
+  for (int m = 0; m < NR; ++m) {
+    const int tr = gr * GROUP_ROWS + (m >> 1), tc = 2 * gc + (m & 1);
+    rows[m] = bh * g.count + (static_cast<int64_t>(tq) * g.nh + tr) * g.nw + tc;
+    const int w = (tr < g.nh && tc < g.nw) ? rowwin[rows[m]] : 0;
+    wlo[m] = w & 0xffff;
+    wn[m] = w >> 16;
+    if (wn[m] > 0) {
+      t_lo = min(t_lo, wlo[m]);
+      t_hi = max(t_hi, wlo[m] + wn[m] - 1);
+    }
   }
   const int nruns = t_hi >= t_lo ? (t_hi - t_lo + 1) * g.nh : 0;
-  const int64_t beg = row_ptr[rowa];
-  int64_t out = beg;
+  int64_t out = FILL ? gptr[gid] : 0;
+  const int64_t beg = out;
   for (int j0 = 0; j0 < nruns; j0 += 64) {
     const int j = j0 + lane;
     const int tk = t_lo + j / g.nh, ktr = j % g.nh;
     int LO = 0xffff, HI = 0;
     if (j < nruns) {
-      if (tk >= loa && tk < loa + nfa) {
-        const int r = runs[rowa * RS + (tk - loa) * g.nh + ktr];
-        LO = min(LO, r & 0xffff);
-        HI = max(HI, r >> 16);
-      }
-      if (tk >= lob && tk < lob + nfb) {
-        const int r = runs[(rowa + 1) * RS + (tk - lob) * g.nh + ktr];
-        LO = min(LO, r & 0xffff);
-        HI = max(HI, r >> 16);
+#pragma unroll
+      for (int m = 0; m < NR; ++m) {
+        if (tk >= wlo[m] && tk < wlo[m] + wn[m]) {
+          const int r = runs[rows[m] * RS + (tk - wlo[m]) * g.nh + ktr];
+          LO = min(LO, r & 0xffff);
+          HI = max(HI, r >> 16);
+        }
       }
     }
     const int len = HI >= LO ? HI - LO + 1 : 0;
     int total;
     const int excl = wave_excl_scan(len, lane, &total);
-    const int kr0 = ktr * g.th;
-    const bool row_cut = kr0 + g.th > g.H;
-    for (int c = 0; c < len; ++c) {
-      const int kc0 = (LO + c) * g.tw;
-      const bool ragged = row_cut || kc0 + g.tw > g.W;
-      out_list[out + excl + c] = make_int2(tk | (ragged ? static_cast<int>(0x80000000u) : 0), kr0 | (kc0 << 16));
+    if (FILL) {
+      const int kr0 = ktr * g.th;
+      const bool row_cut = kr0 + g.th > g.H;
+      for (int c = 0; c < len; ++c) {
+        const int kc0 = (LO + c) * g.tw;
+        const bool ragged = row_cut || kc0 + g.tw > g.W;
+        glist[out + excl + c] = make_int2(tk | (ragged ? static_cast<int>(0x80000000u) : 0), kr0 | (kc0 << 16));
+      }
     }
     out += total;
   }
-  if (lane == 0) out_len[pid] = static_cast<int32_t>(out - beg);
+  if (lane == 0) glen[gid] = static_cast<int32_t>(out - beg);
 }
 
 // Exclusive scan of per-row counts.  One workgroup of 1024 threads walks the
@@ -552,15 +555,16 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
 // ---------------------------------------------------------------------------
 // Block-sparse attention, bf16, 8x8 tiles.
 //
-// Work decomposition.  A workgroup of 4 waves owns two horizontally adjacent
-// query tiles of one frame and walks the ascending union of their tile lists,
-// prepared by the plan (pair_kernel).  Each key tile is streamed once per
-// workgroup into one of two LDS buffers by range-checked buffer DMA
-// (buffer_load_dwordx4 ... lds), so the next tile streams in while the
-// current one is consumed, and all 4 waves use it.  A wave owns 32 queries
-// (lane % 32 = query) and skips a 32-key half of a tile whenever none of its
-// queries retains a key there: tiles that only the neighbouring query tile
-// needs cost loads but no matrix work.
+// Work decomposition.  A workgroup of 4 * GROUP_ROWS waves owns a group of
+// GROUP_ROWS x 2 query tiles of one frame (2 x 2 by default) and walks the
+// ascending union of their tile lists, prepared by the plan
+// (group_list_kernel).  Each key tile is streamed once per workgroup into one
+// of two LDS buffers by range-checked buffer DMA (buffer_load_dwordx4 ... lds),
+// so the next tile streams in while the current one is consumed, and all
+// waves use it: a 2 x 2 group loads each key tile once for 256 queries.  A
+// wave owns 32 queries (lane % 32 = query) and skips a 32-key half of a tile
+// whenever none of its queries retains a key there: tiles that only the other
+// query tiles of the group need cost loads but no matrix work.
 //
 //   S^T (keys x queries) = K Q^T :  A = K rows from LDS, B = Q^T in registers
 //   O^T (d x queries)   += V^T P^T : A = V^T via ds_read_b64_tr_b16, B = P^T
@@ -584,14 +588,15 @@ template <int D> struct AttnLds {
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
+__global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, const int16_t* __restrict__ lv,
     const int32_t* __restrict__ r2c, const int32_t* __restrict__ r2off,
-    const int32_t* __restrict__ dmax, int n_r2c, int row_base, Grid g, int ngw, int n_groups,
-    const int32_t* __restrict__ row_ptr, const int2* __restrict__ pair_list,
-    const int32_t* __restrict__ pair_len) {
+    const int32_t* __restrict__ dmax, int n_r2c, int row_base, Grid g, int ngh, int ngw, int n_groups,
+    const int32_t* __restrict__ gptr, const int2* __restrict__ glist,
+    const int32_t* __restrict__ glen) {
   using L = AttnLds<D>;
+  constexpr int NWAVES = ATTN_THREADS / 64;
   constexpr int KS = D / 16;  // k-steps of S^T
   constexpr int DB = D / 32;  // 32-row blocks of O^T
   constexpr int NONE = 0x7fffffff;
@@ -608,11 +613,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   const int per_xcd = gridDim.x / 8;
   const int gid = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   if (gid >= n_groups) return;  // uniform over the workgroup, before any barrier
-  for (int i = threadIdx.x; i < n_r2c; i += 256) r2s[i] = r2c[i];
+  for (int i = threadIdx.x; i < n_r2c; i += ATTN_THREADS) r2s[i] = r2c[i];
   __syncthreads();
 
-  // Group = two horizontally adjacent query tiles of one frame.
-  const int groups_per_frame = g.nh * ngw;
+  // Group = GROUP_ROWS x 2 query tiles of one frame.
+  const int groups_per_frame = ngh * ngw;
   const int per_head = g.T * groups_per_frame;
   const int bh = gid / per_head;
   const int grem = gid % per_head;
@@ -620,11 +625,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   const int gr = (grem % groups_per_frame) / ngw, gc = grem % ngw;
   const size_t N = static_cast<size_t>(g.T) * g.H * g.W;
 
-  // This wave: tile column gc*2 + wave/2, tile rows 4*(wave%2)..+3; lane%32 -> query.
-  const int tc = gc * 2 + (wave >> 1);
-  const bool tvalid = tc < g.nw;
+  // This wave: tile column gc*2 + (wave/2)%2, tile row gr*GROUP_ROWS + wave/4,
+  // query rows 4*(wave%2)..+3 of that tile; lane%32 -> query.
+  const int tc = gc * 2 + ((wave >> 1) & 1);
+  const int trq = gr * GROUP_ROWS + (wave >> 2);
+  const bool tvalid = tc < g.nw && trq < g.nh;
   const int wq = tc * 8 + (col & 7);
-  const int hq = gr * 8 + 4 * (wave & 1) + (col >> 3);
+  const int hq = trq * 8 + 4 * (wave & 1) + (col >> 3);
   const bool qvalid = tvalid && hq < g.H && wq < g.W;
   const size_t nq = (static_cast<size_t>(tq) * g.H + (qvalid ? hq : 0)) * g.W + (qvalid ? wq : 0);
   bf16x8 qf[KS];
@@ -644,8 +651,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   // current one is entered, long before its first use.  (Vector loads keep the
   // list out of the LDS wait counter: a scalar load in flight would hold up
   // every LDS wait.)
-  const int n_tiles = pair_len[gid];
-  const int2* lst = pair_list + row_ptr[static_cast<int64_t>(bh) * g.count + (tq * g.nh + gr) * g.nw + gc * 2];
+  const int n_tiles = glen[gid];
+  const int2* lst = glist + gptr[gid];
   int2 cur = lane < n_tiles ? lst[lane] : make_int2(0, 0);
   int2 nxt = 64 + lane < n_tiles ? lst[64 + lane] : make_int2(0, 0);
   struct TileGeo {
@@ -678,12 +685,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   // loop's memory counters follow a fixed pattern.  A lane's byte offset from
   // the tile's first key is fixed per segment; it is computed once here, and a
   // load adds it to the tile's offset.
-  constexpr int NK = (L::KSEG + 3) / 4, NV = (L::VSEG + 3) / 4;
+  constexpr int NK = (L::KSEG + NWAVES - 1) / NWAVES, NV = (L::VSEG + NWAVES - 1) / NWAVES;
   struct SegLane {
     int kr, kc, c;  // key row / column within the tile, 16-byte chunk
   };
   auto seg_lane = [&](int stride, int nseg, int i) {
-    const int seg = min(wave + 4 * i, nseg - 1);
+    const int seg = min(wave + NWAVES * i, nseg - 1);
     const int ob = seg * 1024 + lane * 16;
     const int kk = ob / stride;
     const int c = (ob % stride) / 16;
@@ -703,15 +710,19 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   auto lds_seg = [&](char* dst, int nseg, int i) {
     return __builtin_amdgcn_readfirstlane(
         static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(dst))) +
-        min(wave + 4 * i, nseg - 1) * 1024);
+        min(wave + NWAVES * i, nseg - 1) * 1024);
   };
   auto issue = [&](const TileGeo& t, char* buf) {
     char* vbuf = buf + L::KSEG * 1024;
     const uint32_t tile_bytes = static_cast<uint32_t>((t.tk * g.H + t.kr0) * g.W + t.kc0) * (D * 2u);
 #pragma unroll
-    for (int i = 0; i < NK; ++i) lds_dma16_buf(krsrc, tile_bytes + koff[i], lds_seg(buf, L::KSEG, i));
+    for (int i = 0; i < NK; ++i)
+      if (NWAVES * (L::KSEG / NWAVES) == L::KSEG || wave + NWAVES * i < L::KSEG)
+        lds_dma16_buf(krsrc, tile_bytes + koff[i], lds_seg(buf, L::KSEG, i));
 #pragma unroll
-    for (int i = 0; i < NV; ++i) lds_dma16_buf(vrsrc, tile_bytes + voff[i], lds_seg(vbuf, L::VSEG, i));
+    for (int i = 0; i < NV; ++i)
+      if (NWAVES * (L::VSEG / NWAVES) == L::VSEG || wave + NWAVES * i < L::VSEG)
+        lds_dma16_buf(vrsrc, tile_bytes + voff[i], lds_seg(vbuf, L::VSEG, i));
   };
 
   f32x16 oacc[DB];
@@ -1148,21 +1159,26 @@ size_t attention_lds_bytes(int d, int n_r2c) {
   return kv + static_cast<size_t>(n_r2c) * sizeof(int32_t);
 }
 
-hipError_t launch_pair_lists(int BH, const Grid& tiles, int DM, const int32_t* runs,
-                             const int32_t* rowwin, const int32_t* row_ptr, int32_t* pair_list,
-                             int32_t* pair_len, hipStream_t s) {
-  const int ngw = (tiles.nw + 1) / 2;
-  const int64_t n_pairs = static_cast<int64_t>(BH) * tiles.T * tiles.nh * ngw;
-  pair_kernel<<<static_cast<unsigned>((n_pairs + 3) / 4), 256, 0, s>>>(
-      tiles, DM, ngw, n_pairs, runs, rowwin, row_ptr, reinterpret_cast<int2*>(pair_list), pair_len);
+hipError_t launch_group_lists(bool fill, int BH, const Grid& tiles, int DM, const int32_t* runs,
+                              const int32_t* rowwin, const int32_t* gptr, int32_t* glist, int32_t* glen,
+                              hipStream_t s) {
+  const int ngh = (tiles.nh + GROUP_ROWS - 1) / GROUP_ROWS, ngw = (tiles.nw + 1) / 2;
+  const int64_t n_groups = static_cast<int64_t>(BH) * tiles.T * ngh * ngw;
+  const unsigned grid = static_cast<unsigned>((n_groups + 3) / 4);
+  if (fill)
+    group_list_kernel<true><<<grid, 256, 0, s>>>(tiles, DM, ngh, ngw, n_groups, runs, rowwin, gptr,
+                                                 reinterpret_cast<int2*>(glist), glen);
+  else
+    group_list_kernel<false><<<grid, 256, 0, s>>>(tiles, DM, ngh, ngw, n_groups, runs, rowwin, gptr,
+                                                  reinterpret_cast<int2*>(glist), glen);
   return hipGetLastError();
 }
 
 hipError_t launch_attention(int dtype, int d, const void* q, const void* k, const void* v,
                             void* o, const int16_t* lv, const RadiusTable& tab, int row_base,
                             int BH, const Grid& tiles, const int32_t* row_ptr,
-                            const int32_t* col_idx, const int32_t* pair_list,
-                            const int32_t* pair_len, hipStream_t s) {
+                            const int32_t* col_idx, const int32_t* gptr, const int32_t* glist,
+                            const int32_t* glen, hipStream_t s) {
   const int32_t* r2 = tab.r2;
   const unsigned rows = static_cast<unsigned>(BH) * tiles.count;
   if (dtype == 1) {
@@ -1170,15 +1186,15 @@ hipError_t launch_attention(int dtype, int d, const void* q, const void* k, cons
     const auto* kk = static_cast<const uint16_t*>(k);
     const auto* vv = static_cast<const uint16_t*>(v);
     auto* oo = static_cast<uint16_t*>(o);
-    const int ngw = (tiles.nw + 1) / 2;
-    const int64_t groups = static_cast<int64_t>(BH) * tiles.T * tiles.nh * ngw;
+    const int ngh = (tiles.nh + GROUP_ROWS - 1) / GROUP_ROWS, ngw = (tiles.nw + 1) / 2;
+    const int64_t groups = static_cast<int64_t>(BH) * tiles.T * ngh * ngw;
     const unsigned grid = static_cast<unsigned>((groups + 7) / 8 * 8);
     const int ng = static_cast<int>(groups);
     const size_t lds_tab = static_cast<size_t>(tab.n_r2c) * sizeof(int32_t);
-#define TRA_ATTN(DD)                                                                          \
-  attn_bf16_kernel<DD><<<grid, 256, lds_tab, s>>>(qq, kk, vv, oo, lv, tab.r2c, tab.r2off, tab.dmax, \
-                                                  tab.n_r2c, row_base, tiles, ngw, ng, row_ptr,      \
-                                                  reinterpret_cast<const int2*>(pair_list), pair_len)
+#define TRA_ATTN(DD)                                                                                \
+  attn_bf16_kernel<DD><<<grid, ATTN_THREADS, lds_tab, s>>>(qq, kk, vv, oo, lv, tab.r2c, tab.r2off, tab.dmax, \
+                                                           tab.n_r2c, row_base, tiles, ngh, ngw, ng, gptr,     \
+                                                           reinterpret_cast<const int2*>(glist), glen)
     if (d == 128) TRA_ATTN(128);
     else TRA_ATTN(64);
 #undef TRA_ATTN
