@@ -43,6 +43,7 @@ __all__ = [
     "frame_sum", "radius_table", "table_margin", "retained_keys", "retained_count",
     "retained_counts", "dense_mask", "query_tile_row", "csr", "attention_rows",
     "dense_attention", "dense_entropy", "excused_queries", "round_to_dtype", "plan", "ENTROPY_EXCUSE",
+    "GEN_ENTROPY_DISK", "GEN_MANHATTAN", "GEN_RADIAL", "radial_band",
 ]
 
 ENTROPY_EXCUSE = 1e-5  # queries this close (nats) to a level boundary may differ
@@ -239,6 +240,24 @@ def frame_sum(decay, T):
     return sum(decay ** (2 * abs(dl)) for dl in range(-(T - 1), T))
 
 
+GEN_ENTROPY_DISK, GEN_MANHATTAN, GEN_RADIAL = 0, 1, 2
+
+
+def _generator(p):
+    return p.get("generator", GEN_ENTROPY_DISK)
+
+
+def _l1(p):
+    """True when the mask measures distance with the L1 norm (Manhattan)."""
+    return _generator(p) == GEN_MANHATTAN
+
+
+def radial_band(delta):
+    """Octave band of a frame distance: 0 for delta = 0, then 1, 2, 2, 3, 3, 3,
+    3, 4, ... (band b >= 1 holds the 2^(b-1) distances 2^(b-1) .. 2^b - 1)."""
+    return 0 if delta == 0 else delta.bit_length()
+
+
 def _r0_squared(p, T):
     if p["radius_override"] >= 0:
         return [p["radius_override"] ** 2]
@@ -250,7 +269,26 @@ def _r0_squared(p, T):
 def radius_table(p, T):
     """int64 [n_levels, T]: R2[k - k_lo][delta], -1 where frame delta is inactive.
 
-    Row 0 is the only row when a fixed radius override is set (level -1)."""
+    Row 0 is the only row when a fixed radius override is set (level -1).
+    Alternative generators (static, radius r = radius_override):
+      Manhattan  the L1 ball |dt| + |dh| + |dw| <= r of the fixed-radius post
+                 (section 5.2): frame delta holds the 2D L1 disk of radius
+                 floor(r) - delta, inactive below 0 (the entry is an L1 radius);
+      Radial     the static mask whose spatial window shrinks with temporal
+                 distance: in octave band b (radial_band) the disk area halves
+                 per band, R2 = floor(r^2 / 2^b), active while R2 >= 1."""
+    if _generator(p) == GEN_MANHATTAN:
+        assert p["radius_override"] >= 0, "the Manhattan generator needs a fixed radius"
+        R = math.floor(p["radius_override"])
+        return np.array([[R - dl if R - dl >= 0 else -1 for dl in range(T)]], dtype=np.int64)
+    if _generator(p) == GEN_RADIAL:
+        assert p["radius_override"] >= 0, "the Radial generator needs a fixed radius"
+        r0sq = p["radius_override"] ** 2
+        row = []
+        for delta in range(T):
+            v = math.floor(r0sq / 2 ** radial_band(delta))
+            row.append(v if (delta == 0 or v >= 1) else -1)
+        return np.array([row], dtype=np.int64)
     rows = []
     for r0sq in _r0_squared(p, T):
         row = []
@@ -281,6 +319,19 @@ def _row(level, R2, p):
     return R2[0] if p["radius_override"] >= 0 else R2[level - level_range(p)[0]]
 
 
+def _reach(lim, p):
+    """Largest |h_i - h_j| with a retained key in a frame whose entry is lim >= 0."""
+    return lim if _l1(p) else math.isqrt(lim)
+
+
+def _half_width(lim, dh, p):
+    """Half-width of the retained columns at row offset dh (-1: none)."""
+    if _l1(p):
+        return lim - abs(dh) if lim - abs(dh) >= 0 else -1
+    rem = lim - dh * dh
+    return math.isqrt(rem) if rem >= 0 else -1
+
+
 def retained_keys(i, level, R2, T, H, W, p):
     """Sorted key indices retained by query i (disk enumeration per frame)."""
     t, h, w = i // (H * W), (i // W) % H, i % W
@@ -291,10 +342,9 @@ def retained_keys(i, level, R2, T, H, W, p):
         if lim < 0:
             continue
         for hk in range(H):
-            rem = lim - (hk - h) ** 2
-            if rem < 0:
+            a = _half_width(lim, hk - h, p)
+            if a < 0:
                 continue
-            a = math.isqrt(rem)
             for wk in range(max(0, w - a), min(W - 1, w + a) + 1):
                 out.append((tk * H + hk) * W + wk)
     return np.array(out, dtype=np.int64)
@@ -308,8 +358,9 @@ def retained_count(i, level, R2, T, H, W, p):
         lim = r2row[abs(tk - t)]
         if lim < 0:
             continue
-        for hk in range(max(0, h - math.isqrt(lim)), min(H - 1, h + math.isqrt(lim)) + 1):
-            a = math.isqrt(lim - (hk - h) ** 2)
+        reach = _reach(lim, p)
+        for hk in range(max(0, h - reach), min(H - 1, h + reach) + 1):
+            a = _half_width(lim, hk - h, p)
             n += min(W - 1, w + a) - max(0, w - a) + 1
     return n
 
@@ -325,11 +376,15 @@ def retained_counts(lv, R2, T, H, W, p):
     for tk in range(T):
         lim = rows[np.arange(N), np.abs(tk - t)]
         for hk in range(H):
-            rem = lim - (hk - h) ** 2
-            ok = rem >= 0
-            a = np.floor(np.sqrt(np.maximum(rem, 0))).astype(np.int64)
-            a -= (a * a > rem)  # exact integer square root
-            a += ((a + 1) * (a + 1) <= rem)
+            if _l1(p):
+                a = lim - np.abs(hk - h)
+                ok = a >= 0
+            else:
+                rem = lim - (hk - h) ** 2
+                ok = rem >= 0
+                a = np.floor(np.sqrt(np.maximum(rem, 0))).astype(np.int64)
+                a -= (a * a > rem)  # exact integer square root
+                a += ((a + 1) * (a + 1) <= rem)
             cnt = np.minimum(W - 1, w + a) - np.maximum(0, w - a) + 1
             total += np.where(ok, cnt, 0)
     return total
@@ -343,8 +398,11 @@ def dense_mask(lv, R2, T, H, W, p):
     rows = R2[np.zeros(N, dtype=np.int64)] if p["radius_override"] >= 0 else R2[lv - level_range(p)[0]]
     dt = np.abs(t[:, None] - t[None, :])
     lim = np.take_along_axis(rows, dt, axis=1)
-    d2 = (h[:, None] - h[None, :]) ** 2 + (w[:, None] - w[None, :]) ** 2
-    return (lim >= 0) & (d2 <= lim)
+    if _l1(p):
+        d = np.abs(h[:, None] - h[None, :]) + np.abs(w[:, None] - w[None, :])
+    else:
+        d = (h[:, None] - h[None, :]) ** 2 + (w[:, None] - w[None, :]) ** 2
+    return (lim >= 0) & (d <= lim)
 
 
 # ----------------------------------------------------------------------------
@@ -361,8 +419,9 @@ def query_tile_row(a, lv, R2, tiles: Geometry, p):
             lim = r2row[abs(tk - t)]
             if lim < 0:
                 continue
-            for hk in range(max(0, h - math.isqrt(lim)), min(H - 1, h + math.isqrt(lim)) + 1):
-                half = math.isqrt(lim - (hk - h) ** 2)
+            reach = _reach(lim, p)
+            for hk in range(max(0, h - reach), min(H - 1, h + reach) + 1):
+                half = _half_width(lim, hk - h, p)
                 c0 = max(0, w - half) // tiles.bw
                 c1 = min(W - 1, w + half) // tiles.bw
                 base = (tk * tiles.nbh + hk // tiles.bh) * tiles.nbw

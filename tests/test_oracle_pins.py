@@ -353,6 +353,74 @@ def test_csr_coverage_and_minimality(seed):
 
 
 # ---------------------------------------------------------------------------
+# Alternative generators: fixed Manhattan radius, Radial static mask
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("R", range(5))
+def test_manhattan_counts_are_octahedral_numbers(R):
+    """Interior query: the 3D L1 ball of radius R holds the centred octahedral
+    number (2R+1)(2R^2+2R+3)/3 of lattice points; frame delta holds the
+    centred square number 2m^2+2m+1, m = R - delta."""
+    p = _p(radius_override=R + 0.5, generator=O.GEN_MANHATTAN)
+    T, H, W = 2 * R + 3, 2 * R + 5, 2 * R + 7
+    R2 = O.radius_table(p, T)
+    i = ((T // 2) * H + H // 2) * W + W // 2
+    expected = (2 * R + 1) * (2 * R * R + 2 * R + 3) // 3
+    assert O.retained_count(i, -1, R2, T, H, W, p) == expected
+    keys = O.retained_keys(i, -1, R2, T, H, W, p)
+    assert len(keys) == expected
+    t = keys // (H * W)
+    for delta in range(R + 1):
+        m = R - delta
+        assert np.sum(t == T // 2 + delta) == 2 * m * m + 2 * m + 1
+    assert np.sum(np.abs(t - T // 2) > R) == 0
+
+
+def test_radial_table_bands():
+    """Octave bands 0 | 1 | 2-3 | 4-7 | 8-15 | 16-31 and a disk area halving per band."""
+    p = _p(radius_override=8.0, generator=O.GEN_RADIAL)
+    R2 = O.radius_table(p, 20)
+    assert list(R2[0]) == [64, 32, 16, 16] + [8] * 4 + [4] * 8 + [2] * 4
+    assert [O.radial_band(d) for d in range(9)] == [0, 1, 2, 2, 3, 3, 3, 3, 4]
+    # Each band b >= 1 spends the same total area r0^2/2 (2^(b-1) frames of r0^2/2^b):
+    # the O(n log n) budget of a static mask that shrinks with temporal distance.
+    q = _p(radius_override=16.0, generator=O.GEN_RADIAL)
+    row = O.radius_table(q, 128)[0]
+    for b in range(1, 8):
+        assert sum(row[2 ** (b - 1):2 ** b]) == 128
+    tiny = O.radius_table(_p(radius_override=2.0, generator=O.GEN_RADIAL), 6)[0]
+    assert list(tiny) == [4, 2, 1, 1, -1, -1]  # 4/8 < 1: inactive from band 3 on
+
+
+@pytest.mark.parametrize("gen,seed", [(g, s) for g in (1, 2) for s in range(2)])
+def test_generator_masks_enumeration_and_csr(gen, seed):
+    rng = np.random.default_rng(300 + seed)
+    T, H, W = int(rng.integers(1, 5)), int(rng.integers(3, 14)), int(rng.integers(3, 14))
+    p = _p(radius_override=float(rng.uniform(0.0, 6.0)), generator=gen, tile_h=int(rng.choice([2, 3, 8])),
+           tile_w=int(rng.choice([2, 5, 8])))
+    R2 = O.radius_table(p, T)
+    lv = np.full(T * H * W, -1)
+    mask = O.dense_mask(lv, R2, T, H, W, p)
+    n = np.arange(T * H * W)
+    t, h, w = n // (H * W), (n // W) % H, n % W
+    if gen == O.GEN_MANHATTAN:  # the ball itself, straight from the coordinates
+        ref = (np.abs(t[:, None] - t[None, :]) + np.abs(h[:, None] - h[None, :]) + np.abs(w[:, None] - w[None, :])
+               <= math.floor(p["radius_override"]))
+        assert np.array_equal(mask, ref)
+    for i in range(T * H * W):
+        assert np.array_equal(O.retained_keys(i, -1, R2, T, H, W, p), np.nonzero(mask[i])[0])
+        assert O.retained_count(i, -1, R2, T, H, W, p) == mask[i].sum()
+    assert np.array_equal(O.retained_counts(lv, R2, T, H, W, p), mask.sum(axis=1))
+    tiles = O.Geometry(T, H, W, p["tile_h"], p["tile_w"])
+    blk = tiles.block_of_tokens()
+    hit = np.zeros((tiles.count, tiles.count), dtype=bool)
+    qi, kj = np.nonzero(mask)
+    hit[blk[qi], blk[kj]] = True
+    row_ptr, col_idx = O.csr(lv, R2, tiles, p)
+    for a in range(tiles.count):
+        assert np.array_equal(col_idx[row_ptr[a]:row_ptr[a + 1]], np.nonzero(hit[a])[0])
+
+
+# ---------------------------------------------------------------------------
 # Attention
 # ---------------------------------------------------------------------------
 def _sdpa(q, k, v, mask=None):

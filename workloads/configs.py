@@ -42,6 +42,7 @@ class Workload:
     tile_h: int = 8
     tile_w: int = 8
     radius_override: float = -1.0
+    generator: int = 0  # 0: entropy -> disk (the method); 1: fixed Manhattan radius; 2: Radial static mask
     seed: int = 0
     batch: int = 1
     reuse_calls: int = 1  # attention calls that reuse one plan
@@ -57,7 +58,7 @@ class Workload:
     def params(self) -> dict:
         """Method parameters (what the planning call receives)."""
         keys = ("a", "c", "budget_min", "budget_max", "decay", "levels_per_nat",
-                "pool_h", "pool_w", "tile_h", "tile_w", "radius_override")
+                "pool_h", "pool_w", "tile_h", "tile_w", "radius_override", "generator")
         d = asdict(self)
         return {k: d[k] for k in keys}
 
