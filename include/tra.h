@@ -11,6 +11,13 @@
  * block-sparse attention kernel consumes.  The pages fix the shape of each step
  * but no constants; the constants arrive here through tra_params.
  *
+ * Sources cited below:
+ *   [TRA] "Token Radius Attention for Efficient Video Generation" (summary page)
+ *   [P1]  "Token Radius Attention视频生成里被忽略但值得关注的高效注意力思路"
+ *         (post on fixed-radius token masks)
+ *   [RA]  "AI视频生成革命！MIT领衔豪华天团让生成效率暴涨370%，成本直降4.4倍"
+ *         (news page on Radial attention's static mask)
+ *
  * Two calls form the path:
  *   tra_plan_create  entropy -> budget level -> radius table -> CSR tile lists
  *   tra_attention    block-sparse softmax attention with the exact per-token mask
@@ -83,7 +90,29 @@ typedef struct {
 typedef struct {
   double a, c, budget_min, budget_max, decay, radius_override;
   int32_t levels_per_nat, pool_h, pool_w, tile_h, tile_w;
+  int32_t generator; /* tra_generator */
 } tra_params;
+
+/*
+ * Plan generators: which keys a query retains.  All feed the same tile lists
+ * and attention kernels.
+ *   TRA_GEN_ENTROPY_DISK  the method: per-query budget from the entropy ->
+ *                         Euclidean disk per frame with radius r0*phi^delta
+ *                         (or the fixed r0 = radius_override when >= 0).
+ *   TRA_GEN_MANHATTAN     fixed-radius baseline of the generic radius post
+ *                         ([P1] section 5.2): keep j iff |t_i-t_j| + |h_i-h_j|
+ *                         + |w_i-w_j| <= floor(radius_override); the radius
+ *                         table then holds L1 radii floor(R) - delta.
+ *   TRA_GEN_RADIAL        Radial attention's static mask ([RA], a spatial
+ *                         window that shrinks with temporal distance), read as
+ *                         a disk whose area halves per octave band of delta:
+ *                         R2[delta] = floor(radius_override^2 / 2^b), b = 0 for
+ *                         delta = 0 and floor(log2 delta) + 1 otherwise; frames
+ *                         with R2 < 1 are inactive.
+ * The two static generators need radius_override >= 0 and ignore the entropy
+ * (every level is -1).
+ */
+typedef enum { TRA_GEN_ENTROPY_DISK = 0, TRA_GEN_MANHATTAN = 1, TRA_GEN_RADIAL = 2 } tra_generator;
 
 typedef struct tra_plan tra_plan; /* opaque; owns its device buffers */
 

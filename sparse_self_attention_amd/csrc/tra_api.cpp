@@ -75,6 +75,10 @@ tra_status check_params(const tra_shape* s, const tra_params* p, Table* tab) {
     return fail(TRA_ERR_SHAPE, "bf16 attention needs T*H*W*head_dim*2 (bytes of one head) below 2^31");
   if (!std::isfinite(p->radius_override) || p->radius_override >= 32768.0)
     return fail(TRA_ERR_INVALID_ARG, "radius_override must be finite and below 32768");
+  if (p->generator < TRA_GEN_ENTROPY_DISK || p->generator > TRA_GEN_RADIAL)
+    return fail(TRA_ERR_INVALID_ARG, "unknown generator");
+  if (p->generator != TRA_GEN_ENTROPY_DISK && !(p->radius_override >= 0.0))
+    return fail(TRA_ERR_INVALID_ARG, "the Manhattan and Radial generators take their radius from radius_override (>= 0)");
   const int T = s->T;
   const double phi = p->decay;
   Table t;
@@ -108,9 +112,24 @@ tra_status check_params(const tra_shape* s, const tra_params* p, Table* tab) {
   for (int r = 0; r < t.n_levels; ++r) {
     int dm = 0;
     for (int dl = 0; dl < T; ++dl) {
-      const double x = t.r0sq[r] * std::pow(phi, 2.0 * dl);
-      int32_t v = static_cast<int32_t>(std::floor(x));
-      if (dl > 0 && v < 1) v = -1;
+      int32_t v;
+      if (p->generator == TRA_GEN_MANHATTAN) {
+        // L1 ball |dt| + |dh| + |dw| <= R: frame dl holds the 2D L1 disk of radius R - dl.
+        v = static_cast<int32_t>(std::floor(p->radius_override)) - dl;
+        if (v < 0) v = -1;
+      } else {
+        double x;
+        if (p->generator == TRA_GEN_RADIAL) {
+          // Octave band b of dl (0 | 1 | 2-3 | 4-7 | ...): the disk area halves per band.
+          int band = 0;
+          for (int u = dl; u > 0; u >>= 1) ++band;
+          x = std::ldexp(t.r0sq[r], -band);
+        } else {
+          x = t.r0sq[r] * std::pow(phi, 2.0 * dl);
+        }
+        v = static_cast<int32_t>(std::floor(x));
+        if (dl > 0 && v < 1) v = -1;
+      }
       if (v >= 0) dm = dl;
       t.r2[static_cast<size_t>(r) * T + dl] = v;
     }
@@ -197,7 +216,7 @@ tra_status build(tra_plan* p, const void* q, const void* k, const float* Hin, hi
   } else {
     TRA_HIP(tra::launch_fill_levels(p->lv, p->H, p->n_queries, st));
   }
-  TRA_HIP(tra::launch_csr_runs(p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, p->DM, p->counts,
+  TRA_HIP(tra::launch_csr_runs(p->params.generator == TRA_GEN_MANHATTAN, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, p->DM, p->counts,
                                p->runs, p->rowwin, st));
   TRA_HIP(tra::launch_scan(p->counts, p->n_rows, p->row_ptr, p->totals, st));
   TRA_HIP(hipMemcpyAsync(p->totals_host, p->totals, 3 * sizeof(int64_t), hipMemcpyDeviceToHost, st));
@@ -435,7 +454,8 @@ tra_status tra_attention(const tra_plan* plan, const void* q, const void* k, con
   if (o == q || o == k || o == v) return fail(TRA_ERR_INVALID_ARG, "o must not alias q, k or v");
   const tra_shape& s = plan->shape;
   const tra::RadiusTable tab{plan->r2, plan->dmax, plan->r2c, plan->r2off,
-                             static_cast<int>(plan->table.r2c.size()), s.T};
+                             static_cast<int>(plan->table.r2c.size()), s.T,
+                             plan->params.generator == TRA_GEN_MANHATTAN};
   TRA_HIP(tra::launch_attention(s.dtype, s.head_dim, q, k, v, o, plan->lv, tab, plan->row_base,
                                 plan->BH, plan->tiles, plan->row_ptr, plan->col_idx,
                                 plan->gptr, plan->glist, plan->glen, static_cast<hipStream_t>(stream)));
@@ -499,7 +519,7 @@ tra_status tra_plan_stats(const tra_plan* plan, int64_t* retained, int64_t* list
   unsigned long long host[2] = {0, 0};
   hipError_t e = hipMemsetAsync(dev, 0, 2 * sizeof(unsigned long long), hs);
   if (e == hipSuccess)
-    e = tra::launch_stats(plan->lv, plan->r2, plan->shape.T, plan->row_base, plan->BH, plan->tiles,
+    e = tra::launch_stats(plan->params.generator == TRA_GEN_MANHATTAN, plan->lv, plan->r2, plan->shape.T, plan->row_base, plan->BH, plan->tiles,
                           plan->row_ptr, plan->col_idx, dev, hs);
   if (e == hipSuccess) e = hipMemcpyAsync(host, dev, sizeof(host), hipMemcpyDeviceToHost, hs);
   if (e == hipSuccess) e = hipStreamSynchronize(hs);

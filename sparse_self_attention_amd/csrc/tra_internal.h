@@ -37,6 +37,7 @@ struct RadiusTable {
   const int32_t* r2off;
   int n_r2c;
   int T;
+  bool l1;  // entries are L1 radii (Manhattan mask) instead of squared radii
 };
 
 struct EntropyArgs {
@@ -55,7 +56,7 @@ hipError_t launch_fill_levels(int16_t* lv, float* H, int64_t n, hipStream_t s);
 // row) plus the count and the frame window (csr_runs), the scan of the counts,
 // and the expansion of the runs into col_idx.  DM is the largest active frame
 // distance of the radius table; runs holds n_rows * (2*DM + 1) * nh int32.
-hipError_t launch_csr_runs(const int16_t* lv, const int32_t* r2, const int32_t* dmax, int T,
+hipError_t launch_csr_runs(bool l1, const int16_t* lv, const int32_t* r2, const int32_t* dmax, int T,
                            int row_base, int BH, const Grid& tiles, int DM, int32_t* counts,
                            int32_t* runs, int32_t* rowwin, hipStream_t s);
 hipError_t launch_scan(const int32_t* counts, int64_t n_rows, int32_t* row_ptr,
@@ -103,7 +104,7 @@ hipError_t launch_dense(int dtype, int d, const void* q, const void* k, const vo
 hipError_t launch_levels_from_entropy(const float* Hin, int64_t n, const EntropyArgs& ea, float* Hout,
                                       int16_t* lv, hipStream_t s);
 
-hipError_t launch_stats(const int16_t* lv, const int32_t* r2, int T, int row_base, int BH,
+hipError_t launch_stats(bool l1, const int16_t* lv, const int32_t* r2, int T, int row_base, int BH,
                         const Grid& tiles, const int32_t* row_ptr, const int32_t* col_idx,
                         unsigned long long* out2, hipStream_t s);
 

@@ -325,6 +325,27 @@ __global__ void fill_levels_kernel(int16_t* lv, float* H, int64_t n) {
 // ---------------------------------------------------------------------------
 constexpr int32_t RUN_EMPTY = 0xffff;  // LO = 0xffff, HI = 0
 
+// Distance metric of the mask.  Euclidean (L1 = false): a table entry is a
+// squared radius and key (dh, dw) is kept iff dh^2 + dw^2 <= entry.
+// Manhattan (L1 = true): the entry is an L1 radius and the test is
+// |dh| + |dw| <= entry.
+// Largest |dh| with a kept key, for an entry thr >= 0.
+template <bool L1>
+__device__ __forceinline__ int mask_reach(int thr) {
+  return L1 ? thr : isqrt_i(thr);
+}
+// Half-width of the kept columns at row offset dh (-1: none), thr >= 0.
+template <bool L1>
+__device__ __forceinline__ int mask_half_width(int thr, int dh) {
+  if (L1) {
+    const int a = thr - abs(dh);
+    return a >= 0 ? a : -1;
+  }
+  const int rem = thr - dh * dh;
+  return rem >= 0 ? isqrt_i(rem) : -1;
+}
+
+template <bool L1>
 __global__ __launch_bounds__(256) void csr_runs_kernel(const int16_t* __restrict__ lv,
                                                       const int32_t* __restrict__ r2,
                                                       const int32_t* __restrict__ dmax, int T,
@@ -354,7 +375,7 @@ __global__ __launch_bounds__(256) void csr_runs_kernel(const int16_t* __restrict
   for (int tk = t_lo; tk <= t_hi; ++tk) {
     const int delta = tk > tq ? tk - tq : tq - tk;
     const int thr = (valid && delta <= dm) ? r2[trow * T + delta] : -1;
-    const int rad = thr >= 0 ? isqrt_i(thr) : -1;
+    const int rad = thr >= 0 ? mask_reach<L1>(thr) : -1;
     const int top = thr >= 0 ? max(0, hq - rad) : 0x7fffffff;
     const int bot = thr >= 0 ? min(g.H - 1, hq + rad) : -1;
     const int TOP = wave_min_u(top), BOT = wave_max_u(bot);
@@ -366,10 +387,9 @@ __global__ __launch_bounds__(256) void csr_runs_kernel(const int16_t* __restrict
       for (int tr = max(trc, tr_first); tr <= tr_end; ++tr) {
         const int r0 = tr * g.th, r1 = min(g.H, r0 + g.th) - 1;
         const int dh = max(0, max(r0 - hq, hq - r1));
-        const int remv = thr - dh * dh;
+        const int a = thr >= 0 ? mask_half_width<L1>(thr, dh) : -1;
         int lo = 0x7fffffff, hi = -1;
-        if (thr >= 0 && remv >= 0) {
-          const int a = isqrt_i(remv);
+        if (a >= 0) {
           lo = max(0, wq - a) >> tw_shift;
           hi = min(g.W - 1, wq + a) >> tw_shift;
         }
@@ -587,7 +607,7 @@ template <int D> struct AttnLds {
   static_assert(64 * KSTR % 1024 == 0 && 64 * VSTR % 1024 == 0, "tile must be whole segments");
 };
 
-template <int D>
+template <int D, bool L1>
 __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, const int16_t* __restrict__ lv,
@@ -848,12 +868,19 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
     const int dwa = wq - t.kc0 - 4 * h;
     const int dha = hq - t.kr0;
     int dw2[4], rr[8];
-    dw2[0] = __mul24(dwa, dwa);
+    if constexpr (L1) {
 #pragma unroll
-    for (int b = 1; b < 4; ++b) dw2[b] = dw2[b - 1] - 2 * dwa + (2 * b - 1);
-    rr[0] = thr1 - __mul24(dha, dha);
+      for (int b = 0; b < 4; ++b) dw2[b] = abs(dwa - b);
 #pragma unroll
-    for (int a = 1; a < 8; ++a) rr[a] = rr[a - 1] + 2 * dha - (2 * a - 1);
+      for (int a = 0; a < 8; ++a) rr[a] = thr1 - abs(dha - a);
+    } else {
+      dw2[0] = __mul24(dwa, dwa);
+#pragma unroll
+      for (int b = 1; b < 4; ++b) dw2[b] = dw2[b - 1] - 2 * dwa + (2 * b - 1);
+      rr[0] = thr1 - __mul24(dha, dha);
+#pragma unroll
+      for (int a = 1; a < 8; ++a) rr[a] = rr[a - 1] + 2 * dha - (2 * a - 1);
+    }
     if (t.ragged) {  // tile at the bottom/right edge of the grid (wave-uniform)
 #pragma unroll
       for (int b = 0; b < 4; ++b)
@@ -949,7 +976,7 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
 }
 
 // fp32 inputs: one thread per query, K/V tiles in LDS, fp32 online softmax.
-template <int D>
+template <int D, bool L1>
 __global__ __launch_bounds__(64) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, const int16_t* __restrict__ lv, const int32_t* __restrict__ r2,
@@ -998,7 +1025,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
     for (int kk = 0; kk < 64; ++kk) {
       const int kr = kr0 + (kk >> 3), kc = kc0 + (kk & 7);
       const int dh = hq - kr, dw = wq - kc;
-      if (kr >= g.H || kc >= g.W || thr < 0 || dh * dh + dw * dw > thr) continue;
+      if (kr >= g.H || kc >= g.W || thr < 0 || (L1 ? abs(dh) + abs(dw) : dh * dh + dw * dw) > thr) continue;
       float s = 0.f;
 #pragma unroll
       for (int dd = 0; dd < D; ++dd) s = fmaf(qr[dd], k_lds[kk][dd], s);
@@ -1027,6 +1054,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
 // ---------------------------------------------------------------------------
 // Exact pair counts.
 // ---------------------------------------------------------------------------
+template <bool L1>
 __global__ __launch_bounds__(256) void retained_kernel(const int16_t* __restrict__ lv,
                                                       const int32_t* __restrict__ r2, int T,
                                                       int row_base, Grid g, int64_t n_total,
@@ -1043,9 +1071,9 @@ __global__ __launch_bounds__(256) void retained_kernel(const int16_t* __restrict
     for (int tk = 0; tk < T; ++tk) {
       const int thr = row[tk > t ? tk - t : t - tk];
       if (thr < 0) continue;
-      const int rad = isqrt_i(thr);
+      const int rad = mask_reach<L1>(thr);
       for (int hk = max(0, hh - rad); hk <= min(g.H - 1, hh + rad); ++hk) {
-        const int a = isqrt_i(thr - (hk - hh) * (hk - hh));
+        const int a = mask_half_width<L1>(thr, hk - hh);
         cnt += min(g.W - 1, ww + a) - max(0, ww - a) + 1;
       }
     }
@@ -1130,12 +1158,16 @@ static int log2i(int x) {
   return s;
 }
 
-hipError_t launch_csr_runs(const int16_t* lv, const int32_t* r2, const int32_t* dmax, int T,
+hipError_t launch_csr_runs(bool l1, const int16_t* lv, const int32_t* r2, const int32_t* dmax, int T,
                            int row_base, int BH, const Grid& tiles, int DM, int32_t* counts,
                            int32_t* runs, int32_t* rowwin, hipStream_t s) {
   const dim3 grid((tiles.count + 3) / 4, BH), block(256);
-  csr_runs_kernel<<<grid, block, 0, s>>>(lv, r2, dmax, T, row_base, tiles, log2i(tiles.tw), DM,
-                                         counts, runs, rowwin);
+  if (l1)
+    csr_runs_kernel<true><<<grid, block, 0, s>>>(lv, r2, dmax, T, row_base, tiles, log2i(tiles.tw), DM,
+                                                 counts, runs, rowwin);
+  else
+    csr_runs_kernel<false><<<grid, block, 0, s>>>(lv, r2, dmax, T, row_base, tiles, log2i(tiles.tw), DM,
+                                                  counts, runs, rowwin);
   return hipGetLastError();
 }
 
@@ -1191,22 +1223,33 @@ hipError_t launch_attention(int dtype, int d, const void* q, const void* k, cons
     const unsigned grid = static_cast<unsigned>((groups + 7) / 8 * 8);
     const int ng = static_cast<int>(groups);
     const size_t lds_tab = static_cast<size_t>(tab.n_r2c) * sizeof(int32_t);
-#define TRA_ATTN(DD)                                                                                \
-  attn_bf16_kernel<DD><<<grid, ATTN_THREADS, lds_tab, s>>>(qq, kk, vv, oo, lv, tab.r2c, tab.r2off, tab.dmax, \
-                                                           tab.n_r2c, row_base, tiles, ngh, ngw, ng, gptr,     \
-                                                           reinterpret_cast<const int2*>(glist), glen)
-    if (d == 128) TRA_ATTN(128);
-    else TRA_ATTN(64);
+#define TRA_ATTN(DD, M)                                                                                 \
+  attn_bf16_kernel<DD, M><<<grid, ATTN_THREADS, lds_tab, s>>>(qq, kk, vv, oo, lv, tab.r2c, tab.r2off, tab.dmax, \
+                                                              tab.n_r2c, row_base, tiles, ngh, ngw, ng, gptr,     \
+                                                              reinterpret_cast<const int2*>(glist), glen)
+    if (tab.l1) {
+      if (d == 128) TRA_ATTN(128, true);
+      else TRA_ATTN(64, true);
+    } else {
+      if (d == 128) TRA_ATTN(128, false);
+      else TRA_ATTN(64, false);
+    }
 #undef TRA_ATTN
   } else {
     const auto* qq = static_cast<const float*>(q);
     const auto* kk = static_cast<const float*>(k);
     const auto* vv = static_cast<const float*>(v);
     auto* oo = static_cast<float*>(o);
-    if (d == 128)
-      attn_f32_kernel<128><<<rows, 64, 0, s>>>(qq, kk, vv, oo, lv, r2, row_base, tiles.T, tiles, row_ptr, col_idx);
-    else
-      attn_f32_kernel<64><<<rows, 64, 0, s>>>(qq, kk, vv, oo, lv, r2, row_base, tiles.T, tiles, row_ptr, col_idx);
+#define TRA_ATTN32(DD, M) \
+  attn_f32_kernel<DD, M><<<rows, 64, 0, s>>>(qq, kk, vv, oo, lv, r2, row_base, tiles.T, tiles, row_ptr, col_idx)
+    if (tab.l1) {
+      if (d == 128) TRA_ATTN32(128, true);
+      else TRA_ATTN32(64, true);
+    } else {
+      if (d == 128) TRA_ATTN32(128, false);
+      else TRA_ATTN32(64, false);
+    }
+#undef TRA_ATTN32
   }
   return hipGetLastError();
 }
@@ -1230,11 +1273,15 @@ hipError_t launch_level_diff(const int16_t* a, const int16_t* b, int64_t n, unsi
   return hipGetLastError();
 }
 
-hipError_t launch_stats(const int16_t* lv, const int32_t* r2, int T, int row_base, int BH,
+hipError_t launch_stats(bool l1, const int16_t* lv, const int32_t* r2, int T, int row_base, int BH,
                         const Grid& tiles, const int32_t* row_ptr, const int32_t* col_idx,
                         unsigned long long* out2, hipStream_t s) {
   const int64_t nq = static_cast<int64_t>(BH) * tiles.T * tiles.H * tiles.W;
-  retained_kernel<<<static_cast<unsigned>((nq + 255) / 256), 256, 0, s>>>(lv, r2, T, row_base, tiles, nq, out2);
+  const unsigned nb = static_cast<unsigned>((nq + 255) / 256);
+  if (l1)
+    retained_kernel<true><<<nb, 256, 0, s>>>(lv, r2, T, row_base, tiles, nq, out2);
+  else
+    retained_kernel<false><<<nb, 256, 0, s>>>(lv, r2, T, row_base, tiles, nq, out2);
   const int64_t nr = static_cast<int64_t>(BH) * tiles.count;
   listed_kernel<<<static_cast<unsigned>((nr + 255) / 256), 256, 0, s>>>(tiles, nr, row_ptr, col_idx, out2 + 1);
   return hipGetLastError();

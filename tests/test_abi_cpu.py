@@ -69,6 +69,9 @@ def _validate(**kw):
     (dict(budget_max=1e12), "TRA_ERR_INVALID_ARG"),
     # one bf16 head of K would span 2^31 bytes or more (32-bit buffer offsets)
     (dict(grid=(2, 32767, 256), heads=1), "TRA_ERR_SHAPE"),
+    (dict(generator=3), "TRA_ERR_INVALID_ARG"),
+    (dict(generator=1), "TRA_ERR_INVALID_ARG"),  # the static generators need radius_override >= 0
+    (dict(generator=2, radius_override=-1.0), "TRA_ERR_INVALID_ARG"),
 ])
 def test_validation_rejects(kw, code):
     with pytest.raises(tra.TraError) as ei:
@@ -101,6 +104,15 @@ def test_radius_table_matches_oracle(name):
 @pytest.mark.parametrize("decay", [1.0, 0.5, 0.35])
 def test_radius_table_override_matches_oracle(r, decay):
     cfg = small_workload(T=9, radius_override=r, decay=decay)
+    r2, _, k_lo = tra.radius_table((cfg.T, cfg.H, cfg.W), torch.bfloat16, 128, **cfg.params())
+    assert k_lo == -1
+    assert np.array_equal(r2.astype(np.int64), O.radius_table(cfg.params(), cfg.T))
+
+
+@pytest.mark.parametrize("gen,r,T", [(1, 0.0, 5), (1, 7.9, 12), (1, 40.0, 66), (2, 0.0, 4), (2, 5.5, 21),
+                                     (2, 60.0, 66)])
+def test_radius_table_generators_match_oracle(gen, r, T):
+    cfg = small_workload(T=T, radius_override=r, generator=gen)
     r2, _, k_lo = tra.radius_table((cfg.T, cfg.H, cfg.W), torch.bfloat16, 128, **cfg.params())
     assert k_lo == -1
     assert np.array_equal(r2.astype(np.int64), O.radius_table(cfg.params(), cfg.T))

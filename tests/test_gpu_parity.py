@@ -208,3 +208,41 @@ def test_plan_drift(gpu):
     _say("drift", n, "oracle", ref, "excused", slack, "of", cfg.heads * cfg.N)
     assert n > 0
     assert abs(n - ref) <= slack
+
+
+# ---------------------------------------------------------------------------
+# Alternative plan generators on the same kernels
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("gen,r,dtype", [(1, 5.0, "bf16"), (1, 11.0, "bf16"), (2, 6.0, "bf16"), (2, 13.0, "bf16"),
+                                         (1, 4.0, "fp32"), (2, 5.0, "fp32")])
+def test_generator_small_full_parity(gpu, gen, r, dtype):
+    cfg = small_workload(T=4, H=13, W=21, heads=2, radius_override=r, generator=gen, dtype=dtype,
+                         head_dim=128 if dtype == "bf16" else 64)
+    _say("case: generator", gen, "radius", r, dtype)
+    run = gpu_run(cfg, gpu)
+    R2 = O.radius_table(cfg.params(), cfg.T)
+    for h in range(cfg.heads):
+        m = check_head(cfg, run, 0, h)
+        _say("head", h, "O", m["o_max_abs"], m["o_mean_abs"])
+    retained, listed = run["plan"].stats()
+    lv = np.full(cfg.N, -1)
+    assert retained == cfg.heads * int(O.retained_counts(lv, R2, cfg.T, cfg.H, cfg.W, cfg.params()).sum())
+
+
+@pytest.mark.parametrize("gen,r", [(1, 24.0), (2, 40.0)])
+def test_generator_full_size_sampled(gpu, gen, r):
+    base = CONFIGS["wan21_14b_720p"]
+    from dataclasses import replace
+    cfg = replace(base, radius_override=r, generator=gen)
+    _say("case: generator full size", gen, r)
+    run = gpu_run(cfg, gpu)
+    check_csr_properties(cfg, run)
+    rng = np.random.default_rng(41)
+    tiles = O.Geometry(cfg.T, cfg.H, cfg.W, 8, 8)
+    for h in (0, cfg.heads - 1):
+        ts = np.concatenate([rng.choice(tiles.count, size=10, replace=False), [0, tiles.count - 1]])
+        qs = np.concatenate([rng.choice(cfg.N, size=24, replace=False), [0, cfg.N - 1]])
+        m = check_head(cfg, run, 0, h, tile_sample=ts, query_sample=qs)
+        _say("head", h, "O", m["o_max_abs"], m["o_mean_abs"])
+    retained, listed = run["plan"].stats()
+    _say("density", retained / (cfg.heads * cfg.N ** 2), "tile efficiency", retained / listed)
