@@ -13,9 +13,9 @@
  *
  * Sources cited below:
  *   [TRA] "Token Radius Attention for Efficient Video Generation" (summary page)
- *   [P1]  "Token Radius Attention视频生成里被忽略但值得关注的高效注意力思路"
+ *   [BLOG] "Token Radius Attention视频生成里被忽略但值得关注的高效注意力思路"
  *         (post on fixed-radius token masks)
- *   [RA]  "AI视频生成革命！MIT领衔豪华天团让生成效率暴涨370%，成本直降4.4倍"
+ *   [RADIAL] "AI视频生成革命！MIT领衔豪华天团让生成效率暴涨370%，成本直降4.4倍"
  *         (news page on Radial attention's static mask)
  *
  * Two calls form the path:
@@ -100,10 +100,10 @@ typedef struct {
  *                         Euclidean disk per frame with radius r0*phi^delta
  *                         (or the fixed r0 = radius_override when >= 0).
  *   TRA_GEN_MANHATTAN     fixed-radius baseline of the generic radius post
- *                         ([P1] section 5.2): keep j iff |t_i-t_j| + |h_i-h_j|
+ *                         ([BLOG] section 5.2): keep j iff |t_i-t_j| + |h_i-h_j|
  *                         + |w_i-w_j| <= floor(radius_override); the radius
  *                         table then holds L1 radii floor(R) - delta.
- *   TRA_GEN_RADIAL        Radial attention's static mask ([RA], a spatial
+ *   TRA_GEN_RADIAL        Radial attention's static mask ([RADIAL], a spatial
  *                         window that shrinks with temporal distance), read as
  *                         a disk whose area halves per octave band of delta:
  *                         R2[delta] = floor(radius_override^2 / 2^b), b = 0 for
