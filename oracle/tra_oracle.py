@@ -43,7 +43,8 @@ __all__ = [
     "frame_sum", "radius_table", "table_margin", "retained_keys", "retained_count",
     "retained_counts", "dense_mask", "query_tile_row", "csr", "attention_rows",
     "dense_attention", "dense_entropy", "excused_queries", "round_to_dtype", "plan", "ENTROPY_EXCUSE",
-    "GEN_ENTROPY_DISK", "GEN_MANHATTAN", "GEN_RADIAL", "radial_band",
+    "GEN_ENTROPY_DISK", "GEN_MANHATTAN", "GEN_RADIAL", "radial_band", "tile_votes", "csr_vote",
+    "listed_keys", "attention_rows_listed",
 ]
 
 ENTROPY_EXCUSE = 1e-5  # queries this close (nats) to a level boundary may differ
@@ -435,6 +436,61 @@ def csr(lv, R2, tiles: Geometry, p):
     row_ptr = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int64)
     col_idx = np.concatenate(rows) if rows else np.zeros(0, dtype=np.int64)
     return row_ptr, col_idx
+
+
+# ----------------------------------------------------------------------------
+# Token voting with a threshold; block-only masks
+# ----------------------------------------------------------------------------
+def tile_votes(a, lv, R2, tiles: Geometry, p):
+    """{key tile id: number of retained pairs (i, j) with i in query tile a and j
+    in that key tile}: the votes of [TRA]'s token voting (section 2, "Exécution
+    Efficace"), which turns token masks into block masks."""
+    key_tile = tiles.block_of_tokens()
+    votes = {}
+    for i in tiles.tokens(a):
+        keys = retained_keys(int(i), int(lv[i]), R2, tiles.T, tiles.H, tiles.W, p)
+        for b, n in zip(*np.unique(key_tile[keys], return_counts=True)):
+            votes[int(b)] = votes.get(int(b), 0) + int(n)
+    return votes
+
+
+def csr_vote(lv, R2, tiles: Geometry, p, theta):
+    """(row_ptr, col_idx): key tile b is listed for query tile a iff it holds at
+    least `theta` votes (theta = 1 gives `csr`)."""
+    rows = []
+    for a in range(tiles.count):
+        votes = tile_votes(a, lv, R2, tiles, p)
+        rows.append(np.array(sorted(b for b, n in votes.items() if n >= theta), dtype=np.int64))
+    row_ptr = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int64)
+    col_idx = np.concatenate(rows) if rows else np.zeros(0, dtype=np.int64)
+    return row_ptr, col_idx
+
+
+def listed_keys(i, tiles: Geometry, row_ptr, col_idx):
+    """Sorted key indices of every tile listed for query i's tile."""
+    a = int(tiles.block_of_tokens()[i])
+    toks = [tiles.tokens(b) for b in col_idx[row_ptr[a]:row_ptr[a + 1]]]
+    return np.sort(np.concatenate(toks)) if toks else np.zeros(0, dtype=np.int64)
+
+
+def attention_rows_listed(q, k, v, rows, lv, R2, tiles: Geometry, p, row_ptr, col_idx, block_only):
+    """O_i over the keys of the tiles listed for i's tile: all of them (block-only
+    mask, the block-sparse execution of the pages) or only those i retains
+    (exact mask restricted to the listed tiles).  A query left with no key (its
+    tiles all fell below the vote threshold) gets O_i = 0."""
+    q = np.asarray(q, dtype=np.float64)
+    d = q.shape[1]
+    out = np.zeros((len(rows), v.shape[1]), dtype=np.float64)
+    for slot, i in enumerate(rows):
+        keys = listed_keys(int(i), tiles, row_ptr, col_idx)
+        if not block_only:
+            keys = np.intersect1d(keys, retained_keys(int(i), int(lv[i]), R2, tiles.T, tiles.H, tiles.W, p))
+        if len(keys) == 0:
+            continue
+        s = (np.asarray(k[keys], dtype=np.float64) @ q[i]) / math.sqrt(d)
+        e = np.exp(s - s.max())
+        out[slot] = (e / e.sum()) @ np.asarray(v[keys], dtype=np.float64)
+    return out
 
 
 # ----------------------------------------------------------------------------

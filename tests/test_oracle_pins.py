@@ -421,6 +421,64 @@ def test_generator_masks_enumeration_and_csr(gen, seed):
 
 
 # ---------------------------------------------------------------------------
+# Token voting with a threshold; block-only masks
+# ---------------------------------------------------------------------------
+def _vote_case(seed):
+    rng = np.random.default_rng(400 + seed)
+    T, H, W = int(rng.integers(1, 4)), int(rng.integers(3, 17)), int(rng.integers(3, 17))
+    p = _p(budget_min=2.0, budget_max=300.0, decay=float(rng.uniform(0.3, 1.0)),
+           tile_h=int(rng.choice([2, 3, 4])), tile_w=int(rng.choice([2, 5, 4])))
+    R2 = O.radius_table(p, T)
+    lv = _random_levels(rng, T * H * W, p)
+    return T, H, W, p, R2, lv, O.Geometry(T, H, W, p["tile_h"], p["tile_w"])
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_tile_votes_match_brute_force_mask(seed):
+    T, H, W, p, R2, lv, tiles = _vote_case(seed)
+    mask = O.dense_mask(lv, R2, T, H, W, p)
+    blk = tiles.block_of_tokens()
+    counts = np.zeros((tiles.count, tiles.count), dtype=np.int64)
+    qi, kj = np.nonzero(mask)
+    np.add.at(counts, (blk[qi], blk[kj]), 1)
+    for a in range(tiles.count):
+        votes = O.tile_votes(a, lv, R2, tiles, p)
+        assert votes == {int(b): int(counts[a, b]) for b in np.nonzero(counts[a])[0]}
+    rp1, ci1 = O.csr_vote(lv, R2, tiles, p, 1)
+    rp, ci = O.csr(lv, R2, tiles, p)
+    assert np.array_equal(rp1, rp) and np.array_equal(ci1, ci)
+    for theta in (2, 5, 17):
+        rpt, cit = O.csr_vote(lv, R2, tiles, p, theta)
+        for a in range(tiles.count):
+            assert np.array_equal(cit[rpt[a]:rpt[a + 1]], np.nonzero(counts[a] >= theta)[0])
+
+
+def test_listed_attention_matches_library_sdpa():
+    T, H, W, p, R2, lv, tiles = _vote_case(7)
+    rng = np.random.default_rng(17)
+    d = 16
+    N = T * H * W
+    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
+    mask = O.dense_mask(lv, R2, T, H, W, p)
+    blk = tiles.block_of_tokens()
+    rp, ci = O.csr_vote(lv, R2, tiles, p, 3)
+    listed = np.zeros((tiles.count, tiles.count), dtype=bool)
+    for a in range(tiles.count):
+        listed[a, ci[rp[a]:rp[a + 1]]] = True
+    block_mask = listed[blk[:, None], blk[None, :]]
+    rows = np.nonzero(block_mask.any(axis=1) & (mask & block_mask).any(axis=1))[0]
+    got_b = O.attention_rows_listed(q, k, v, rows, lv, R2, tiles, p, rp, ci, True)
+    assert np.max(np.abs(got_b - _sdpa(q, k, v, block_mask)[rows])) < 1e-12
+    got_x = O.attention_rows_listed(q, k, v, rows, lv, R2, tiles, p, rp, ci, False)
+    assert np.max(np.abs(got_x - _sdpa(q, k, v, mask & block_mask)[rows])) < 1e-12
+    # With threshold 1 the exact mask loses nothing to the tile lists.
+    rp1, ci1 = O.csr(lv, R2, tiles, p)
+    allr = np.arange(N)
+    assert np.max(np.abs(O.attention_rows_listed(q, k, v, allr, lv, R2, tiles, p, rp1, ci1, False)
+                         - O.attention_rows(q, k, v, allr, lv, R2, T, H, W, p))) < 1e-12
+
+
+# ---------------------------------------------------------------------------
 # Attention
 # ---------------------------------------------------------------------------
 def _sdpa(q, k, v, mask=None):
