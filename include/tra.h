@@ -90,7 +90,13 @@ typedef struct {
 typedef struct {
   double a, c, budget_min, budget_max, decay, radius_override;
   int32_t levels_per_nat, pool_h, pool_w, tile_h, tile_w;
-  int32_t generator; /* tra_generator */
+  int32_t generator;      /* tra_generator */
+  int32_t vote_threshold; /* >= 1: a key tile is listed for a query tile when at
+                             least this many of their (query, key) pairs are
+                             retained ([TRA] section 2, token voting); 1 = any */
+  int32_t block_mask;     /* 0: exact per-token mask inside listed tiles;
+                             1: block-only mask, every key of a listed tile
+                             (the block-sparse execution the pages feed) */
 } tra_params;
 
 /*

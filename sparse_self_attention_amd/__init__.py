@@ -42,7 +42,8 @@ class _Params(ctypes.Structure):
                 ("budget_max", ctypes.c_double), ("decay", ctypes.c_double),
                 ("radius_override", ctypes.c_double), ("levels_per_nat", ctypes.c_int32),
                 ("pool_h", ctypes.c_int32), ("pool_w", ctypes.c_int32), ("tile_h", ctypes.c_int32),
-                ("tile_w", ctypes.c_int32), ("generator", ctypes.c_int32)]
+                ("tile_w", ctypes.c_int32), ("generator", ctypes.c_int32), ("vote_threshold", ctypes.c_int32),
+                ("block_mask", ctypes.c_int32)]
 
 
 class _Info(ctypes.Structure):
@@ -125,7 +126,7 @@ def _check(status, fn):
 
 DEFAULT_PARAMS = dict(a=1.0, c=0.0, budget_min=16.0, budget_max=2048.0, decay=0.5,
                       radius_override=-1.0, levels_per_nat=8, pool_h=16, pool_w=16,
-                      tile_h=8, tile_w=8, generator=0)
+                      tile_h=8, tile_w=8, generator=0, vote_threshold=1, block_mask=0)
 GENERATORS = {"entropy_disk": 0, "manhattan": 1, "radial": 2}
 _DTYPES = {torch.bfloat16: 1, torch.float32: 0}
 

@@ -77,6 +77,9 @@ tra_status check_params(const tra_shape* s, const tra_params* p, Table* tab) {
     return fail(TRA_ERR_INVALID_ARG, "radius_override must be finite and below 32768");
   if (p->generator < TRA_GEN_ENTROPY_DISK || p->generator > TRA_GEN_RADIAL)
     return fail(TRA_ERR_INVALID_ARG, "unknown generator");
+  if (p->vote_threshold < 1 || p->vote_threshold > p->tile_h * p->tile_w * p->tile_h * p->tile_w)
+    return fail(TRA_ERR_INVALID_ARG, "vote_threshold must lie in [1, (tile_h*tile_w)^2]");
+  if (p->block_mask != 0 && p->block_mask != 1) return fail(TRA_ERR_INVALID_ARG, "block_mask must be 0 or 1");
   if (p->generator != TRA_GEN_ENTROPY_DISK && !(p->radius_override >= 0.0))
     return fail(TRA_ERR_INVALID_ARG, "the Manhattan and Radial generators take their radius from radius_override (>= 0)");
   const int T = s->T;
@@ -180,7 +183,16 @@ struct tra_plan {
   int32_t* glen = nullptr;   // per group: list length
   int32_t* gptr = nullptr;   // per group: list offset (exclusive scan of glen)
   int64_t n_groups = 0;
-  int64_t* totals = nullptr;      // device: nnz, longest row, overflow flag (+4: the same for groups)
+  int64_t* totals = nullptr;      // device: nnz, longest row, overflow flag (+4: groups, +8: filtered CSR)
+  // vote threshold > 1: per-entry votes of the unfiltered CSR, the filtered CSR's
+  // second buffers (swapped in after filtering) and the retained-pair count
+  int16_t* votes = nullptr;
+  int64_t votes_cap = 0;
+  int32_t* row_ptr2 = nullptr;
+  int32_t* col_idx2 = nullptr;
+  int64_t col2_cap = 0;
+  unsigned long long* kept_votes = nullptr;  // device
+  int64_t retained_votes = 0;
   int64_t* totals_host = nullptr; // pinned
   int64_t nnz = 0;
   int32_t max_row_len = 0;
@@ -191,7 +203,8 @@ namespace {
 void release(tra_plan* p) {
   if (!p) return;
   void* bufs[] = {p->kbar, p->H, p->lv, p->r2, p->dmax, p->r2c, p->r2off, p->pool_w,
-                  p->counts, p->row_ptr, p->col_idx, p->runs, p->rowwin, p->glist, p->glen, p->gptr, p->totals};
+                  p->counts, p->row_ptr, p->col_idx, p->runs, p->rowwin, p->glist, p->glen, p->gptr, p->totals, p->votes,
+                  p->row_ptr2, p->col_idx2, p->kept_votes};
   for (void* b : bufs)
     if (b) (void)hipFree(b);
   if (p->totals_host) (void)hipHostFree(p->totals_host);
@@ -233,6 +246,43 @@ tra_status build(tra_plan* p, const void* q, const void* k, const float* Hin, hi
     p->col_cap = cap;
   }
   TRA_HIP(tra::launch_csr_expand(p->BH, p->tiles, p->DM, p->runs, p->rowwin, p->row_ptr, p->col_idx, st));
+  const int theta = p->params.vote_threshold;
+  const bool l1 = p->params.generator == TRA_GEN_MANHATTAN;
+  if (theta > 1) {
+    // Token voting with a threshold: votes per entry, then the entries with at
+    // least theta votes form the plan's CSR.
+    if (p->nnz > p->votes_cap) {
+      if (p->votes) TRA_HIP(hipFree(p->votes));
+      p->votes = nullptr;
+      p->votes_cap = 0;
+      TRA_HIP(hipMalloc(&p->votes, p->col_cap * sizeof(int16_t)));
+      p->votes_cap = p->col_cap;
+    }
+    TRA_HIP(hipMemsetAsync(p->kept_votes, 0, sizeof(unsigned long long), st));
+    TRA_HIP(tra::launch_votes(l1, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, p->row_ptr, p->col_idx,
+                              theta, p->votes, p->counts, p->kept_votes, st));
+    TRA_HIP(tra::launch_scan(p->counts, p->n_rows, p->row_ptr2, p->totals + 8, st));
+    TRA_HIP(hipMemcpyAsync(p->totals_host, p->totals + 8, 2 * sizeof(int64_t), hipMemcpyDeviceToHost, st));
+    TRA_HIP(hipMemcpyAsync(p->totals_host + 2, p->kept_votes, sizeof(int64_t), hipMemcpyDeviceToHost, st));
+    TRA_HIP(hipStreamSynchronize(st));
+    const int64_t nnz2 = p->totals_host[0];
+    if (nnz2 > p->col2_cap) {
+      if (p->col_idx2) TRA_HIP(hipFree(p->col_idx2));
+      p->col_idx2 = nullptr;
+      p->col2_cap = 0;
+      const int64_t cap = nnz2 + nnz2 / 8 + 64;
+      TRA_HIP(hipMalloc(&p->col_idx2, cap * sizeof(int32_t)));
+      p->col2_cap = cap;
+    }
+    TRA_HIP(tra::launch_vote_compact(p->n_rows, p->row_ptr, p->col_idx, p->votes, theta, p->row_ptr2, p->col_idx2,
+                                     st));
+    std::swap(p->row_ptr, p->row_ptr2);
+    std::swap(p->col_idx, p->col_idx2);
+    std::swap(p->col_cap, p->col2_cap);
+    p->nnz = nnz2;
+    p->max_row_len = static_cast<int32_t>(p->totals_host[1]);
+    p->retained_votes = p->totals_host[2];
+  }
   if (s.dtype == TRA_BF16) {
     if (p->nnz > p->glist_cap) {
       if (p->glist) TRA_HIP(hipFree(p->glist));
@@ -241,11 +291,12 @@ tra_status build(tra_plan* p, const void* q, const void* k, const float* Hin, hi
       TRA_HIP(hipMalloc(&p->glist, p->col_cap * 2 * sizeof(int32_t)));
       p->glist_cap = p->col_cap;
     }
-    TRA_HIP(tra::launch_group_lists(false, p->BH, p->tiles, p->DM, p->runs, p->rowwin, nullptr, nullptr,
-                                    p->glen, st));
+    const int32_t* frp = theta > 1 ? p->row_ptr : nullptr;
+    TRA_HIP(tra::launch_group_lists(false, p->BH, p->tiles, p->DM, p->runs, p->rowwin, frp, p->col_idx, nullptr,
+                                    nullptr, p->glen, st));
     TRA_HIP(tra::launch_scan(p->glen, p->n_groups, p->gptr, p->totals + 4, st));
-    TRA_HIP(tra::launch_group_lists(true, p->BH, p->tiles, p->DM, p->runs, p->rowwin, p->gptr, p->glist,
-                                    p->glen, st));
+    TRA_HIP(tra::launch_group_lists(true, p->BH, p->tiles, p->DM, p->runs, p->rowwin, frp, p->col_idx, p->gptr,
+                                    p->glist, p->glen, st));
   }
   return TRA_OK;
 }
@@ -318,7 +369,11 @@ tra_status create_plan(const tra_shape* shape, const tra_params* params, Table&&
   TRA_HIP_P(hipMalloc(&p->pool_w, static_cast<size_t>(p->pool.count) * sizeof(float)));
   TRA_HIP_P(hipMalloc(&p->counts, p->n_rows * sizeof(int32_t)));
   TRA_HIP_P(hipMalloc(&p->row_ptr, (p->n_rows + 1) * sizeof(int32_t)));
-  TRA_HIP_P(hipMalloc(&p->totals, 8 * sizeof(int64_t)));
+  TRA_HIP_P(hipMalloc(&p->totals, 12 * sizeof(int64_t)));
+  if (params->vote_threshold > 1) {
+    TRA_HIP_P(hipMalloc(&p->row_ptr2, (p->n_rows + 1) * sizeof(int32_t)));
+    TRA_HIP_P(hipMalloc(&p->kept_votes, sizeof(unsigned long long)));
+  }
   for (int32_t dm : p->table.dmax) p->DM = std::max(p->DM, static_cast<int>(dm));
   {
     const int64_t run_entries = p->n_rows * (2 * p->DM + 1) * p->tiles.nh;
@@ -458,7 +513,8 @@ tra_status tra_attention(const tra_plan* plan, const void* q, const void* k, con
                              plan->params.generator == TRA_GEN_MANHATTAN};
   TRA_HIP(tra::launch_attention(s.dtype, s.head_dim, q, k, v, o, plan->lv, tab, plan->row_base,
                                 plan->BH, plan->tiles, plan->row_ptr, plan->col_idx,
-                                plan->gptr, plan->glist, plan->glen, static_cast<hipStream_t>(stream)));
+                                plan->gptr, plan->glist, plan->glen, plan->params.block_mask != 0,
+                                static_cast<hipStream_t>(stream)));
   return TRA_OK;
 }
 
@@ -525,6 +581,11 @@ tra_status tra_plan_stats(const tra_plan* plan, int64_t* retained, int64_t* list
   if (e == hipSuccess) e = hipStreamSynchronize(hs);
   (void)hipFree(dev);
   if (e != hipSuccess) return fail(TRA_ERR_HIP, std::string("tra_plan_stats: ") + hipGetErrorString(e));
+  // Pairs the attention visits under the plan's semantics: block-only masks
+  // keep every pair of a listed tile pair; a vote threshold keeps the votes
+  // of the listed tiles.
+  if (plan->params.block_mask) host[0] = host[1];
+  else if (plan->params.vote_threshold > 1) host[0] = static_cast<unsigned long long>(plan->retained_votes);
   if (retained) *retained = static_cast<int64_t>(host[0]);
   if (listed) *listed = static_cast<int64_t>(host[1]);
   return TRA_OK;

@@ -68,7 +68,7 @@ hipError_t launch_attention(int dtype, int d, const void* q, const void* k, cons
                             void* o, const int16_t* lv, const RadiusTable& tab, int row_base,
                             int BH, const Grid& tiles, const int32_t* row_ptr,
                             const int32_t* col_idx, const int32_t* gptr, const int32_t* glist,
-                            const int32_t* glen, hipStream_t s);
+                            const int32_t* glen, bool block_mask, hipStream_t s);
 // Work unit of the bf16 attention kernel: a group of GROUP_ROWS x 2 query
 // tiles of one frame, run by one workgroup of ATTN_THREADS threads (two waves
 // per query tile).
@@ -85,8 +85,16 @@ inline int64_t group_count(int BH, const Grid& tiles) {
 // at glist + 2 * gptr[group] (gptr: exclusive scan of the lengths).  The sum
 // of the lengths is at most nnz.
 hipError_t launch_group_lists(bool fill, int BH, const Grid& tiles, int DM, const int32_t* runs,
-                              const int32_t* rowwin, const int32_t* gptr, int32_t* glist, int32_t* glen,
-                              hipStream_t s);
+                              const int32_t* rowwin, const int32_t* frow_ptr, const int32_t* fcol,
+                              const int32_t* gptr, int32_t* glist, int32_t* glen, hipStream_t s);
+// Token votes per CSR entry (votes, int16 per entry), per-row count of entries
+// with at least theta votes (counts2) and the sum of their votes (added to
+// *kept_votes); then the filtered CSR (row_ptr2 = scan of counts2).
+hipError_t launch_votes(bool l1, const int16_t* lv, const int32_t* r2, const int32_t* dmax, int T, int row_base,
+                        int BH, const Grid& tiles, const int32_t* row_ptr, const int32_t* col_idx, int theta,
+                        int16_t* votes, int32_t* counts2, unsigned long long* kept_votes, hipStream_t s);
+hipError_t launch_vote_compact(int64_t n_rows, const int32_t* row_ptr, const int32_t* col_idx, const int16_t* votes,
+                               int theta, const int32_t* row_ptr2, int32_t* col_idx2, hipStream_t s);
 // Dynamic LDS the bf16 attention kernel needs for its staged K/V buffers
 // plus a compact radius table of n_r2c entries; 0 if it exceeds the device limit.
 size_t attention_lds_bytes(int d, int n_r2c);

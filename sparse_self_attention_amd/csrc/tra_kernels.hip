@@ -435,18 +435,36 @@ __global__ __launch_bounds__(256) void csr_expand_kernel(Grid g, int DM, int64_t
   }
 }
 
+// Sorted-array membership (binary search).
+__device__ __forceinline__ bool sorted_contains(const int32_t* __restrict__ a, int n, int key) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < key) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo < n && a[lo] == key;
+}
+
 // Union of the tile lists of a group of GROUP_ROWS x 2 query tiles of one
 // frame (the unit of work of the bf16 attention kernel), from the runs of
 // their rows: per (frame, tile row) the union of the runs is again a run
 // (each nonempty run contains its own query tile's column, and the group's
 // columns are adjacent).  Entries in ascending order as
-// (frame | ragged << 31, row0 | col0 << 16), where ragged marks a tile cut by
-// the bottom or right edge of the grid.  FILL = false: the union's length to
-// glen[gid]; FILL = true: the entries from glist + gptr[gid].  One wave per group.
+// (frame | member << 16 | ragged << 31, row0 | col0 << 16): member has bit
+// m = 2 * (tile row in the group) + (tile column in the group) set when query
+// tile m lists the key tile, ragged marks a tile cut by the bottom or right
+// edge of the grid.  With a vote threshold above one (frow_ptr != NULL) a
+// query tile lists a key tile when its filtered CSR row holds it, and key
+// tiles no query tile lists are left out.  FILL = false: the list's length to
+// glen[gid]; FILL = true: the entries from glist + gptr[gid].  One wave per
+// group.
 template <bool FILL>
 __global__ __launch_bounds__(256) void group_list_kernel(Grid g, int DM, int ngh, int ngw, int64_t n_groups,
                                                         const int32_t* __restrict__ runs,
                                                         const int32_t* __restrict__ rowwin,
+                                                        const int32_t* __restrict__ frow_ptr,
+                                                        const int32_t* __restrict__ fcol,
                                                         const int32_t* __restrict__ gptr,
                                                         int2* __restrict__ glist, int32_t* __restrict__ glen) {
   const int lane = threadIdx.x & 63;
@@ -480,31 +498,135 @@ __global__ __launch_bounds__(256) void group_list_kernel(Grid g, int DM, int ngh
     const int j = j0 + lane;
     const int tk = t_lo + j / g.nh, ktr = j % g.nh;
     int LO = 0xffff, HI = 0;
-    if (j < nruns) {
+    int rlo[NR], rhi[NR];
 #pragma unroll
-      for (int m = 0; m < NR; ++m) {
-        if (tk >= wlo[m] && tk < wlo[m] + wn[m]) {
-          const int r = runs[rows[m] * RS + (tk - wlo[m]) * g.nh + ktr];
-          LO = min(LO, r & 0xffff);
-          HI = max(HI, r >> 16);
-        }
+    for (int m = 0; m < NR; ++m) {
+      rlo[m] = 0xffff;
+      rhi[m] = 0;
+      if (j < nruns && tk >= wlo[m] && tk < wlo[m] + wn[m]) {
+        const int r = runs[rows[m] * RS + (tk - wlo[m]) * g.nh + ktr];
+        rlo[m] = r & 0xffff;
+        rhi[m] = r >> 16;
+        LO = min(LO, rlo[m]);
+        HI = max(HI, rhi[m]);
       }
     }
-    const int len = HI >= LO ? HI - LO + 1 : 0;
+    const int base = (tk * g.nh + ktr) * g.nw;
+    auto member = [&](int c) {
+      int mb = 0;
+#pragma unroll
+      for (int m = 0; m < NR; ++m) {
+        bool in = c >= rlo[m] && c <= rhi[m];
+        if (in && frow_ptr) {
+          const int b0 = frow_ptr[rows[m]];
+          in = sorted_contains(fcol + b0, frow_ptr[rows[m] + 1] - b0, base + c);
+        }
+        mb |= in ? 1 << m : 0;
+      }
+      return mb;
+    };
+    int len = 0;
+    if (frow_ptr) {
+      for (int c = LO; c <= HI; ++c) len += member(c) != 0;
+    } else {
+      len = HI >= LO ? HI - LO + 1 : 0;
+    }
     int total;
     const int excl = wave_excl_scan(len, lane, &total);
     if (FILL) {
       const int kr0 = ktr * g.th;
       const bool row_cut = kr0 + g.th > g.H;
-      for (int c = 0; c < len; ++c) {
-        const int kc0 = (LO + c) * g.tw;
+      int o = 0;
+      for (int c = LO; c <= HI; ++c) {
+        const int mb = member(c);
+        if (mb == 0) continue;
+        const int kc0 = c * g.tw;
         const bool ragged = row_cut || kc0 + g.tw > g.W;
-        glist[out + excl + c] = make_int2(tk | (ragged ? static_cast<int>(0x80000000u) : 0), kr0 | (kc0 << 16));
+        glist[out + excl + o] = make_int2(tk | (mb << 16) | (ragged ? static_cast<int>(0x80000000u) : 0),
+                                          kr0 | (kc0 << 16));
+        ++o;
       }
     }
     out += total;
   }
   if (lane == 0) glen[gid] = static_cast<int32_t>(out - beg);
+}
+
+// Token votes of every tile-list entry: one wave per query tile (lane =
+// query), each lane counting the keys of the entry's key tile it retains.
+// votes[e] receives the entry's total; counts2[row] the number of entries with
+// at least theta votes, and *kept_votes the sum of their votes (the retained
+// pairs under the threshold).
+template <bool L1>
+__global__ __launch_bounds__(256) void vote_kernel(const int16_t* __restrict__ lv, const int32_t* __restrict__ r2,
+                                                  const int32_t* __restrict__ dmax, int T, int row_base, Grid g,
+                                                  int64_t n_rows, const int32_t* __restrict__ row_ptr,
+                                                  const int32_t* __restrict__ col_idx, int theta,
+                                                  int16_t* __restrict__ votes, int32_t* __restrict__ counts2,
+                                                  unsigned long long* __restrict__ kept_votes) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= n_rows) return;  // wave-uniform
+  const int bh = static_cast<int>(row / g.count), tile = static_cast<int>(row % g.count);
+  const size_t N = static_cast<size_t>(g.T) * g.H * g.W;
+  const int tq = tile / g.per_frame, rem = tile % g.per_frame;
+  const int hq = (rem / g.nw) * g.th + (lane >> 3), wq = (rem % g.nw) * g.tw + (lane & 7);
+  const bool valid = hq < g.H && wq < g.W;
+  int trow = 0, dm = -1;
+  if (valid) {
+    trow = lv[static_cast<size_t>(bh) * N + (static_cast<size_t>(tq) * g.H + hq) * g.W + wq] - row_base;
+    dm = dmax[trow];
+  }
+  int kept = 0;
+  unsigned long long kv = 0;
+  for (int e = row_ptr[row]; e < row_ptr[row + 1]; ++e) {
+    const int K = col_idx[e];
+    const int tk = K / g.per_frame, krem = K % g.per_frame;
+    const int kr0 = (krem / g.nw) * g.th, kc0 = (krem % g.nw) * g.tw;
+    const int kr1 = min(kr0 + g.th, g.H) - 1, kc1 = min(kc0 + g.tw, g.W) - 1;
+    const int delta = tk > tq ? tk - tq : tq - tk;
+    const int thr = (valid && delta <= dm) ? r2[trow * T + delta] : -1;
+    int v = 0;
+    if (thr >= 0) {
+      for (int r = kr0; r <= kr1; ++r) {
+        const int a = mask_half_width<L1>(thr, r - hq);
+        if (a >= 0) v += max(0, min(wq + a, kc1) - max(wq - a, kc0) + 1);
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    if (lane == 0) votes[e] = static_cast<int16_t>(v);
+    if (v >= theta) {
+      ++kept;
+      kv += static_cast<unsigned long long>(v);
+    }
+  }
+  if (lane == 0) {
+    counts2[row] = kept;
+    atomicAdd(kept_votes, kv);
+  }
+}
+
+// Entries with at least theta votes, in order, into the filtered CSR.  One
+// wave per row.
+__global__ __launch_bounds__(256) void vote_compact_kernel(int64_t n_rows, const int32_t* __restrict__ row_ptr,
+                                                          const int32_t* __restrict__ col_idx,
+                                                          const int16_t* __restrict__ votes, int theta,
+                                                          const int32_t* __restrict__ row_ptr2,
+                                                          int32_t* __restrict__ col_idx2) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= n_rows) return;  // wave-uniform
+  const int b = row_ptr[row], e = row_ptr[row + 1];
+  int out = row_ptr2[row];
+  for (int j0 = b; j0 < e; j0 += 64) {
+    const int j = j0 + lane;
+    const int keep = (j < e && votes[j] >= theta) ? 1 : 0;
+    int total;
+    const int excl = wave_excl_scan(keep, lane, &total);
+    if (keep) col_idx2[out + excl] = col_idx[j];
+    out += total;
+  }
 }
 
 // Exclusive scan of per-row counts.  One workgroup of 1024 threads walks the
@@ -607,7 +729,7 @@ template <int D> struct AttnLds {
   static_assert(64 * KSTR % 1024 == 0 && 64 * VSTR % 1024 == 0, "tile must be whole segments");
 };
 
-template <int D, bool L1>
+template <int D, bool L1, bool BLOCK>
 __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, const int16_t* __restrict__ lv,
@@ -652,6 +774,8 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
   const bool tvalid = tc < g.nw && trq < g.nh;
   const int wq = tc * 8 + (col & 7);
   const int hq = trq * 8 + 4 * (wave & 1) + (col >> 3);
+  // This wave's query tile in the group's membership bits (see group_list_kernel).
+  const int mbit = 1 << (2 * (wave >> 2) + ((wave >> 1) & 1));
   const bool qvalid = tvalid && hq < g.H && wq < g.W;
   const size_t nq = (static_cast<size_t>(tq) * g.H + (qvalid ? hq : 0)) * g.W + (qvalid ? wq : 0);
   bf16x8 qf[KS];
@@ -676,7 +800,7 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
   int2 cur = lane < n_tiles ? lst[lane] : make_int2(0, 0);
   int2 nxt = 64 + lane < n_tiles ? lst[64 + lane] : make_int2(0, 0);
   struct TileGeo {
-    int tk, kr0, kc0;
+    int tk, kr0, kc0, member;
     bool ragged;
   };
   // Entry j (entries are read in order, each once).
@@ -687,7 +811,7 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
     }
     const int ex = __builtin_amdgcn_readlane(cur.x, j & 63);
     const int ey = __builtin_amdgcn_readlane(cur.y, j & 63);
-    return TileGeo{ex & 0x7fffffff, ey & 0xffff, ey >> 16, ex < 0};
+    return TileGeo{ex & 0xffff, ey & 0xffff, ey >> 16, (ex >> 16) & 0xf, ex < 0};
   };
 
   // One buffer resource per head for K and V: every tile, edge tiles
@@ -868,7 +992,12 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
     const int dwa = wq - t.kc0 - 4 * h;
     const int dha = hq - t.kr0;
     int dw2[4], rr[8];
-    if constexpr (L1) {
+    if constexpr (BLOCK) {  // block-only mask: every key of a listed tile inside the grid
+#pragma unroll
+      for (int b = 0; b < 4; ++b) dw2[b] = 0;
+#pragma unroll
+      for (int a = 0; a < 8; ++a) rr[a] = 1;
+    } else if constexpr (L1) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) dw2[b] = abs(dwa - b);
 #pragma unroll
@@ -894,10 +1023,15 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int* r = rr + 4 * blk;
-      doq[blk] = __any(mindw < max(max(r[0], r[1]), max(r[2], r[3])));
+      doq[blk] = (t.member & mbit) && __any(mindw < max(max(r[0], r[1]), max(r[2], r[3])));
     }
     // Sign bytes of the two differences -> 16-bit keep masks of block blk.
     auto masks = [&](int blk, uint32_t* msk) {
+      if (BLOCK && !t.ragged) {
+#pragma unroll
+        for (int x = 0; x < 8; ++x) msk[x] = 0xffffffffu;
+        return;
+      }
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
         const int ra = rr[4 * blk + (x >> 1)];
@@ -976,7 +1110,7 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
 }
 
 // fp32 inputs: one thread per query, K/V tiles in LDS, fp32 online softmax.
-template <int D, bool L1>
+template <int D, bool L1, bool BLOCK>
 __global__ __launch_bounds__(64) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, const int16_t* __restrict__ lv, const int32_t* __restrict__ r2,
@@ -1025,7 +1159,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
     for (int kk = 0; kk < 64; ++kk) {
       const int kr = kr0 + (kk >> 3), kc = kc0 + (kk & 7);
       const int dh = hq - kr, dw = wq - kc;
-      if (kr >= g.H || kc >= g.W || thr < 0 || (L1 ? abs(dh) + abs(dw) : dh * dh + dw * dw) > thr) continue;
+      if (kr >= g.H || kc >= g.W) continue;
+      if (!BLOCK && (thr < 0 || (L1 ? abs(dh) + abs(dw) : dh * dh + dw * dw) > thr)) continue;
       float s = 0.f;
 #pragma unroll
       for (int dd = 0; dd < D; ++dd) s = fmaf(qr[dd], k_lds[kk][dd], s);
@@ -1045,7 +1180,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
   }
   if (qvalid) {
     float* op = o + (static_cast<size_t>(bh) * N + nq) * D;
-    const float inv = 1.f / lsum;
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;  // no key under a vote threshold: O = 0
 #pragma unroll
     for (int dd = 0; dd < D; ++dd) op[dd] = acc[dd] * inv;
   }
@@ -1192,17 +1327,38 @@ size_t attention_lds_bytes(int d, int n_r2c) {
 }
 
 hipError_t launch_group_lists(bool fill, int BH, const Grid& tiles, int DM, const int32_t* runs,
-                              const int32_t* rowwin, const int32_t* gptr, int32_t* glist, int32_t* glen,
-                              hipStream_t s) {
+                              const int32_t* rowwin, const int32_t* frow_ptr, const int32_t* fcol,
+                              const int32_t* gptr, int32_t* glist, int32_t* glen, hipStream_t s) {
   const int ngh = (tiles.nh + GROUP_ROWS - 1) / GROUP_ROWS, ngw = (tiles.nw + 1) / 2;
   const int64_t n_groups = static_cast<int64_t>(BH) * tiles.T * ngh * ngw;
   const unsigned grid = static_cast<unsigned>((n_groups + 3) / 4);
   if (fill)
-    group_list_kernel<true><<<grid, 256, 0, s>>>(tiles, DM, ngh, ngw, n_groups, runs, rowwin, gptr,
-                                                 reinterpret_cast<int2*>(glist), glen);
+    group_list_kernel<true><<<grid, 256, 0, s>>>(tiles, DM, ngh, ngw, n_groups, runs, rowwin, frow_ptr, fcol,
+                                                 gptr, reinterpret_cast<int2*>(glist), glen);
   else
-    group_list_kernel<false><<<grid, 256, 0, s>>>(tiles, DM, ngh, ngw, n_groups, runs, rowwin, gptr,
-                                                  reinterpret_cast<int2*>(glist), glen);
+    group_list_kernel<false><<<grid, 256, 0, s>>>(tiles, DM, ngh, ngw, n_groups, runs, rowwin, frow_ptr, fcol,
+                                                  gptr, reinterpret_cast<int2*>(glist), glen);
+  return hipGetLastError();
+}
+
+hipError_t launch_votes(bool l1, const int16_t* lv, const int32_t* r2, const int32_t* dmax, int T, int row_base,
+                        int BH, const Grid& tiles, const int32_t* row_ptr, const int32_t* col_idx, int theta,
+                        int16_t* votes, int32_t* counts2, unsigned long long* kept_votes, hipStream_t s) {
+  const int64_t n_rows = static_cast<int64_t>(BH) * tiles.count;
+  const unsigned grid = static_cast<unsigned>((n_rows + 3) / 4);
+  if (l1)
+    vote_kernel<true><<<grid, 256, 0, s>>>(lv, r2, dmax, T, row_base, tiles, n_rows, row_ptr, col_idx, theta,
+                                           votes, counts2, kept_votes);
+  else
+    vote_kernel<false><<<grid, 256, 0, s>>>(lv, r2, dmax, T, row_base, tiles, n_rows, row_ptr, col_idx, theta,
+                                            votes, counts2, kept_votes);
+  return hipGetLastError();
+}
+
+hipError_t launch_vote_compact(int64_t n_rows, const int32_t* row_ptr, const int32_t* col_idx, const int16_t* votes,
+                               int theta, const int32_t* row_ptr2, int32_t* col_idx2, hipStream_t s) {
+  vote_compact_kernel<<<static_cast<unsigned>((n_rows + 3) / 4), 256, 0, s>>>(n_rows, row_ptr, col_idx, votes, theta,
+                                                                            row_ptr2, col_idx2);
   return hipGetLastError();
 }
 
@@ -1210,7 +1366,7 @@ hipError_t launch_attention(int dtype, int d, const void* q, const void* k, cons
                             void* o, const int16_t* lv, const RadiusTable& tab, int row_base,
                             int BH, const Grid& tiles, const int32_t* row_ptr,
                             const int32_t* col_idx, const int32_t* gptr, const int32_t* glist,
-                            const int32_t* glen, hipStream_t s) {
+                            const int32_t* glen, bool block_mask, hipStream_t s) {
   const int32_t* r2 = tab.r2;
   const unsigned rows = static_cast<unsigned>(BH) * tiles.count;
   if (dtype == 1) {
@@ -1223,16 +1379,19 @@ hipError_t launch_attention(int dtype, int d, const void* q, const void* k, cons
     const unsigned grid = static_cast<unsigned>((groups + 7) / 8 * 8);
     const int ng = static_cast<int>(groups);
     const size_t lds_tab = static_cast<size_t>(tab.n_r2c) * sizeof(int32_t);
-#define TRA_ATTN(DD, M)                                                                                 \
-  attn_bf16_kernel<DD, M><<<grid, ATTN_THREADS, lds_tab, s>>>(qq, kk, vv, oo, lv, tab.r2c, tab.r2off, tab.dmax, \
-                                                              tab.n_r2c, row_base, tiles, ngh, ngw, ng, gptr,     \
-                                                              reinterpret_cast<const int2*>(glist), glen)
-    if (tab.l1) {
-      if (d == 128) TRA_ATTN(128, true);
-      else TRA_ATTN(64, true);
+#define TRA_ATTN(DD, M, B)                                                                                 \
+  attn_bf16_kernel<DD, M, B><<<grid, ATTN_THREADS, lds_tab, s>>>(qq, kk, vv, oo, lv, tab.r2c, tab.r2off, tab.dmax, \
+                                                                 tab.n_r2c, row_base, tiles, ngh, ngw, ng, gptr,     \
+                                                                 reinterpret_cast<const int2*>(glist), glen)
+    if (block_mask) {
+      if (d == 128) TRA_ATTN(128, false, true);
+      else TRA_ATTN(64, false, true);
+    } else if (tab.l1) {
+      if (d == 128) TRA_ATTN(128, true, false);
+      else TRA_ATTN(64, true, false);
     } else {
-      if (d == 128) TRA_ATTN(128, false);
-      else TRA_ATTN(64, false);
+      if (d == 128) TRA_ATTN(128, false, false);
+      else TRA_ATTN(64, false, false);
     }
 #undef TRA_ATTN
   } else {
@@ -1240,14 +1399,17 @@ hipError_t launch_attention(int dtype, int d, const void* q, const void* k, cons
     const auto* kk = static_cast<const float*>(k);
     const auto* vv = static_cast<const float*>(v);
     auto* oo = static_cast<float*>(o);
-#define TRA_ATTN32(DD, M) \
-  attn_f32_kernel<DD, M><<<rows, 64, 0, s>>>(qq, kk, vv, oo, lv, r2, row_base, tiles.T, tiles, row_ptr, col_idx)
-    if (tab.l1) {
-      if (d == 128) TRA_ATTN32(128, true);
-      else TRA_ATTN32(64, true);
+#define TRA_ATTN32(DD, M, B) \
+  attn_f32_kernel<DD, M, B><<<rows, 64, 0, s>>>(qq, kk, vv, oo, lv, r2, row_base, tiles.T, tiles, row_ptr, col_idx)
+    if (block_mask) {
+      if (d == 128) TRA_ATTN32(128, false, true);
+      else TRA_ATTN32(64, false, true);
+    } else if (tab.l1) {
+      if (d == 128) TRA_ATTN32(128, true, false);
+      else TRA_ATTN32(64, true, false);
     } else {
-      if (d == 128) TRA_ATTN32(128, false);
-      else TRA_ATTN32(64, false);
+      if (d == 128) TRA_ATTN32(128, false, false);
+      else TRA_ATTN32(64, false, false);
     }
 #undef TRA_ATTN32
   }

@@ -246,3 +246,76 @@ def test_generator_full_size_sampled(gpu, gen, r):
         _say("head", h, "O", m["o_max_abs"], m["o_mean_abs"])
     retained, listed = run["plan"].stats()
     _say("density", retained / (cfg.heads * cfg.N ** 2), "tile efficiency", retained / listed)
+
+
+# ---------------------------------------------------------------------------
+# Token voting with a threshold; block-only masks
+# ---------------------------------------------------------------------------
+def _check_listed(cfg, run, h, block_only, tile_sample=None, query_sample=None):
+    p = cfg.params()
+    exp = run["export"]
+    lv = exp["levels"][h].astype(np.int64)
+    R2 = O.radius_table(p, cfg.T)
+    tiles = O.Geometry(cfg.T, cfg.H, cfg.W, cfg.tile_h, cfg.tile_w)
+    rp = exp["row_ptr"].astype(np.int64)
+    base = h * tiles.count
+    rows_h = rp[base:base + tiles.count + 1]
+    ci_h = exp["col_idx"][rows_h[0]:rows_h[-1]].astype(np.int64)
+    rp_h = rows_h - rows_h[0]
+    theta = p["vote_threshold"]
+    for a in (range(tiles.count) if tile_sample is None else tile_sample):
+        votes = O.tile_votes(int(a), lv, R2, tiles, p)
+        ref = np.array(sorted(b for b, n in votes.items() if n >= theta), dtype=np.int64)
+        assert np.array_equal(ci_h[rp_h[a]:rp_h[a + 1]], ref), f"tile list of query tile {a} differs"
+    qs = np.arange(cfg.N) if query_sample is None else np.asarray(query_sample)
+    qh, kh, vh = (run[x][0, h].double().cpu().numpy() for x in ("q", "k", "v"))
+    ref = O.attention_rows_listed(qh, kh, vh, qs, lv, R2, tiles, p, rp_h, ci_h, block_only)
+    err = np.abs(run["o"][0, h].double().cpu().numpy()[qs] - ref)
+    assert err.max() <= MAX_ABS_ and err.mean() <= MEAN_ABS_, (err.max(), err.mean())
+    return err
+
+
+MAX_ABS_, MEAN_ABS_ = 2e-2, 2e-3
+
+
+@pytest.mark.parametrize("theta,block,dtype", [(4, 0, "bf16"), (40, 0, "bf16"), (1, 1, "bf16"), (8, 1, "bf16"),
+                                               (300, 1, "bf16"), (6, 0, "fp32"), (1, 1, "fp32"), (20, 1, "fp32")])
+def test_vote_threshold_and_block_mask_small(gpu, theta, block, dtype):
+    cfg = small_workload(T=3, H=13, W=21, heads=2, c=-0.5, budget_max=819.0, vote_threshold=theta,
+                         block_mask=block, dtype=dtype, head_dim=128 if dtype == "bf16" else 64)
+    _say("case: votes", theta, "block", block, dtype)
+    run = gpu_run(cfg, gpu)
+    for h in range(cfg.heads):
+        err = _check_listed(cfg, run, h, bool(block))
+        _say("head", h, "O", err.max(), err.mean())
+    retained, listed = run["plan"].stats()
+    p = cfg.params()
+    R2 = O.radius_table(p, cfg.T)
+    tiles = O.Geometry(cfg.T, cfg.H, cfg.W, cfg.tile_h, cfg.tile_w)
+    if block:
+        assert retained == listed
+    else:
+        ref = 0
+        for h in range(cfg.heads):
+            lv = run["export"]["levels"][h].astype(np.int64)
+            for a in range(tiles.count):
+                ref += sum(n for n in O.tile_votes(a, lv, R2, tiles, p).values() if n >= theta)
+        assert retained == ref
+
+
+@pytest.mark.parametrize("theta,block", [(64, 1), (256, 0)])
+def test_vote_threshold_full_size_sampled(gpu, theta, block):
+    from dataclasses import replace
+    cfg = replace(CONFIGS["wan21_14b_720p"], vote_threshold=theta, block_mask=block)
+    _say("case: votes full size", theta, block)
+    run = gpu_run(cfg, gpu)
+    check_csr_properties(cfg, run)
+    rng = np.random.default_rng(51)
+    tiles = O.Geometry(cfg.T, cfg.H, cfg.W, 8, 8)
+    for h in (0, cfg.heads - 1):
+        ts = np.concatenate([rng.choice(tiles.count, size=6, replace=False), [0, tiles.count - 1]])
+        qs = np.concatenate([rng.choice(cfg.N, size=16, replace=False), [0, cfg.N - 1]])
+        err = _check_listed(cfg, run, h, bool(block), tile_sample=ts, query_sample=qs)
+        _say("head", h, "O", err.max(), err.mean())
+    retained, listed = run["plan"].stats()
+    _say("pairs", retained, "listed", listed, "density", retained / (cfg.heads * cfg.N ** 2))

@@ -43,6 +43,8 @@ class Workload:
     tile_w: int = 8
     radius_override: float = -1.0
     generator: int = 0  # 0: entropy -> disk (the method); 1: fixed Manhattan radius; 2: Radial static mask
+    vote_threshold: int = 1  # key tile listed when >= this many pairs are retained
+    block_mask: int = 0  # 1: block-only mask (every key of a listed tile)
     seed: int = 0
     batch: int = 1
     reuse_calls: int = 1  # attention calls that reuse one plan
@@ -58,7 +60,8 @@ class Workload:
     def params(self) -> dict:
         """Method parameters (what the planning call receives)."""
         keys = ("a", "c", "budget_min", "budget_max", "decay", "levels_per_nat",
-                "pool_h", "pool_w", "tile_h", "tile_w", "radius_override", "generator")
+                "pool_h", "pool_w", "tile_h", "tile_w", "radius_override", "generator",
+                "vote_threshold", "block_mask")
         d = asdict(self)
         return {k: d[k] for k in keys}
 
