@@ -94,6 +94,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--vote-threshold", type=int, default=None,
+                    help="plan variant: list a key tile only with at least this many retained pairs")
+    ap.add_argument("--block-mask", action="store_true",
+                    help="plan variant: block-only masks (every key of a listed tile)")
+    ap.add_argument("--generator", choices=["entropy_disk", "manhattan", "radial"], default="entropy_disk")
+    ap.add_argument("--radius", type=float, default=None, help="fixed radius (static generators)")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense-attention comparison")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a reference for "
                          "hardware byte counters)")
@@ -108,6 +115,17 @@ def main():
     tra.load_library()  # fails loudly when libtra.so is missing
 
     cfg = get_config(args.workload)
+    variant = {}
+    if args.vote_threshold is not None:
+        variant["vote_threshold"] = args.vote_threshold
+    if args.block_mask:
+        variant["block_mask"] = 1
+    if args.generator != "entropy_disk":
+        variant["generator"] = tra.GENERATORS[args.generator]
+        variant["radius_override"] = args.radius if args.radius is not None else 16.0
+    if variant:
+        from dataclasses import replace
+        cfg = replace(cfg, **variant)
     dev = torch.device("cuda:0")
     if args.copy_probe_mb > 0:
         src = torch.ones(args.copy_probe_mb << 18, dtype=torch.float32, device=dev)
@@ -213,11 +231,14 @@ def main():
     def dense(with_entropy):
         tra.dense_attention(q, k, v, grid, out=outs[0], entropy=H_warm if with_entropy else False)
 
-    dense(False)
-    dense(True)
-    torch.cuda.synchronize()
-    dense_ms = time_ms(lambda: dense(False), 3)
-    dense_ent_ms = time_ms(lambda: dense(True), 3)
+    if args.no_dense:
+        dense_ms = dense_ent_ms = float("nan")
+    else:
+        dense(False)
+        dense(True)
+        torch.cuda.synchronize()
+        dense_ms = time_ms(lambda: dense(False), 3)
+        dense_ent_ms = time_ms(lambda: dense(True), 3)
     dense_flops = 4.0 * cfg.head_dim * cfg.batch * cfg.heads * float(cfg.N) ** 2
     log(f"[bench] dense attention {dense_ms:.2f} ms, dense warm-up pass with entropy {dense_ent_ms:.2f} ms")
 
@@ -245,7 +266,8 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic",
-        "config": {"workload": cfg.name, "B": cfg.batch, "heads": cfg.heads, "grid": list(grid),
+        "config": {"workload": cfg.name + ("+" + "+".join(f"{k}={v}" for k, v in variant.items()) if variant else ""),
+                   "B": cfg.batch, "heads": cfg.heads, "grid": list(grid),
                    "head_dim": cfg.head_dim, "attention_calls_per_plan": calls,
                    "retained_density": retained / (cfg.heads * cfg.N ** 2),
                    "tile_efficiency": retained / listed},
@@ -253,11 +275,6 @@ def main():
         "timing_ms": {"attention": pct(attn_ms_all), "plan": pct(plan_ms_all),
                       "cold_attention_median": float(np.median(cold_attn)),
                       "cold_plan_median": float(np.median(cold_plan))},
-        "dense": {"ms": dense_ms, "tflops": dense_flops / (dense_ms * 1e-3) / 1e12,
-                  "frac_bf16_peak": dense_flops / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                  "warmup_with_entropy_ms": dense_ent_ms,
-                  "sparse_attention_speedup": dense_ms / attn_ms,
-                  "step_speedup": (calls * dense_ms) / ms_step},
         "plan_drift": {"call": calls, "changed_levels": drift,
                        "fraction": drift / (cfg.batch * cfg.heads * cfg.N)},
         "attention": {"retained_tflops": achieved, "frac_bf16_peak": achieved / PEAK_BF16_TFLOPS,
@@ -271,7 +288,13 @@ def main():
                      "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": measured_traffic() if cfg.name == WORKLOAD else None},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_dense:
+        result["dense"] = {"ms": dense_ms, "tflops": dense_flops / (dense_ms * 1e-3) / 1e12,
+                           "frac_bf16_peak": dense_flops / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                           "warmup_with_entropy_ms": dense_ent_ms,
+                           "sparse_attention_speedup": dense_ms / attn_ms,
+                           "step_speedup": (calls * dense_ms) / ms_step}
+    if not args.no_cpu_baseline and not variant:
         log("[bench] timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(cfg, q, k, v, None)
     print(json.dumps(result), flush=True)

@@ -84,6 +84,16 @@ __device__ __forceinline__ int wave_max_u(int v) {
   return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
              max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
+// Wave-wide sum with a wave-uniform result (same DPP pattern: pairs, quads,
+// then rotations by 4 and 8 inside each row of 16).
+__device__ __forceinline__ int wave_sum_u(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) + __builtin_amdgcn_readlane(v, 32) +
+         __builtin_amdgcn_readlane(v, 48);
+}
 // Exclusive prefix sum over the wave's lanes; *total receives the wave sum.
 __device__ __forceinline__ int wave_excl_scan(int v, int lane, int* total) {
   int x = v;

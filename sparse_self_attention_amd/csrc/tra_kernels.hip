@@ -579,22 +579,37 @@ __global__ __launch_bounds__(256) void vote_kernel(const int16_t* __restrict__ l
   }
   int kept = 0;
   unsigned long long kv = 0;
+  // Entries come in runs of one (frame, key tile row): the lane's chord
+  // half-widths over the tile row's 8 key rows (-1: none) are computed once
+  // per run.
+  int half[8];
+  int prevK = -2, kcol = 0;
   for (int e = row_ptr[row]; e < row_ptr[row + 1]; ++e) {
     const int K = col_idx[e];
-    const int tk = K / g.per_frame, krem = K % g.per_frame;
-    const int kr0 = (krem / g.nw) * g.th, kc0 = (krem % g.nw) * g.tw;
-    const int kr1 = min(kr0 + g.th, g.H) - 1, kc1 = min(kc0 + g.tw, g.W) - 1;
-    const int delta = tk > tq ? tk - tq : tq - tk;
-    const int thr = (valid && delta <= dm) ? r2[trow * T + delta] : -1;
-    int v = 0;
-    if (thr >= 0) {
-      for (int r = kr0; r <= kr1; ++r) {
-        const int a = mask_half_width<L1>(thr, r - hq);
-        if (a >= 0) v += max(0, min(wq + a, kc1) - max(wq - a, kc0) + 1);
-      }
-    }
+    // The next column of the same run needs no division (wave-uniform test).
+    if (K == prevK + 1 && kcol + 1 < g.nw) {
+      ++kcol;
+    } else {
+      const int tk = K / g.per_frame, krem = K % g.per_frame;
+      const int ktr = krem / g.nw;
+      kcol = krem % g.nw;
+      const int kr0 = ktr * g.th;
+      const int delta = tk > tq ? tk - tq : tq - tk;
+      const int thr = (valid && delta <= dm) ? r2[trow * T + delta] : -1;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+      for (int r = 0; r < 8; ++r)
+        half[r] = (thr >= 0 && kr0 + r < g.H) ? mask_half_width<L1>(thr, kr0 + r - hq) : -1;
+    }
+    prevK = K;
+    const int kc0 = kcol * g.tw;
+    const int kc1 = min(kc0 + g.tw, g.W) - 1;
+    int v = 0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int a = half[r];
+      if (a >= 0) v += max(0, min(wq + a, kc1) - max(wq - a, kc0) + 1);
+    }
+    v = wave_sum_u(v);
     if (lane == 0) votes[e] = static_cast<int16_t>(v);
     if (v >= theta) {
       ++kept;
