@@ -209,8 +209,10 @@ tra_status tra_plan_export(const tra_plan* plan, int16_t* levels, float* entropy
 
 /*
  * Exact pair counts of a plan (synchronises `stream`):
- *   retained  sum over queries of the keys each retains (the FLOPs that count:
- *             4*d per retained pair)
+ *   retained  sum over queries of the keys each attends to (the FLOPs that
+ *             count: 4*d per pair): the keys it retains; with vote_threshold
+ *             > 1 only those inside its tile's listed tiles (the votes of the
+ *             kept tiles); with block_mask, every key of the listed tiles
  *   listed    sum over CSR entries of (valid queries x valid keys) of the pair
  *             of tiles: the pairs a tile-granular kernel visits
  */
