@@ -43,7 +43,7 @@ __all__ = [
     "frame_sum", "radius_table", "table_margin", "retained_keys", "retained_count",
     "retained_counts", "dense_mask", "query_tile_row", "csr", "attention_rows",
     "dense_attention", "dense_entropy", "excused_queries", "round_to_dtype", "plan", "ENTROPY_EXCUSE",
-    "GEN_ENTROPY_DISK", "GEN_MANHATTAN", "GEN_RADIAL", "radial_band", "tile_votes", "csr_vote",
+    "GEN_ENTROPY_DISK", "GEN_MANHATTAN", "GEN_RADIAL", "GEN_WINDOW_1D", "radial_band", "tile_votes", "csr_vote",
     "listed_keys", "attention_rows_listed",
 ]
 
@@ -241,7 +241,7 @@ def frame_sum(decay, T):
     return sum(decay ** (2 * abs(dl)) for dl in range(-(T - 1), T))
 
 
-GEN_ENTROPY_DISK, GEN_MANHATTAN, GEN_RADIAL = 0, 1, 2
+GEN_ENTROPY_DISK, GEN_MANHATTAN, GEN_RADIAL, GEN_WINDOW_1D = 0, 1, 2, 3
 
 
 def _generator(p):
@@ -251,6 +251,11 @@ def _generator(p):
 def _l1(p):
     """True when the mask measures distance with the L1 norm (Manhattan)."""
     return _generator(p) == GEN_MANHATTAN
+
+
+def _window(p):
+    """True for the 1-D ablation: distance along the raster token order."""
+    return _generator(p) == GEN_WINDOW_1D
 
 
 def radial_band(delta):
@@ -282,6 +287,19 @@ def radius_table(p, T):
         assert p["radius_override"] >= 0, "the Manhattan generator needs a fixed radius"
         R = math.floor(p["radius_override"])
         return np.array([[R - dl if R - dl >= 0 else -1 for dl in range(T)]], dtype=np.int64)
+    if _window(p):
+        # 1-D ablation ([TRA] section 4: the radius mask replaced by a 1-D
+        # distance): query i keeps the keys j with |n_i - n_j| <= rho along the
+        # raster order, rho = floor((B - 1)/2) so that the window of 2 rho + 1
+        # tokens holds the quantised budget B (or floor(radius_override) when
+        # set).  The same rho stands in every column (frame distances play no
+        # part of their own).
+        if p["radius_override"] >= 0:
+            rhos = [math.floor(p["radius_override"])]
+        else:
+            k_lo, k_hi = level_range(p)
+            rhos = [math.floor((math.exp(k / p["levels_per_nat"]) - 1.0) / 2.0) for k in range(k_lo, k_hi + 1)]
+        return np.array([[r] * T for r in rhos], dtype=np.int64)
     if _generator(p) == GEN_RADIAL:
         assert p["radius_override"] >= 0, "the Radial generator needs a fixed radius"
         r0sq = p["radius_override"] ** 2
@@ -337,6 +355,9 @@ def retained_keys(i, level, R2, T, H, W, p):
     """Sorted key indices retained by query i (disk enumeration per frame)."""
     t, h, w = i // (H * W), (i // W) % H, i % W
     r2row = _row(level, R2, p)
+    if _window(p):
+        rho = int(r2row[0])
+        return np.arange(max(0, i - rho), min(T * H * W - 1, i + rho) + 1, dtype=np.int64)
     out = []
     for tk in range(T):
         lim = r2row[abs(tk - t)]
@@ -354,6 +375,9 @@ def retained_keys(i, level, R2, T, H, W, p):
 def retained_count(i, level, R2, T, H, W, p):
     t, h, w = i // (H * W), (i // W) % H, i % W
     r2row = _row(level, R2, p)
+    if _window(p):
+        rho = int(r2row[0])
+        return min(T * H * W - 1, i + rho) - max(0, i - rho) + 1
     n = 0
     for tk in range(T):
         lim = r2row[abs(tk - t)]
@@ -373,6 +397,9 @@ def retained_counts(lv, R2, T, H, W, p):
     n = np.arange(N)
     t, h, w = n // (H * W), (n // W) % H, n % W
     rows = R2[np.zeros(N, dtype=np.int64)] if p["radius_override"] >= 0 else R2[lv - level_range(p)[0]]
+    if _window(p):
+        rho = rows[:, 0]
+        return np.minimum(N - 1, n + rho) - np.maximum(0, n - rho) + 1
     total = np.zeros(N, dtype=np.int64)
     for tk in range(T):
         lim = rows[np.arange(N), np.abs(tk - t)]
@@ -399,6 +426,8 @@ def dense_mask(lv, R2, T, H, W, p):
     rows = R2[np.zeros(N, dtype=np.int64)] if p["radius_override"] >= 0 else R2[lv - level_range(p)[0]]
     dt = np.abs(t[:, None] - t[None, :])
     lim = np.take_along_axis(rows, dt, axis=1)
+    if _window(p):
+        return np.abs(n[:, None] - n[None, :]) <= rows[:, :1]
     if _l1(p):
         d = np.abs(h[:, None] - h[None, :]) + np.abs(w[:, None] - w[None, :])
     else:
@@ -413,6 +442,11 @@ def query_tile_row(a, lv, R2, tiles: Geometry, p):
     """Sorted key tile ids listed for query tile a (any retained pair votes)."""
     T, H, W = tiles.T, tiles.H, tiles.W
     hit = set()
+    if _window(p):
+        key_tile = tiles.block_of_tokens()
+        for i in tiles.tokens(a):
+            hit.update(np.unique(key_tile[retained_keys(int(i), int(lv[i]), R2, T, H, W, p)]).tolist())
+        return np.array(sorted(hit), dtype=np.int64)
     for i in tiles.tokens(a):
         t, h, w = i // (H * W), (i // W) % H, i % W
         r2row = _row(lv[i], R2, p)

@@ -420,6 +420,49 @@ def test_generator_masks_enumeration_and_csr(gen, seed):
         assert np.array_equal(col_idx[row_ptr[a]:row_ptr[a + 1]], np.nonzero(hit[a])[0])
 
 
+def test_window_1d_table_holds_the_budget():
+    """Each level's window of 2 rho + 1 tokens is the largest odd window within
+    the quantised budget B = e^(k/q): 2 rho + 1 <= B < 2 rho + 3."""
+    p = _p(generator=O.GEN_WINDOW_1D)
+    R2 = O.radius_table(p, 3)
+    k_lo, k_hi = O.level_range(p)
+    assert R2.shape == (k_hi - k_lo + 1, 3)
+    for r, k in enumerate(range(k_lo, k_hi + 1)):
+        B = math.exp(k / p["levels_per_nat"])
+        rho = int(R2[r, 0])
+        assert np.all(R2[r] == rho)
+        assert 2 * rho + 1 <= B < 2 * rho + 3
+    assert list(O.radius_table(_p(generator=O.GEN_WINDOW_1D, radius_override=7.9), 2)[0]) == [7, 7]
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_window_1d_masks_enumeration_and_csr(seed):
+    rng = np.random.default_rng(500 + seed)
+    T, H, W = int(rng.integers(1, 4)), int(rng.integers(2, 12)), int(rng.integers(2, 12))
+    p = _p(budget_min=2.0, budget_max=300.0, generator=O.GEN_WINDOW_1D,
+           tile_h=int(rng.choice([2, 3, 8])), tile_w=int(rng.choice([2, 5, 8])))
+    R2 = O.radius_table(p, T)
+    lv = _random_levels(rng, T * H * W, p)
+    mask = O.dense_mask(lv, R2, T, H, W, p)
+    # the window straight from coordinates
+    t, h, w = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    n = ((t * H + h) * W + w).reshape(-1)
+    rho = R2[lv - O.level_range(p)[0], 0]
+    assert np.array_equal(mask, np.abs(n[:, None] - n[None, :]) <= rho[:, None])
+    for i in range(T * H * W):
+        assert np.array_equal(O.retained_keys(i, lv[i], R2, T, H, W, p), np.nonzero(mask[i])[0])
+        assert O.retained_count(i, lv[i], R2, T, H, W, p) == mask[i].sum()
+    assert np.array_equal(O.retained_counts(lv, R2, T, H, W, p), mask.sum(axis=1))
+    tiles = O.Geometry(T, H, W, p["tile_h"], p["tile_w"])
+    blk = tiles.block_of_tokens()
+    hit = np.zeros((tiles.count, tiles.count), dtype=bool)
+    qi, kj = np.nonzero(mask)
+    hit[blk[qi], blk[kj]] = True
+    row_ptr, col_idx = O.csr(lv, R2, tiles, p)
+    for a in range(tiles.count):
+        assert np.array_equal(col_idx[row_ptr[a]:row_ptr[a + 1]], np.nonzero(hit[a])[0])
+
+
 # ---------------------------------------------------------------------------
 # Token voting with a threshold; block-only masks
 # ---------------------------------------------------------------------------
