@@ -98,7 +98,8 @@ def main():
                     help="plan variant: list a key tile only with at least this many retained pairs")
     ap.add_argument("--block-mask", action="store_true",
                     help="plan variant: block-only masks (every key of a listed tile)")
-    ap.add_argument("--generator", choices=["entropy_disk", "manhattan", "radial"], default="entropy_disk")
+    ap.add_argument("--generator", choices=["entropy_disk", "manhattan", "radial", "window_1d"],
+                    default="entropy_disk")
     ap.add_argument("--radius", type=float, default=None, help="fixed radius (static generators)")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-attention comparison")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -122,7 +123,8 @@ def main():
         variant["block_mask"] = 1
     if args.generator != "entropy_disk":
         variant["generator"] = tra.GENERATORS[args.generator]
-        variant["radius_override"] = args.radius if args.radius is not None else 16.0
+        if args.radius is not None or args.generator != "window_1d":
+            variant["radius_override"] = args.radius if args.radius is not None else 16.0
     if variant:
         from dataclasses import replace
         cfg = replace(cfg, **variant)

@@ -115,10 +115,23 @@ typedef struct {
  *                         R2[delta] = floor(radius_override^2 / 2^b), b = 0 for
  *                         delta = 0 and floor(log2 delta) + 1 otherwise; frames
  *                         with R2 < 1 are inactive.
- * The two static generators need radius_override >= 0 and ignore the entropy
- * (every level is -1).
+ *   TRA_GEN_WINDOW_1D     the 1-D distance ablation ([TRA] section 4): keep j
+ *                         iff |n_i - n_j| <= rho along the raster token order,
+ *                         rho = floor((B_i - 1)/2) for the query's quantised
+ *                         budget B_i (floor(radius_override) when >= 0), so the
+ *                         window of 2 rho + 1 tokens holds the budget; every
+ *                         radius-table entry of a level is its rho.  Needs at
+ *                         most 64 tile columns (W <= 512 with 8-wide tiles),
+ *                         vote_threshold 1, and rho < 2^24.
+ * The Manhattan and Radial generators need radius_override >= 0 and ignore the
+ * entropy (every level is -1).
  */
-typedef enum { TRA_GEN_ENTROPY_DISK = 0, TRA_GEN_MANHATTAN = 1, TRA_GEN_RADIAL = 2 } tra_generator;
+typedef enum {
+  TRA_GEN_ENTROPY_DISK = 0,
+  TRA_GEN_MANHATTAN = 1,
+  TRA_GEN_RADIAL = 2,
+  TRA_GEN_WINDOW_1D = 3
+} tra_generator;
 
 typedef struct tra_plan tra_plan; /* opaque; owns its device buffers */
 
@@ -206,6 +219,21 @@ tra_status tra_plan_get_info(const tra_plan* plan, tra_plan_info* info);
  */
 tra_status tra_plan_export(const tra_plan* plan, int16_t* levels, float* entropy, int32_t* r2,
                            int32_t* row_ptr, int32_t* col_idx, void* kbar, void* stream);
+
+/*
+ * The bf16 attention kernel's unit of work (host copies; synchronises
+ * `stream`): a group is 2 x 2 query tiles of one frame (group id = (b*heads +
+ * head, frame, group row, group column) in row-major order), walked over the
+ * ascending union of their tile lists.  *n_groups and *n_entries receive the
+ * counts (call with NULL arrays first); gptr/glen int32 [n_groups] the offset
+ * and length of each group's list in glist; glist int32 [2*n_entries], entry
+ * (frame | member << 16 | edge << 31, row0 | col0 << 16), member bit
+ * 2*(tile row in group) + (tile column in group) set when that query tile
+ * lists the key tile, edge set for a tile cut by the grid's bottom or right
+ * edge.  TRA_ERR_DTYPE for fp32 plans (their kernel reads the CSR).
+ */
+tra_status tra_plan_export_groups(const tra_plan* plan, int64_t* n_groups, int64_t* n_entries, int32_t* gptr,
+                                  int32_t* glen, int32_t* glist, void* stream);
 
 /*
  * Exact pair counts of a plan (synchronises `stream`):

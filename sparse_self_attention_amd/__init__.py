@@ -81,6 +81,8 @@ _SIGS = {
                                                     ctypes.POINTER(_P)]),
     "tra_plan_rebuild_from_entropy": (ctypes.c_int, [_P, _P, _P]),
     "tra_dense_attention": (ctypes.c_int, [ctypes.POINTER(_Shape), _P, _P, _P, _P, _P, _P]),
+    "tra_plan_export_groups": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+                                              _P, _P, _P, _P]),
     "tra_schedule_create": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.POINTER(_Params),
                                            ctypes.POINTER(_SchedParams), ctypes.POINTER(_P)]),
     "tra_schedule_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.POINTER(_StepInfo)]),
@@ -127,7 +129,7 @@ def _check(status, fn):
 DEFAULT_PARAMS = dict(a=1.0, c=0.0, budget_min=16.0, budget_max=2048.0, decay=0.5,
                       radius_override=-1.0, levels_per_nat=8, pool_h=16, pool_w=16,
                       tile_h=8, tile_w=8, generator=0, vote_threshold=1, block_mask=0)
-GENERATORS = {"entropy_disk": 0, "manhattan": 1, "radial": 2}
+GENERATORS = {"entropy_disk": 0, "manhattan": 1, "radial": 2, "window_1d": 3}
 _DTYPES = {torch.bfloat16: 1, torch.float32: 0}
 
 
@@ -241,6 +243,22 @@ class Plan:
                 "row_ptr": row_ptr, "col_idx": col_idx[:inf["nnz"]],
                 "kbar": kbar.reshape(BH, inf["n_pool"], s.head_dim), "k_lo": inf["k_lo"],
                 "n_qtiles": inf["n_qtiles"]}
+
+    def export_groups(self):
+        """bf16 plans: host copies of the attention kernel's group lists as
+        (gptr, glen, entries [n, 2]) numpy int32 arrays."""
+        import numpy as np
+        lib = load_library()
+        ng, ne = ctypes.c_int64(), ctypes.c_int64()
+        _check(lib.tra_plan_export_groups(self.handle, ctypes.byref(ng), ctypes.byref(ne), None, None, None,
+                                          _stream(self.device)), "tra_plan_export_groups")
+        gptr = np.zeros(ng.value, dtype=np.int32)
+        glen = np.zeros(ng.value, dtype=np.int32)
+        gl = np.zeros((max(1, ne.value), 2), dtype=np.int32)
+        _check(lib.tra_plan_export_groups(self.handle, ctypes.byref(ng), ctypes.byref(ne), gptr.ctypes.data_as(_P),
+                                          glen.ctypes.data_as(_P), gl.ctypes.data_as(_P), _stream(self.device)),
+               "tra_plan_export_groups")
+        return gptr, glen, gl[:ne.value]
 
     def stats(self):
         """(retained pairs, listed pairs): exact counts over the whole plan."""

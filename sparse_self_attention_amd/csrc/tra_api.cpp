@@ -75,12 +75,17 @@ tra_status check_params(const tra_shape* s, const tra_params* p, Table* tab) {
     return fail(TRA_ERR_SHAPE, "bf16 attention needs T*H*W*head_dim*2 (bytes of one head) below 2^31");
   if (!std::isfinite(p->radius_override) || p->radius_override >= 32768.0)
     return fail(TRA_ERR_INVALID_ARG, "radius_override must be finite and below 32768");
-  if (p->generator < TRA_GEN_ENTROPY_DISK || p->generator > TRA_GEN_RADIAL)
+  if (p->generator < TRA_GEN_ENTROPY_DISK || p->generator > TRA_GEN_WINDOW_1D)
     return fail(TRA_ERR_INVALID_ARG, "unknown generator");
+  if (p->generator == TRA_GEN_WINDOW_1D) {
+    if ((s->W + p->tile_w - 1) / p->tile_w > 64)
+      return fail(TRA_ERR_SHAPE, "the 1-D window generator builds its tile lists for at most 64 tile columns");
+    if (p->vote_threshold > 1) return fail(TRA_ERR_INVALID_ARG, "the 1-D window generator takes vote_threshold 1");
+  }
   if (p->vote_threshold < 1 || p->vote_threshold > p->tile_h * p->tile_w * p->tile_h * p->tile_w)
     return fail(TRA_ERR_INVALID_ARG, "vote_threshold must lie in [1, (tile_h*tile_w)^2]");
   if (p->block_mask != 0 && p->block_mask != 1) return fail(TRA_ERR_INVALID_ARG, "block_mask must be 0 or 1");
-  if (p->generator != TRA_GEN_ENTROPY_DISK && !(p->radius_override >= 0.0))
+  if ((p->generator == TRA_GEN_MANHATTAN || p->generator == TRA_GEN_RADIAL) && !(p->radius_override >= 0.0))
     return fail(TRA_ERR_INVALID_ARG, "the Manhattan and Radial generators take their radius from radius_override (>= 0)");
   const int T = s->T;
   const double phi = p->decay;
@@ -107,7 +112,22 @@ tra_status check_params(const tra_shape* s, const tra_params* p, Table* tab) {
     for (int dl = -(T - 1); dl <= T - 1; ++dl) S += std::pow(phi, 2.0 * std::abs(dl));
     for (int k = t.k_lo; k <= t.k_hi; ++k) t.r0sq.push_back(std::exp(k / q) / (M_PI * S));
   }
-  if (t.r0sq.back() >= 1073741824.0) return fail(TRA_ERR_INVALID_ARG, "radius^2 must stay below 2^30");
+  if (p->generator != TRA_GEN_WINDOW_1D && t.r0sq.back() >= 1073741824.0)
+    return fail(TRA_ERR_INVALID_ARG, "radius^2 must stay below 2^30");
+  // 1-D window half-widths: rho = floor((B - 1)/2) for budget B = exp(k/q), so
+  // that the window of 2 rho + 1 tokens holds the budget (floor(r) under
+  // radius_override).
+  std::vector<int32_t> rho(t.n_levels, 0);
+  if (p->generator == TRA_GEN_WINDOW_1D) {
+    for (int r = 0; r < t.n_levels; ++r) {
+      const double x = p->radius_override >= 0.0
+                           ? std::floor(p->radius_override)
+                           : std::floor((std::exp((t.k_lo + r) / static_cast<double>(p->levels_per_nat)) - 1.0) / 2.0);
+      if (!(x < 16777216.0)) return fail(TRA_ERR_INVALID_ARG, "1-D window half-width must stay below 2^24");
+      rho[r] = static_cast<int32_t>(x);
+    }
+  }
+  const int64_t HW = static_cast<int64_t>(s->H) * s->W;
   if (static_cast<int64_t>(t.n_levels) * T > (int64_t(1) << 22))
     return fail(TRA_ERR_INVALID_ARG, "radius table too large");
   t.r2.resize(static_cast<size_t>(t.n_levels) * T);
@@ -116,6 +136,14 @@ tra_status check_params(const tra_shape* s, const tra_params* p, Table* tab) {
     int dm = 0;
     for (int dl = 0; dl < T; ++dl) {
       int32_t v;
+      if (p->generator == TRA_GEN_WINDOW_1D) {
+        // The same rho in every column; frames beyond reach are marked by dmax
+        // (the nearest tokens of frames dl apart are dl*H*W - (H*W - 1) apart).
+        v = rho[r];
+        if (dl * HW - (HW - 1) <= rho[r]) dm = dl;
+        t.r2[static_cast<size_t>(r) * T + dl] = v;
+        continue;
+      }
       if (p->generator == TRA_GEN_MANHATTAN) {
         // L1 ball |dt| + |dh| + |dw| <= R: frame dl holds the 2D L1 disk of radius R - dl.
         v = static_cast<int32_t>(std::floor(p->radius_override)) - dl;
@@ -150,6 +178,12 @@ tra_status check_params(const tra_shape* s, const tra_params* p, Table* tab) {
 }
 
 size_t dtype_size(int dtype) { return dtype == TRA_BF16 ? 2 : 4; }
+
+int metric_of(const tra_params& p) {
+  if (p.generator == TRA_GEN_MANHATTAN) return tra::METRIC_L1;
+  if (p.generator == TRA_GEN_WINDOW_1D) return tra::METRIC_WINDOW;
+  return tra::METRIC_L2;
+}
 
 }  // namespace
 
@@ -229,8 +263,14 @@ tra_status build(tra_plan* p, const void* q, const void* k, const float* Hin, hi
   } else {
     TRA_HIP(tra::launch_fill_levels(p->lv, p->H, p->n_queries, st));
   }
-  TRA_HIP(tra::launch_csr_runs(p->params.generator == TRA_GEN_MANHATTAN, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, p->DM, p->counts,
-                               p->runs, p->rowwin, st));
+  const bool window = p->params.generator == TRA_GEN_WINDOW_1D;
+  if (window) {
+    TRA_HIP(tra::launch_window_csr(false, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, nullptr,
+                                   p->counts, nullptr, st));
+  } else {
+    TRA_HIP(tra::launch_csr_runs(p->params.generator == TRA_GEN_MANHATTAN, p->lv, p->r2, p->dmax, s.T, p->row_base,
+                                 p->BH, p->tiles, p->DM, p->counts, p->runs, p->rowwin, st));
+  }
   TRA_HIP(tra::launch_scan(p->counts, p->n_rows, p->row_ptr, p->totals, st));
   TRA_HIP(hipMemcpyAsync(p->totals_host, p->totals, 3 * sizeof(int64_t), hipMemcpyDeviceToHost, st));
   TRA_HIP(hipStreamSynchronize(st));
@@ -245,7 +285,12 @@ tra_status build(tra_plan* p, const void* q, const void* k, const float* Hin, hi
     TRA_HIP(hipMalloc(&p->col_idx, cap * sizeof(int32_t)));
     p->col_cap = cap;
   }
-  TRA_HIP(tra::launch_csr_expand(p->BH, p->tiles, p->DM, p->runs, p->rowwin, p->row_ptr, p->col_idx, st));
+  if (window) {
+    TRA_HIP(tra::launch_window_csr(true, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, p->row_ptr,
+                                   p->counts, p->col_idx, st));
+  } else {
+    TRA_HIP(tra::launch_csr_expand(p->BH, p->tiles, p->DM, p->runs, p->rowwin, p->row_ptr, p->col_idx, st));
+  }
   const int theta = p->params.vote_threshold;
   const bool l1 = p->params.generator == TRA_GEN_MANHATTAN;
   if (theta > 1) {
@@ -291,12 +336,20 @@ tra_status build(tra_plan* p, const void* q, const void* k, const float* Hin, hi
       TRA_HIP(hipMalloc(&p->glist, p->col_cap * 2 * sizeof(int32_t)));
       p->glist_cap = p->col_cap;
     }
-    const int32_t* frp = theta > 1 ? p->row_ptr : nullptr;
-    TRA_HIP(tra::launch_group_lists(false, p->BH, p->tiles, p->DM, p->runs, p->rowwin, frp, p->col_idx, nullptr,
-                                    nullptr, p->glen, st));
-    TRA_HIP(tra::launch_scan(p->glen, p->n_groups, p->gptr, p->totals + 4, st));
-    TRA_HIP(tra::launch_group_lists(true, p->BH, p->tiles, p->DM, p->runs, p->rowwin, frp, p->col_idx, p->gptr,
-                                    p->glist, p->glen, st));
+    if (window) {
+      TRA_HIP(tra::launch_window_groups(false, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, nullptr,
+                                        nullptr, p->glen, st));
+      TRA_HIP(tra::launch_scan(p->glen, p->n_groups, p->gptr, p->totals + 4, st));
+      TRA_HIP(tra::launch_window_groups(true, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, p->gptr,
+                                        p->glist, p->glen, st));
+    } else {
+      const int32_t* frp = theta > 1 ? p->row_ptr : nullptr;
+      TRA_HIP(tra::launch_group_lists(false, p->BH, p->tiles, p->DM, p->runs, p->rowwin, frp, p->col_idx, nullptr,
+                                      nullptr, p->glen, st));
+      TRA_HIP(tra::launch_scan(p->glen, p->n_groups, p->gptr, p->totals + 4, st));
+      TRA_HIP(tra::launch_group_lists(true, p->BH, p->tiles, p->DM, p->runs, p->rowwin, frp, p->col_idx, p->gptr,
+                                      p->glist, p->glen, st));
+    }
   }
   return TRA_OK;
 }
@@ -375,7 +428,7 @@ tra_status create_plan(const tra_shape* shape, const tra_params* params, Table&&
     TRA_HIP_P(hipMalloc(&p->kept_votes, sizeof(unsigned long long)));
   }
   for (int32_t dm : p->table.dmax) p->DM = std::max(p->DM, static_cast<int>(dm));
-  {
+  if (params->generator != TRA_GEN_WINDOW_1D) {  // the window builds its lists without runs
     const int64_t run_entries = p->n_rows * (2 * p->DM + 1) * p->tiles.nh;
     if (run_entries > (int64_t(1) << 32)) return fin(fail(TRA_ERR_SHAPE, "tile-list run buffer too large"));
     TRA_HIP_P(hipMalloc(&p->runs, run_entries * sizeof(int32_t)));
@@ -510,7 +563,7 @@ tra_status tra_attention(const tra_plan* plan, const void* q, const void* k, con
   const tra_shape& s = plan->shape;
   const tra::RadiusTable tab{plan->r2, plan->dmax, plan->r2c, plan->r2off,
                              static_cast<int>(plan->table.r2c.size()), s.T,
-                             plan->params.generator == TRA_GEN_MANHATTAN};
+                             metric_of(plan->params)};
   TRA_HIP(tra::launch_attention(s.dtype, s.head_dim, q, k, v, o, plan->lv, tab, plan->row_base,
                                 plan->BH, plan->tiles, plan->row_ptr, plan->col_idx,
                                 plan->gptr, plan->glist, plan->glen, plan->params.block_mask != 0,
@@ -567,6 +620,25 @@ tra_status tra_plan_export(const tra_plan* plan, int16_t* levels, float* entropy
   return TRA_OK;
 }
 
+tra_status tra_plan_export_groups(const tra_plan* plan, int64_t* n_groups, int64_t* n_entries, int32_t* gptr,
+                                  int32_t* glen, int32_t* glist, void* stream) {
+  if (!plan) return fail(TRA_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->shape.dtype != TRA_BF16) return fail(TRA_ERR_DTYPE, "group lists exist for bf16 plans only");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  TRA_HIP(hipStreamSynchronize(hs));
+  int32_t last[2] = {0, 0};
+  TRA_HIP(hipMemcpy(&last[0], plan->gptr + plan->n_groups - 1, sizeof(int32_t), hipMemcpyDeviceToHost));
+  TRA_HIP(hipMemcpy(&last[1], plan->glen + plan->n_groups - 1, sizeof(int32_t), hipMemcpyDeviceToHost));
+  const int64_t entries = static_cast<int64_t>(last[0]) + last[1];
+  if (n_groups) *n_groups = plan->n_groups;
+  if (n_entries) *n_entries = entries;
+  if (gptr) TRA_HIP(hipMemcpy(gptr, plan->gptr, plan->n_groups * sizeof(int32_t), hipMemcpyDeviceToHost));
+  if (glen) TRA_HIP(hipMemcpy(glen, plan->glen, plan->n_groups * sizeof(int32_t), hipMemcpyDeviceToHost));
+  if (glist && entries > 0)
+    TRA_HIP(hipMemcpy(glist, plan->glist, entries * 2 * sizeof(int32_t), hipMemcpyDeviceToHost));
+  return TRA_OK;
+}
+
 tra_status tra_plan_stats(const tra_plan* plan, int64_t* retained, int64_t* listed, void* stream) {
   if (!plan) return fail(TRA_ERR_INVALID_ARG, "plan is NULL");
   hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -575,7 +647,7 @@ tra_status tra_plan_stats(const tra_plan* plan, int64_t* retained, int64_t* list
   unsigned long long host[2] = {0, 0};
   hipError_t e = hipMemsetAsync(dev, 0, 2 * sizeof(unsigned long long), hs);
   if (e == hipSuccess)
-    e = tra::launch_stats(plan->params.generator == TRA_GEN_MANHATTAN, plan->lv, plan->r2, plan->shape.T, plan->row_base, plan->BH, plan->tiles,
+    e = tra::launch_stats(metric_of(plan->params), plan->lv, plan->r2, plan->shape.T, plan->row_base, plan->BH, plan->tiles,
                           plan->row_ptr, plan->col_idx, dev, hs);
   if (e == hipSuccess) e = hipMemcpyAsync(host, dev, sizeof(host), hipMemcpyDeviceToHost, hs);
   if (e == hipSuccess) e = hipStreamSynchronize(hs);

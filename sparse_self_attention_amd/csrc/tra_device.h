@@ -84,6 +84,21 @@ __device__ __forceinline__ int wave_max_u(int v) {
   return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
              max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
+// Wave-wide OR with a wave-uniform result (same DPP pattern).
+__device__ __forceinline__ uint32_t wave_or_u(uint32_t v) {
+  v |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false));
+  v |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false));
+  v |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x124, 0xF, 0xF, false));
+  v |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x128, 0xF, 0xF, false));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 0) |
+                               __builtin_amdgcn_readlane(static_cast<int>(v), 16) |
+                               __builtin_amdgcn_readlane(static_cast<int>(v), 32) |
+                               __builtin_amdgcn_readlane(static_cast<int>(v), 48));
+}
+__device__ __forceinline__ uint64_t wave_or_u64(uint64_t v) {
+  return (static_cast<uint64_t>(wave_or_u(static_cast<uint32_t>(v >> 32))) << 32) |
+         wave_or_u(static_cast<uint32_t>(v));
+}
 // Wave-wide sum with a wave-uniform result (same DPP pattern: pairs, quads,
 // then rotations by 4 and 8 inside each row of 16).
 __device__ __forceinline__ int wave_sum_u(int v) {

@@ -37,8 +37,13 @@ struct RadiusTable {
   const int32_t* r2off;
   int n_r2c;
   int T;
-  bool l1;  // entries are L1 radii (Manhattan mask) instead of squared radii
+  int metric;  // METRIC_*: how the entries are compared with key distances
 };
+
+// Mask metrics.  L2: entries are squared radii of a disk per frame; L1:
+// entries are L1 radii (Manhattan); WINDOW: every entry is the half-width rho
+// of a window along the raster order (|n_i - n_j| <= rho).
+constexpr int METRIC_L2 = 0, METRIC_L1 = 1, METRIC_WINDOW = 2;
 
 struct EntropyArgs {
   double a, c;
@@ -90,6 +95,15 @@ hipError_t launch_group_lists(bool fill, int BH, const Grid& tiles, int DM, cons
 // Token votes per CSR entry (votes, int16 per entry), per-row count of entries
 // with at least theta votes (counts2) and the sum of their votes (added to
 // *kept_votes); then the filtered CSR (row_ptr2 = scan of counts2).
+// Tile lists of the 1-D window mask from per-(frame, tile row) column masks
+// (tiles.nw <= 64): CSR counts (fill = false) or columns from row_ptr (fill =
+// true); group lists with membership bits (count into glen, or fill from gptr).
+hipError_t launch_window_csr(bool fill, const int16_t* lv, const int32_t* r2, const int32_t* dmax, int T,
+                             int row_base, int BH, const Grid& tiles, const int32_t* row_ptr, int32_t* counts,
+                             int32_t* col_idx, hipStream_t s);
+hipError_t launch_window_groups(bool fill, const int16_t* lv, const int32_t* r2, const int32_t* dmax, int T,
+                                int row_base, int BH, const Grid& tiles, const int32_t* gptr, int32_t* glist,
+                                int32_t* glen, hipStream_t s);
 hipError_t launch_votes(bool l1, const int16_t* lv, const int32_t* r2, const int32_t* dmax, int T, int row_base,
                         int BH, const Grid& tiles, const int32_t* row_ptr, const int32_t* col_idx, int theta,
                         int16_t* votes, int32_t* counts2, unsigned long long* kept_votes, hipStream_t s);
@@ -112,7 +126,7 @@ hipError_t launch_dense(int dtype, int d, const void* q, const void* k, const vo
 hipError_t launch_levels_from_entropy(const float* Hin, int64_t n, const EntropyArgs& ea, float* Hout,
                                       int16_t* lv, hipStream_t s);
 
-hipError_t launch_stats(bool l1, const int16_t* lv, const int32_t* r2, int T, int row_base, int BH,
+hipError_t launch_stats(int metric, const int16_t* lv, const int32_t* r2, int T, int row_base, int BH,
                         const Grid& tiles, const int32_t* row_ptr, const int32_t* col_idx,
                         unsigned long long* out2, hipStream_t s);
 

@@ -644,6 +644,132 @@ __global__ __launch_bounds__(256) void vote_compact_kernel(int64_t n_rows, const
   }
 }
 
+// ---------------------------------------------------------------------------
+// Tile lists of the 1-D window mask (key j kept iff |n_i - n_j| <= rho along
+// the raster order).  A query's window touches, in one key tile row of one
+// frame, a prefix, a middle run and/or a suffix of the tile columns, so the
+// lists are built from 64-bit column masks (at most 64 tile columns).
+// ---------------------------------------------------------------------------
+// Tile columns of (frame tk, tile row ktr) that the head-local raster range
+// [lo, hi] touches.
+__device__ __forceinline__ uint64_t window_tile_mask(int lo, int hi, int tk, int ktr, const Grid& g) {
+  const int F = tk * g.H * g.W;
+  const int r0 = ktr * g.th, r1 = min(r0 + g.th, g.H) - 1;
+  const int a = max(lo - F, r0 * g.W), b = min(hi - F, r1 * g.W + g.W - 1);
+  if (a > b) return 0;
+  const int ra = a / g.W, rb = b / g.W;
+  const int ca = a - ra * g.W, cb = b - rb * g.W;
+  auto cols = [&](int c0, int c1) {
+    const int t0 = c0 / g.tw, t1 = c1 / g.tw;
+    return ((2ull << t1) - 1ull) & ~((1ull << t0) - 1ull);
+  };
+  if (ra == rb) return cols(ca, cb);
+  if (rb > ra + 1) return cols(0, g.W - 1);
+  return cols(ca, g.W - 1) | cols(0, cb);
+}
+
+// Per query lane: the window [lo, hi] (lo > hi when the query is outside the
+// grid) and the largest frame distance it reaches.
+struct WindowQuery {
+  int lo, hi, dm;
+};
+__device__ __forceinline__ WindowQuery window_query(const int16_t* __restrict__ lv, const int32_t* __restrict__ r2,
+                                                    const int32_t* __restrict__ dmax, int T, int row_base,
+                                                    const Grid& g, int bh, int tq, int hq, int wq) {
+  WindowQuery w{1, 0, -1};
+  if (hq < g.H && wq < g.W) {
+    const int N = g.T * g.H * g.W;
+    const int n = (tq * g.H + hq) * g.W + wq;
+    const int trow = lv[static_cast<size_t>(bh) * N + n] - row_base;
+    const int rho = r2[trow * T];
+    w.lo = max(0, n - rho);
+    w.hi = min(N - 1, n + rho);
+    w.dm = dmax[trow];
+  }
+  return w;
+}
+
+// CSR rows: FILL = false writes each row's count, FILL = true its key tiles
+// from row_ptr[row] on.  One wave per query tile, lane = query.
+template <bool FILL>
+__global__ __launch_bounds__(256) void window_csr_kernel(const int16_t* __restrict__ lv, const int32_t* __restrict__ r2,
+                                                        const int32_t* __restrict__ dmax, int T, int row_base, Grid g,
+                                                        int64_t n_rows, const int32_t* __restrict__ row_ptr,
+                                                        int32_t* __restrict__ counts, int32_t* __restrict__ col_idx) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= n_rows) return;  // wave-uniform
+  const int bh = static_cast<int>(row / g.count), tile = static_cast<int>(row % g.count);
+  const int tq = tile / g.per_frame, rem = tile % g.per_frame;
+  const WindowQuery wq = window_query(lv, r2, dmax, T, row_base, g, bh, tq, (rem / g.nw) * g.th + (lane >> 3),
+                                     (rem % g.nw) * g.tw + (lane & 7));
+  const int dmw = wave_max_u(wq.dm);
+  const int t_lo = max(0, tq - dmw), t_hi = min(T - 1, tq + dmw);
+  int out = FILL ? row_ptr[row] : 0;
+  for (int tk = t_lo; tk <= t_hi; ++tk) {
+    for (int ktr = 0; ktr < g.nh; ++ktr) {
+      const uint64_t M = wave_or_u64(window_tile_mask(wq.lo, wq.hi, tk, ktr, g));
+      if (FILL && lane < g.nw && ((M >> lane) & 1ull))
+        col_idx[out + __popcll(M & ((1ull << lane) - 1ull))] = (tk * g.nh + ktr) * g.nw + lane;
+      out += __popcll(M);
+    }
+  }
+  if (!FILL && lane == 0) counts[row] = out;
+}
+
+// Group lists (GROUP_ROWS x 2 query tiles, the entries and membership bits of
+// group_list_kernel).  One wave per group.
+template <bool FILL>
+__global__ __launch_bounds__(256) void window_group_kernel(const int16_t* __restrict__ lv, const int32_t* __restrict__ r2,
+                                                          const int32_t* __restrict__ dmax, int T, int row_base, Grid g,
+                                                          int ngh, int ngw, int64_t n_groups,
+                                                          const int32_t* __restrict__ gptr, int2* __restrict__ glist,
+                                                          int32_t* __restrict__ glen) {
+  const int lane = threadIdx.x & 63;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (gid >= n_groups) return;  // wave-uniform
+  const int64_t per_head = static_cast<int64_t>(g.T) * ngh * ngw;
+  const int bh = static_cast<int>(gid / per_head);
+  const int grem = static_cast<int>(gid % per_head);
+  const int gc = grem % ngw, gr = (grem / ngw) % ngh, tq = grem / (ngw * ngh);
+  constexpr int NR = 2 * GROUP_ROWS;
+  WindowQuery wq[NR];
+  int dm = -1;
+#pragma unroll
+  for (int m = 0; m < NR; ++m) {
+    const int tr = gr * GROUP_ROWS + (m >> 1), tc = 2 * gc + (m & 1);
+    wq[m] = WindowQuery{1, 0, -1};
+    if (tr < g.nh && tc < g.nw)
+      wq[m] = window_query(lv, r2, dmax, T, row_base, g, bh, tq, tr * g.th + (lane >> 3), tc * g.tw + (lane & 7));
+    dm = max(dm, wq[m].dm);
+  }
+  const int dmw = wave_max_u(dm);
+  const int t_lo = max(0, tq - dmw), t_hi = min(T - 1, tq + dmw);
+  int64_t out = FILL ? gptr[gid] : 0;
+  const int64_t beg = out;
+  for (int tk = t_lo; tk <= t_hi; ++tk) {
+    for (int ktr = 0; ktr < g.nh; ++ktr) {
+      uint64_t M[NR], U = 0;
+#pragma unroll
+      for (int m = 0; m < NR; ++m) {
+        M[m] = wave_or_u64(window_tile_mask(wq[m].lo, wq[m].hi, tk, ktr, g));
+        U |= M[m];
+      }
+      if (FILL && lane < g.nw && ((U >> lane) & 1ull)) {
+        int mb = 0;
+#pragma unroll
+        for (int m = 0; m < NR; ++m) mb |= ((M[m] >> lane) & 1ull) ? 1 << m : 0;
+        const int kr0 = ktr * g.th, kc0 = lane * g.tw;
+        const bool ragged = kr0 + g.th > g.H || kc0 + g.tw > g.W;
+        glist[out + __popcll(U & ((1ull << lane) - 1ull))] =
+            make_int2(tk | (mb << 16) | (ragged ? static_cast<int>(0x80000000u) : 0), kr0 | (kc0 << 16));
+      }
+      out += __popcll(U);
+    }
+  }
+  if (lane == 0) glen[gid] = static_cast<int32_t>(out - beg);
+}
+
 // Exclusive scan of per-row counts.  One workgroup of 1024 threads walks the
 // counts in tiles of 4096 (4 per thread, 16-byte loads): a thread's partial
 // sums, a wave scan of the thread totals, a scan of the 16 wave totals, and a
@@ -744,7 +870,7 @@ template <int D> struct AttnLds {
   static_assert(64 * KSTR % 1024 == 0 && 64 * VSTR % 1024 == 0, "tile must be whole segments");
 };
 
-template <int D, bool L1, bool BLOCK>
+template <int D, int METRIC, bool BLOCK>
 __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, const int16_t* __restrict__ lv,
@@ -791,6 +917,7 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
   const int hq = trq * 8 + 4 * (wave & 1) + (col >> 3);
   // This wave's query tile in the group's membership bits (see group_list_kernel).
   const int mbit = 1 << (2 * (wave >> 2) + ((wave >> 1) & 1));
+  [[maybe_unused]] const int nqh = (tq * g.H + hq) * g.W + wq;  // raster index (1-D window mask)
   const bool qvalid = tvalid && hq < g.H && wq < g.W;
   const size_t nq = (static_cast<size_t>(tq) * g.H + (qvalid ? hq : 0)) * g.W + (qvalid ? wq : 0);
   bf16x8 qf[KS];
@@ -997,6 +1124,7 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
   // rr <= 2^30 (radius tables stay below 2^30), so the differences below
   // stay inside int32.
   constexpr int COL_OUT = 0x40000001, ROW_OUT = -1;
+  constexpr int WIN_COL_OUT = 0x20000000, WIN_ROW_OUT = -0x20000000;
   // When `more`, the LDS DMA of the next tile (tn into nbuf) is issued once
   // the score MFMAs are in flight, so that the matrix unit works while the
   // DMA instructions wait to issue.
@@ -1007,12 +1135,26 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
     const int dwa = wq - t.kc0 - 4 * h;
     const int dha = hq - t.kr0;
     int dw2[4], rr[8];
+    [[maybe_unused]] int dn[8];
     if constexpr (BLOCK) {  // block-only mask: every key of a listed tile inside the grid
 #pragma unroll
       for (int b = 0; b < 4; ++b) dw2[b] = 0;
 #pragma unroll
       for (int a = 0; a < 8; ++a) rr[a] = 1;
-    } else if constexpr (L1) {
+    } else if constexpr (METRIC == METRIC_WINDOW) {
+      // 1-D window: key (a, b) is kept iff |x| <= rho, x = base - a*W - b the
+      // query's raster index minus the key's.  Upper bound: -b < rr[a]; lower
+      // bound: b < dn[a].
+      const int rho = delta <= tdmax ? tv : -1;
+      const int base = nqh - ((t.tk * g.H + t.kr0) * g.W + t.kc0 + 4 * h);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) dw2[b] = -b;
+#pragma unroll
+      for (int a = 0; a < 8; ++a) {
+        rr[a] = rho - base + a * g.W + 1;
+        dn[a] = rho + base - a * g.W + 1;
+      }
+    } else if constexpr (METRIC == METRIC_L1) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) dw2[b] = abs(dwa - b);
 #pragma unroll
@@ -1026,19 +1168,31 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
       for (int a = 1; a < 8; ++a) rr[a] = rr[a - 1] + 2 * dha - (2 * a - 1);
     }
     if (t.ragged) {  // tile at the bottom/right edge of the grid (wave-uniform)
+      // The window's entries span up to 2^26 either side of zero, so its
+      // sentinels are +-2^29: their differences (up to 2^30) stay inside int32
+      // also where an out-of-grid row meets an out-of-grid column.
 #pragma unroll
       for (int b = 0; b < 4; ++b)
-        if (t.kc0 + 4 * h + b >= g.W) dw2[b] = COL_OUT;
+        if (t.kc0 + 4 * h + b >= g.W) dw2[b] = METRIC == METRIC_WINDOW ? WIN_COL_OUT : COL_OUT;
 #pragma unroll
       for (int a = 0; a < 8; ++a)
-        if (t.kr0 + a >= g.H) rr[a] = ROW_OUT;
+        if (t.kr0 + a >= g.H) rr[a] = METRIC == METRIC_WINDOW ? WIN_ROW_OUT : ROW_OUT;
     }
     const int mindw = min(min(dw2[0], dw2[1]), min(dw2[2], dw2[3]));
     bool doq[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int* r = rr + 4 * blk;
-      doq[blk] = (t.member & mbit) && __any(mindw < max(max(r[0], r[1]), max(r[2], r[3])));
+      if constexpr (METRIC == METRIC_WINDOW && !BLOCK) {
+        // Some b in [0, 3] with -b < rr[a] and b < dn[a] (edge columns count;
+        // their masks drop them).
+        bool any = false;
+#pragma unroll
+        for (int a = 4 * blk; a < 4 * blk + 4; ++a) any |= max(0, 1 - rr[a]) <= min(3, dn[a] - 1);
+        doq[blk] = (t.member & mbit) && __any(any);
+      } else {
+        doq[blk] = (t.member & mbit) && __any(mindw < max(max(r[0], r[1]), max(r[2], r[3])));
+      }
     }
     // Sign bytes of the two differences -> 16-bit keep masks of block blk.
     auto masks = [&](int blk, uint32_t* msk) {
@@ -1050,7 +1204,12 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
         const int ra = rr[4 * blk + (x >> 1)];
-        const int t0 = dw2[2 * (x & 1)] - ra, t1 = dw2[2 * (x & 1) + 1] - ra;
+        int t0 = dw2[2 * (x & 1)] - ra, t1 = dw2[2 * (x & 1) + 1] - ra;
+        if constexpr (METRIC == METRIC_WINDOW && !BLOCK) {
+          const int da = dn[4 * blk + (x >> 1)];
+          t0 &= 2 * (x & 1) - da;
+          t1 &= 2 * (x & 1) + 1 - da;
+        }
         msk[x] = __builtin_amdgcn_perm(static_cast<uint32_t>(t1), static_cast<uint32_t>(t0), 0x0B0B0909u);
       }
     };
@@ -1125,7 +1284,7 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
 }
 
 // fp32 inputs: one thread per query, K/V tiles in LDS, fp32 online softmax.
-template <int D, bool L1, bool BLOCK>
+template <int D, int METRIC, bool BLOCK>
 __global__ __launch_bounds__(64) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, const int16_t* __restrict__ lv, const int32_t* __restrict__ r2,
@@ -1175,7 +1334,15 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
       const int kr = kr0 + (kk >> 3), kc = kc0 + (kk & 7);
       const int dh = hq - kr, dw = wq - kc;
       if (kr >= g.H || kc >= g.W) continue;
-      if (!BLOCK && (thr < 0 || (L1 ? abs(dh) + abs(dw) : dh * dh + dw * dw) > thr)) continue;
+      if (!BLOCK) {
+        if (thr < 0) continue;
+        if (METRIC == METRIC_WINDOW) {
+          const long long dn = static_cast<long long>(nq) - ((static_cast<long long>(tk) * g.H + kr) * g.W + kc);
+          if (dn > thr || -dn > thr) continue;
+        } else if ((METRIC == METRIC_L1 ? abs(dh) + abs(dw) : dh * dh + dw * dw) > thr) {
+          continue;
+        }
+      }
       float s = 0.f;
 #pragma unroll
       for (int dd = 0; dd < D; ++dd) s = fmaf(qr[dd], k_lds[kk][dd], s);
@@ -1204,7 +1371,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
 // ---------------------------------------------------------------------------
 // Exact pair counts.
 // ---------------------------------------------------------------------------
-template <bool L1>
+template <int METRIC>
 __global__ __launch_bounds__(256) void retained_kernel(const int16_t* __restrict__ lv,
                                                       const int32_t* __restrict__ r2, int T,
                                                       int row_base, Grid g, int64_t n_total,
@@ -1218,13 +1385,19 @@ __global__ __launch_bounds__(256) void retained_kernel(const int16_t* __restrict
     const int t = static_cast<int>(n / (g.H * g.W)), hh = static_cast<int>((n / g.W) % g.H),
               ww = static_cast<int>(n % g.W);
     const int32_t* row = r2 + (lv[i] - row_base) * T;
-    for (int tk = 0; tk < T; ++tk) {
-      const int thr = row[tk > t ? tk - t : t - tk];
-      if (thr < 0) continue;
-      const int rad = mask_reach<L1>(thr);
-      for (int hk = max(0, hh - rad); hk <= min(g.H - 1, hh + rad); ++hk) {
-        const int a = mask_half_width<L1>(thr, hk - hh);
-        cnt += min(g.W - 1, ww + a) - max(0, ww - a) + 1;
+    if (METRIC == METRIC_WINDOW) {
+      const int64_t rho = row[0];
+      cnt = static_cast<unsigned long long>(min(N - 1, n + rho) - max(int64_t(0), n - rho) + 1);
+    } else {
+      constexpr bool L1 = METRIC == METRIC_L1;
+      for (int tk = 0; tk < T; ++tk) {
+        const int thr = row[tk > t ? tk - t : t - tk];
+        if (thr < 0) continue;
+        const int rad = mask_reach<L1>(thr);
+        for (int hk = max(0, hh - rad); hk <= min(g.H - 1, hh + rad); ++hk) {
+          const int a = mask_half_width<L1>(thr, hk - hh);
+          cnt += min(g.W - 1, ww + a) - max(0, ww - a) + 1;
+        }
       }
     }
   }
@@ -1356,6 +1529,33 @@ hipError_t launch_group_lists(bool fill, int BH, const Grid& tiles, int DM, cons
   return hipGetLastError();
 }
 
+hipError_t launch_window_csr(bool fill, const int16_t* lv, const int32_t* r2, const int32_t* dmax, int T,
+                             int row_base, int BH, const Grid& tiles, const int32_t* row_ptr, int32_t* counts,
+                             int32_t* col_idx, hipStream_t s) {
+  const int64_t n_rows = static_cast<int64_t>(BH) * tiles.count;
+  const unsigned grid = static_cast<unsigned>((n_rows + 3) / 4);
+  if (fill)
+    window_csr_kernel<true><<<grid, 256, 0, s>>>(lv, r2, dmax, T, row_base, tiles, n_rows, row_ptr, counts, col_idx);
+  else
+    window_csr_kernel<false><<<grid, 256, 0, s>>>(lv, r2, dmax, T, row_base, tiles, n_rows, row_ptr, counts, col_idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_window_groups(bool fill, const int16_t* lv, const int32_t* r2, const int32_t* dmax, int T,
+                                int row_base, int BH, const Grid& tiles, const int32_t* gptr, int32_t* glist,
+                                int32_t* glen, hipStream_t s) {
+  const int ngh = (tiles.nh + GROUP_ROWS - 1) / GROUP_ROWS, ngw = (tiles.nw + 1) / 2;
+  const int64_t n_groups = static_cast<int64_t>(BH) * tiles.T * ngh * ngw;
+  const unsigned grid = static_cast<unsigned>((n_groups + 3) / 4);
+  if (fill)
+    window_group_kernel<true><<<grid, 256, 0, s>>>(lv, r2, dmax, T, row_base, tiles, ngh, ngw, n_groups, gptr,
+                                                   reinterpret_cast<int2*>(glist), glen);
+  else
+    window_group_kernel<false><<<grid, 256, 0, s>>>(lv, r2, dmax, T, row_base, tiles, ngh, ngw, n_groups, gptr,
+                                                    reinterpret_cast<int2*>(glist), glen);
+  return hipGetLastError();
+}
+
 hipError_t launch_votes(bool l1, const int16_t* lv, const int32_t* r2, const int32_t* dmax, int T, int row_base,
                         int BH, const Grid& tiles, const int32_t* row_ptr, const int32_t* col_idx, int theta,
                         int16_t* votes, int32_t* counts2, unsigned long long* kept_votes, hipStream_t s) {
@@ -1399,14 +1599,17 @@ hipError_t launch_attention(int dtype, int d, const void* q, const void* k, cons
                                                                  tab.n_r2c, row_base, tiles, ngh, ngw, ng, gptr,     \
                                                                  reinterpret_cast<const int2*>(glist), glen)
     if (block_mask) {
-      if (d == 128) TRA_ATTN(128, false, true);
-      else TRA_ATTN(64, false, true);
-    } else if (tab.l1) {
-      if (d == 128) TRA_ATTN(128, true, false);
-      else TRA_ATTN(64, true, false);
+      if (d == 128) TRA_ATTN(128, METRIC_L2, true);
+      else TRA_ATTN(64, METRIC_L2, true);
+    } else if (tab.metric == METRIC_L1) {
+      if (d == 128) TRA_ATTN(128, METRIC_L1, false);
+      else TRA_ATTN(64, METRIC_L1, false);
+    } else if (tab.metric == METRIC_WINDOW) {
+      if (d == 128) TRA_ATTN(128, METRIC_WINDOW, false);
+      else TRA_ATTN(64, METRIC_WINDOW, false);
     } else {
-      if (d == 128) TRA_ATTN(128, false, false);
-      else TRA_ATTN(64, false, false);
+      if (d == 128) TRA_ATTN(128, METRIC_L2, false);
+      else TRA_ATTN(64, METRIC_L2, false);
     }
 #undef TRA_ATTN
   } else {
@@ -1417,14 +1620,17 @@ hipError_t launch_attention(int dtype, int d, const void* q, const void* k, cons
 #define TRA_ATTN32(DD, M, B) \
   attn_f32_kernel<DD, M, B><<<rows, 64, 0, s>>>(qq, kk, vv, oo, lv, r2, row_base, tiles.T, tiles, row_ptr, col_idx)
     if (block_mask) {
-      if (d == 128) TRA_ATTN32(128, false, true);
-      else TRA_ATTN32(64, false, true);
-    } else if (tab.l1) {
-      if (d == 128) TRA_ATTN32(128, true, false);
-      else TRA_ATTN32(64, true, false);
+      if (d == 128) TRA_ATTN32(128, METRIC_L2, true);
+      else TRA_ATTN32(64, METRIC_L2, true);
+    } else if (tab.metric == METRIC_L1) {
+      if (d == 128) TRA_ATTN32(128, METRIC_L1, false);
+      else TRA_ATTN32(64, METRIC_L1, false);
+    } else if (tab.metric == METRIC_WINDOW) {
+      if (d == 128) TRA_ATTN32(128, METRIC_WINDOW, false);
+      else TRA_ATTN32(64, METRIC_WINDOW, false);
     } else {
-      if (d == 128) TRA_ATTN32(128, false, false);
-      else TRA_ATTN32(64, false, false);
+      if (d == 128) TRA_ATTN32(128, METRIC_L2, false);
+      else TRA_ATTN32(64, METRIC_L2, false);
     }
 #undef TRA_ATTN32
   }
@@ -1450,15 +1656,17 @@ hipError_t launch_level_diff(const int16_t* a, const int16_t* b, int64_t n, unsi
   return hipGetLastError();
 }
 
-hipError_t launch_stats(bool l1, const int16_t* lv, const int32_t* r2, int T, int row_base, int BH,
+hipError_t launch_stats(int metric, const int16_t* lv, const int32_t* r2, int T, int row_base, int BH,
                         const Grid& tiles, const int32_t* row_ptr, const int32_t* col_idx,
                         unsigned long long* out2, hipStream_t s) {
   const int64_t nq = static_cast<int64_t>(BH) * tiles.T * tiles.H * tiles.W;
   const unsigned nb = static_cast<unsigned>((nq + 255) / 256);
-  if (l1)
-    retained_kernel<true><<<nb, 256, 0, s>>>(lv, r2, T, row_base, tiles, nq, out2);
+  if (metric == METRIC_L1)
+    retained_kernel<METRIC_L1><<<nb, 256, 0, s>>>(lv, r2, T, row_base, tiles, nq, out2);
+  else if (metric == METRIC_WINDOW)
+    retained_kernel<METRIC_WINDOW><<<nb, 256, 0, s>>>(lv, r2, T, row_base, tiles, nq, out2);
   else
-    retained_kernel<false><<<nb, 256, 0, s>>>(lv, r2, T, row_base, tiles, nq, out2);
+    retained_kernel<METRIC_L2><<<nb, 256, 0, s>>>(lv, r2, T, row_base, tiles, nq, out2);
   const int64_t nr = static_cast<int64_t>(BH) * tiles.count;
   listed_kernel<<<static_cast<unsigned>((nr + 255) / 256), 256, 0, s>>>(tiles, nr, row_ptr, col_idx, out2 + 1);
   return hipGetLastError();

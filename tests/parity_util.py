@@ -101,3 +101,46 @@ def check_csr_properties(cfg, run):
     rows = np.arange(len(rp) - 1) % tiles.count
     own = [rows[r] in ci[rp[r]:rp[r + 1]] for r in range(0, len(rp) - 1, max(1, (len(rp) - 1) // 500))]
     assert all(own)
+
+
+def expected_group_lists(cfg, row_ptr, col_idx, bh):
+    """The bf16 kernel's group lists of head slice bh, derived from CSR rows:
+    per 2x2 group of query tiles, the ascending union of the members' key
+    tiles with member bits and edge flags (as the C ABI exports them)."""
+    tiles = O.Geometry(cfg.T, cfg.H, cfg.W, cfg.tile_h, cfg.tile_w)
+    nh, nw = tiles.nbh, tiles.nbw
+    ngh, ngw = (nh + 1) // 2, (nw + 1) // 2
+    out = {}
+    for t in range(cfg.T):
+        for gr in range(ngh):
+            for gc in range(ngw):
+                members = {}
+                for m in range(4):
+                    tr, tc = 2 * gr + (m >> 1), 2 * gc + (m & 1)
+                    if tr < nh and tc < nw:
+                        r = bh * tiles.count + (t * nh + tr) * nw + tc
+                        for K in col_idx[row_ptr[r]:row_ptr[r + 1]]:
+                            members[int(K)] = members.get(int(K), 0) | (1 << m)
+                ent = []
+                for K in sorted(members):
+                    tk, rem = divmod(K, tiles.per_frame)
+                    ktr, kc = divmod(rem, nw)
+                    kr0, kc0 = ktr * 8, kc * 8
+                    edge = kr0 + 8 > cfg.H or kc0 + 8 > cfg.W
+                    x = (tk | (members[K] << 16) | (1 << 31 if edge else 0)) - (1 << 32 if edge else 0)
+                    ent.append((x, kr0 | (kc0 << 16)))
+                gid = (bh * cfg.T + t) * ngh * ngw + gr * ngw + gc
+                out[gid] = np.array(ent, dtype=np.int64).reshape(-1, 2)
+    return out
+
+
+def check_group_lists(cfg, run, bh):
+    """Group lists of head slice bh equal those derived from the plan's CSR
+    (which the other checks compare with the oracle), entry for entry."""
+    gptr, glen, gl = run["plan"].export_groups()
+    exp = run["export"]
+    want = expected_group_lists(cfg, exp["row_ptr"].astype(np.int64), exp["col_idx"].astype(np.int64), bh)
+    for gid, ent in want.items():
+        got = gl[gptr[gid]:gptr[gid] + glen[gid]].astype(np.int64)
+        assert np.array_equal(got, ent), f"group {gid}: {got[:6].tolist()} vs {ent[:6].tolist()}"
+    return len(want)

@@ -69,7 +69,9 @@ def _validate(**kw):
     (dict(budget_max=1e12), "TRA_ERR_INVALID_ARG"),
     # one bf16 head of K would span 2^31 bytes or more (32-bit buffer offsets)
     (dict(grid=(2, 32767, 256), heads=1), "TRA_ERR_SHAPE"),
-    (dict(generator=3), "TRA_ERR_INVALID_ARG"),
+    (dict(generator=4), "TRA_ERR_INVALID_ARG"),
+    (dict(generator=3, grid=(2, 8, 520)), "TRA_ERR_SHAPE"),  # the 1-D window: at most 64 tile columns
+    (dict(generator=3, vote_threshold=2), "TRA_ERR_INVALID_ARG"),
     (dict(generator=1), "TRA_ERR_INVALID_ARG"),  # the static generators need radius_override >= 0
     (dict(generator=2, radius_override=-1.0), "TRA_ERR_INVALID_ARG"),
 ])
@@ -115,6 +117,13 @@ def test_radius_table_generators_match_oracle(gen, r, T):
     cfg = small_workload(T=T, radius_override=r, generator=gen)
     r2, _, k_lo = tra.radius_table((cfg.T, cfg.H, cfg.W), torch.bfloat16, 128, **cfg.params())
     assert k_lo == -1
+    assert np.array_equal(r2.astype(np.int64), O.radius_table(cfg.params(), cfg.T))
+
+
+@pytest.mark.parametrize("r,bmax,T", [(-1.0, 2048.0, 4), (-1.0, 9000.0, 21), (0.0, 2048.0, 3), (33.7, 2048.0, 5)])
+def test_radius_table_window_matches_oracle(r, bmax, T):
+    cfg = small_workload(T=T, radius_override=r, generator=3, budget_max=bmax)
+    r2, _, k_lo = tra.radius_table((cfg.T, cfg.H, cfg.W), torch.bfloat16, 128, **cfg.params())
     assert np.array_equal(r2.astype(np.int64), O.radius_table(cfg.params(), cfg.T))
 
 

@@ -42,7 +42,8 @@ class Workload:
     tile_h: int = 8
     tile_w: int = 8
     radius_override: float = -1.0
-    generator: int = 0  # 0: entropy -> disk (the method); 1: fixed Manhattan radius; 2: Radial static mask
+    generator: int = 0  # 0: entropy -> disk (the method); 1: fixed Manhattan radius; 2: Radial static mask;
+    #                     3: 1-D window along the raster order (ablation)
     vote_threshold: int = 1  # key tile listed when >= this many pairs are retained
     block_mask: int = 0  # 1: block-only mask (every key of a listed tile)
     seed: int = 0
