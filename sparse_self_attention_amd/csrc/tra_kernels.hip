@@ -908,15 +908,18 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
   const int gr = (grem % groups_per_frame) / ngw, gc = grem % ngw;
   const size_t N = static_cast<size_t>(g.T) * g.H * g.W;
 
-  // This wave: tile column gc*2 + (wave/2)%2, tile row gr*GROUP_ROWS + wave/4,
-  // query rows 4*(wave%2)..+3 of that tile; lane%32 -> query.
-  const int tc = gc * 2 + ((wave >> 1) & 1);
+  // This wave: tile row gr*GROUP_ROWS + wave/4, tile column gc*2 + wcol, query
+  // rows 4*(wave%2)..+3 of that tile; lane%32 -> query.  Waves w and w+4 share
+  // a SIMD; they take tiles of different rows and columns, so that a key tile
+  // listed by one row or one column of the group keeps every SIMD busy.
+  const int wcol = ((wave >> 1) ^ (wave >> 2)) & 1;
+  const int tc = gc * 2 + wcol;
   const int trq = gr * GROUP_ROWS + (wave >> 2);
   const bool tvalid = tc < g.nw && trq < g.nh;
   const int wq = tc * 8 + (col & 7);
   const int hq = trq * 8 + 4 * (wave & 1) + (col >> 3);
   // This wave's query tile in the group's membership bits (see group_list_kernel).
-  const int mbit = 1 << (2 * (wave >> 2) + ((wave >> 1) & 1));
+  const int mbit = 1 << (2 * (wave >> 2) + wcol);
   [[maybe_unused]] const int nqh = (tq * g.H + hq) * g.W + wq;  // raster index (1-D window mask)
   const bool qvalid = tvalid && hq < g.H && wq < g.W;
   const size_t nq = (static_cast<size_t>(tq) * g.H + (qvalid ? hq : 0)) * g.W + (qvalid ? wq : 0);
@@ -1038,22 +1041,18 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
   // values the PV product uses.
   //
   // Lazy rescale: the reference (shared by both lanes of a query) moves only
-  // when a score exceeds it by more than 2^8, so probabilities stay <= 256
-  // between moves.  The probabilities are formed against the current
-  // reference first; the cheap test on the unmasked maximum then decides
-  // (rarely) to move the reference by the exact masked maximum and form them
-  // again.
-  auto rowmax = [&](const f32x16& sacc) {
-    float mx = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
-#pragma unroll
-    for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sacc[i]), sacc[i + 1]);
-    return fmaxf(mx, sacc[15]);
-  };
+  // when the kept probabilities of a lane's block, formed against it, sum to
+  // more than 2^10 (so between moves every kept probability is <= 2^10), or
+  // when no reference is set yet.  The probabilities and their sum are formed
+  // first; the test on the sum (which the running sum needs anyway) then
+  // decides, rarely, to move the reference to the exact masked maximum and
+  // form them again.
   // P^T as the two 16-key B operands of the PV product; returns the block's
   // contribution to the running sum.
   auto probs = [&](const f32x16& sacc, const uint32_t* msk, bf16x8* pf) {
-    // With no kept key seen yet the reference is -inf: this block's
-    // probabilities are then all masked, and any value works.
+    // With no reference yet (-inf) the block is formed against 0 and then
+    // formed again once the reference has moved; if it cannot move (no key
+    // of the block is kept), every probability is masked.
     const float msub = mref == TRA_NEG_INF ? 0.f : mref;
     const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
     float ls[2] = {0.f, 0.f};
@@ -1071,8 +1070,8 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
     }
     return ls[0] + ls[1];
   };
-  // Moves the reference to the exact masked maximum of the block when that
-  // exceeds it by more than 2^8 (rare path).
+  // Moves the reference to the exact masked maximum of the block where that
+  // exceeds it (rare path).
   auto move_ref = [&](const f32x16& sacc, const uint32_t* msk) {
     float mx = TRA_NEG_INF;
 #pragma unroll
@@ -1083,7 +1082,7 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
                                     (__float_as_int(TRA_NEG_INF) & ~keep)));
     }
     mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(mx))));
-    if (__any(mx * c1 > mref + 8.f)) {
+    if (__any(mx * c1 > mref)) {
       const float mn = fmaxf(mref, mx * c1);
       const float alpha = mref == TRA_NEG_INF ? 0.f : __builtin_amdgcn_exp2f(mref - mn);
       lsum *= alpha;
@@ -1094,9 +1093,8 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
   };
   // softmax step of one block: returns P^T in pf and updates the running sum.
   auto softmax = [&](const f32x16& sacc, const uint32_t* msk, bf16x8* pf) {
-    const float mx = rowmax(sacc);
     float ls = probs(sacc, msk, pf);
-    if (__any(mx * c1 > mref + 8.f)) {
+    if (__any(!(ls <= 1024.f) || mref == TRA_NEG_INF)) {
       move_ref(sacc, msk);
       ls = probs(sacc, msk, pf);
     }
@@ -1213,32 +1211,25 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
         msk[x] = __builtin_amdgcn_perm(static_cast<uint32_t>(t1), static_cast<uint32_t>(t0), 0x0B0B0909u);
       }
     };
-    if (doq[0] && doq[1]) {
-      // Both blocks: the vector work of one block overlaps the matrix work of
-      // the other.
-      uint32_t m0[8], m1[8];
-      const f32x16 s0 = scores(buf, 0);
-      masks(0, m0);
-      const f32x16 s1 = scores(buf, 1);
-      if (more) issue(tn, nbuf);
-      bf16x8 pf0[2], pf1[2];
-      softmax(s0, m0, pf0);
-      pv(buf, 0, pf0);
-      masks(1, m1);
-      softmax(s1, m1, pf1);
-      pv(buf, 1, pf1);
-    } else if (doq[0] || doq[1]) {
-      const int blk = doq[0] ? 0 : 1;
-      uint32_t m[8];
-      const f32x16 s0 = scores(buf, blk);
-      masks(blk, m);
-      if (more) issue(tn, nbuf);
-      bf16x8 pf[2];
-      softmax(s0, m, pf);
-      pv(buf, blk, pf);
-    } else if (more) {
-      issue(tn, nbuf);
+    // The two blocks run one after the other (one code path per block, no
+    // separate path for "both"): with a single path the compiler keeps the
+    // output accumulators in place across the loop instead of copying them
+    // between register sets, which costs more than the lost overlap.
+    bool issued = !more;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      if (doq[blk]) {
+        uint32_t m[8];
+        const f32x16 sacc = scores(buf, blk);
+        masks(blk, m);
+        if (!issued) issue(tn, nbuf);
+        issued = true;
+        bf16x8 pf[2];
+        softmax(sacc, m, pf);
+        pv(buf, blk, pf);
+      }
     }
+    if (!issued) issue(tn, nbuf);
   };
 
   // One barrier per key tile.  At the barrier of tile e every wave has its
