@@ -1026,13 +1026,18 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
   const int partner = (lane ^ 32) << 2;  // ds_bpermute address of the other half
 
   // S^T block blk (keys 32*blk..+31 of the tile x this wave's 32 queries).
+  // All eight K fragments are read before the chain starts (the scheduling
+  // fence keeps the compiler from spreading the reads between the MFMAs,
+  // where each pair of them would wait out a full LDS latency).
   auto scores = [&](const char* buf, int blk) {
+    bf16x8 af[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      af[ks] = *reinterpret_cast<const bf16x8*>(buf + kread + 32 * blk * L::KSTR + 32 * ks);
+    __builtin_amdgcn_sched_barrier(0);
     f32x16 acc = (f32x16){0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 af = *reinterpret_cast<const bf16x8*>(buf + kread + 32 * blk * L::KSTR + 32 * ks);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], acc, 0, 0, 0);
-    }
+    for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qf[ks], acc, 0, 0, 0);
     return acc;
   };
   // Online softmax of one 32-key block.  msk[x] holds the radius mask of
