@@ -567,7 +567,7 @@ tra_status tra_attention(const tra_plan* plan, const void* q, const void* k, con
   TRA_HIP(tra::launch_attention(s.dtype, s.head_dim, q, k, v, o, plan->lv, tab, plan->row_base,
                                 plan->BH, plan->tiles, plan->row_ptr, plan->col_idx,
                                 plan->gptr, plan->glist, plan->glen, plan->params.block_mask != 0,
-                                static_cast<hipStream_t>(stream)));
+                                plan->params.vote_threshold == 1, static_cast<hipStream_t>(stream)));
   return TRA_OK;
 }
 

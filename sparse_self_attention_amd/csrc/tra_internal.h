@@ -73,7 +73,7 @@ hipError_t launch_attention(int dtype, int d, const void* q, const void* k, cons
                             void* o, const int16_t* lv, const RadiusTable& tab, int row_base,
                             int BH, const Grid& tiles, const int32_t* row_ptr,
                             const int32_t* col_idx, const int32_t* gptr, const int32_t* glist,
-                            const int32_t* glen, bool block_mask, hipStream_t s);
+                            const int32_t* glen, bool block_mask, bool self_ref, hipStream_t s);
 // Work unit of the bf16 attention kernel: a group of GROUP_ROWS x 2 query
 // tiles of one frame, run by one workgroup of ATTN_THREADS threads (two waves
 // per query tile).

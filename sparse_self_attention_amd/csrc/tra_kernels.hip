@@ -877,7 +877,7 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
     const int32_t* __restrict__ r2c, const int32_t* __restrict__ r2off,
     const int32_t* __restrict__ dmax, int n_r2c, int row_base, Grid g, int ngh, int ngw, int n_groups,
     const int32_t* __restrict__ gptr, const int2* __restrict__ glist,
-    const int32_t* __restrict__ glen) {
+    const int32_t* __restrict__ glen, int self_ref) {
   using L = AttnLds<D>;
   constexpr int NWAVES = ATTN_THREADS / 64;
   constexpr int KS = D / 16;  // k-steps of S^T
@@ -1017,8 +1017,31 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = (f32x16){0.f};
-  float mref = TRA_NEG_INF, lsum = 0.f;
+  float lsum = 0.f;
   const float c1 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
+  // The softmax reference (log2 units).  When the plan lists every query's
+  // own tile (self_ref), it starts at the query's score with its own key,
+  // which every generator retains and the loop therefore visits: kept
+  // probabilities cannot all underflow, and no block has to be formed twice
+  // just to set a first reference.  Otherwise it starts at -inf and the first
+  // block with a kept key sets it.  Each lane of a query pair holds half of
+  // the dot product.
+  float mref = TRA_NEG_INF;
+  if (self_ref) {
+    const uint16_t* kp = k + (static_cast<size_t>(bh) * N + nq) * D;
+    float dot = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 kv = *reinterpret_cast<const uint4*>(kp + 16 * ks + 8 * h);
+      const uint4 qv = __builtin_bit_cast(uint4, qf[ks]);
+      dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qv.x), __builtin_bit_cast(bf16x2, kv.x), dot, false);
+      dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qv.y), __builtin_bit_cast(bf16x2, kv.y), dot, false);
+      dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qv.z), __builtin_bit_cast(bf16x2, kv.z), dot, false);
+      dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qv.w), __builtin_bit_cast(bf16x2, kv.w), dot, false);
+    }
+    dot += __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __float_as_int(dot)));
+    mref = dot * c1;
+  }
   // Per-lane LDS byte bases; every read below adds a compile-time offset.
   const int g4 = lane >> 4, r4 = (lane & 15) >> 2, j4 = lane & 3;
   const int kread = col * L::KSTR + h * 16;
@@ -1048,16 +1071,15 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
   // Lazy rescale: the reference (shared by both lanes of a query) moves only
   // when the kept probabilities of a lane's block, formed against it, sum to
   // more than 2^10 (so between moves every kept probability is <= 2^10), or
-  // when no reference is set yet.  The probabilities and their sum are formed
-  // first; the test on the sum (which the running sum needs anyway) then
-  // decides, rarely, to move the reference to the exact masked maximum and
-  // form them again.
+  // while it is unset.  The probabilities and their sum are formed first; the test on the sum (which
+  // the running sum needs anyway) then decides, rarely, to move the reference
+  // to the exact masked maximum and form them again.
   // P^T as the two 16-key B operands of the PV product; returns the block's
   // contribution to the running sum.
   auto probs = [&](const f32x16& sacc, const uint32_t* msk, bf16x8* pf) {
-    // With no reference yet (-inf) the block is formed against 0 and then
-    // formed again once the reference has moved; if it cannot move (no key
-    // of the block is kept), every probability is masked.
+    // With no reference yet (-inf) the block is formed against 0 and formed
+    // again once the reference has moved; if it cannot move (no kept key in
+    // the block), every probability is masked.
     const float msub = mref == TRA_NEG_INF ? 0.f : mref;
     const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
     float ls[2] = {0.f, 0.f};
@@ -1577,7 +1599,7 @@ hipError_t launch_attention(int dtype, int d, const void* q, const void* k, cons
                             void* o, const int16_t* lv, const RadiusTable& tab, int row_base,
                             int BH, const Grid& tiles, const int32_t* row_ptr,
                             const int32_t* col_idx, const int32_t* gptr, const int32_t* glist,
-                            const int32_t* glen, bool block_mask, hipStream_t s) {
+                            const int32_t* glen, bool block_mask, bool self_ref, hipStream_t s) {
   const int32_t* r2 = tab.r2;
   const unsigned rows = static_cast<unsigned>(BH) * tiles.count;
   if (dtype == 1) {
@@ -1593,7 +1615,8 @@ hipError_t launch_attention(int dtype, int d, const void* q, const void* k, cons
 #define TRA_ATTN(DD, M, B)                                                                                 \
   attn_bf16_kernel<DD, M, B><<<grid, ATTN_THREADS, lds_tab, s>>>(qq, kk, vv, oo, lv, tab.r2c, tab.r2off, tab.dmax, \
                                                                  tab.n_r2c, row_base, tiles, ngh, ngw, ng, gptr,     \
-                                                                 reinterpret_cast<const int2*>(glist), glen)
+                                                                 reinterpret_cast<const int2*>(glist), glen,         \
+                                                                 self_ref ? 1 : 0)
     if (block_mask) {
       if (d == 128) TRA_ATTN(128, METRIC_L2, true);
       else TRA_ATTN(64, METRIC_L2, true);
