@@ -1071,9 +1071,9 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
   // Lazy rescale: the reference (shared by both lanes of a query) moves only
   // when the kept probabilities of a lane's block, formed against it, sum to
   // more than 2^10 (so between moves every kept probability is <= 2^10), or
-  // while it is unset.  The probabilities and their sum are formed first; the test on the sum (which
-  // the running sum needs anyway) then decides, rarely, to move the reference
-  // to the exact masked maximum and form them again.
+  // while it is unset.  The probabilities and their sum are formed first; the
+  // test on the sum (which the running sum needs anyway) then decides, rarely,
+  // to move the reference to the exact masked maximum and form them again.
   // P^T as the two 16-key B operands of the PV product; returns the block's
   // contribution to the running sum.
   auto probs = [&](const f32x16& sacc, const uint32_t* msk, bf16x8* pf) {
