@@ -15,6 +15,10 @@
 //   csr_runs_kernel       per query tile: union over its 64 queries of the disk
 //                         footprints, as key-tile runs per frame and tile row
 //   csr_expand_kernel     runs -> CSR column indices
+//   window_csr_kernel,    the 1-D window generator's tile lists (raster-order
+//   window_group_kernel   distance) and group lists, from per-row column masks
+//   vote_kernel,          token voting: retained pairs per listed tile pair, and
+//   vote_compact_kernel   the lists filtered by a vote threshold
 //   group_list_kernel     runs of a group of adjacent query tiles -> their merged list
 //   scan_kernel           exclusive scan of the per-tile counts
 //   attn_bf16_kernel      block-sparse flash attention: S^T = K Q^T and
@@ -22,7 +26,12 @@
 //                         in LDS (V read back transposed with ds_read_b64_tr_b16),
 //                         exact radius mask in registers, fp32 online softmax
 //   attn_f32_kernel       plain fp32 vector variant for fp32 inputs
-//   stats kernels         exact retained / listed pair counts
+//   retained_kernel,      exact retained / listed pair counts
+//   listed_kernel
+//   level_diff_kernel     plan drift: queries whose level a rebuild would change
+//   fill_levels_kernel    levels of the fixed-radius mode
+// The dense warm-up pass (dense attention with exact entropies) is in
+// tra_dense.hip.
 #include "tra_internal.h"
 #include "tra_device.h"
 
