@@ -122,7 +122,6 @@ __global__ __launch_bounds__(512) void dense_bf16_kernel(
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = (f32x16){0.f};
-  float mref = TRA_NEG_INF;
   float lsum = 0.f;            // without entropy: sum of the bf16 probabilities used by PV
   double lsum_d = 0.0, bsum_d = 0.0;  // with entropy: sum p and sum p*t, this lane's keys
   const float c1 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
@@ -130,6 +129,25 @@ __global__ __launch_bounds__(512) void dense_bf16_kernel(
   const int kread = col * L::KSTR + h * 16;
   const int vread = (4 * (g4 >> 1) + r4) * L::VSTR + (16 * (g4 & 1) + 4 * j4) * 2;
   const int partner = (lane ^ 32) << 2;
+  // The softmax reference (log2 units) starts at the query's score with its
+  // own key, which the pass visits like every other key, so it is finite from
+  // the start.  Each lane of a query pair holds half of the dot product.
+  float mref;
+  {
+    const uint16_t* kp = k + (head + min(n, N - 1)) * D;
+    float dot = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 kv = *reinterpret_cast<const uint4*>(kp + 16 * ks + 8 * h);
+      const uint4 qv = __builtin_bit_cast(uint4, qf[ks]);
+      dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qv.x), __builtin_bit_cast(bf16x2, kv.x), dot, false);
+      dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qv.y), __builtin_bit_cast(bf16x2, kv.y), dot, false);
+      dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qv.z), __builtin_bit_cast(bf16x2, kv.z), dot, false);
+      dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qv.w), __builtin_bit_cast(bf16x2, kv.w), dot, false);
+    }
+    dot += __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(dot)));
+    mref = dot * c1;
+  }
 
   auto scores = [&](const char* buf, int blk) {
     f32x16 acc = (f32x16){0.f};
@@ -147,9 +165,10 @@ __global__ __launch_bounds__(512) void dense_bf16_kernel(
     return fmaxf(mx, s[15]);
   };
   // Probabilities against the current reference (lazy rescale: the reference
-  // moves only when a score exceeds it by more than 2^8).
+  // moves only when a lane's probabilities of a block, formed against it, sum
+  // to more than 2^10, so between moves every probability is <= 2^10).
   auto probs = [&](const f32x16& s, bf16x8* pf, float* ls, float* bs) {
-    const float msub = mref == TRA_NEG_INF ? 0.f : mref;
+    const float msub = mref;
     const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
     float l2[2] = {0.f, 0.f}, b2[2] = {0.f, 0.f};
 #pragma unroll
@@ -175,27 +194,23 @@ __global__ __launch_bounds__(512) void dense_bf16_kernel(
     *bs = b2[0] + b2[1];
   };
   auto softmax = [&](const f32x16& s, bf16x8* pf) {
-    float mx = rowmax(s);
     float ls, bs;
     probs(s, pf, &ls, &bs);
-    if (__any(mx * c1 > mref + 8.f)) {
+    if (__any(!(ls <= 1024.f))) {
+      float mx = rowmax(s);
       mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(mx))));
-      if (__any(mx * c1 > mref + 8.f)) {
+      if (__any(mx * c1 > mref)) {
         const float mn = fmaxf(mref, mx * c1);
-        if (mref == TRA_NEG_INF) {
-          // First block: nothing accumulated yet.
-        } else {
-          const float alpha = __builtin_amdgcn_exp2f(mref - mn);
+        const float alpha = __builtin_amdgcn_exp2f(mref - mn);
 #pragma unroll
-          for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-          if constexpr (ENT) {
-            // t moves by (mref - mn): sum p*t -> alpha * (sum p*t + (mref - mn) * sum p).
-            const double ad = static_cast<double>(alpha);
-            bsum_d = ad * (bsum_d + static_cast<double>(mref - mn) * lsum_d);
-            lsum_d *= ad;
-          } else {
-            lsum *= alpha;
-          }
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+        if constexpr (ENT) {
+          // t moves by (mref - mn): sum p*t -> alpha * (sum p*t + (mref - mn) * sum p).
+          const double ad = static_cast<double>(alpha);
+          bsum_d = ad * (bsum_d + static_cast<double>(mref - mn) * lsum_d);
+          lsum_d *= ad;
+        } else {
+          lsum *= alpha;
         }
         mref = mn;
         probs(s, pf, &ls, &bs);
