@@ -381,8 +381,12 @@ __global__ __launch_bounds__(256) void csr_runs_kernel(const int16_t* __restrict
   const int t_lo = max(0, tq - dmw), t_hi = min(T - 1, tq + dmw);
   int32_t* rrow = runs + row * static_cast<int64_t>((2 * DM + 1) * g.nh);
   int count = 0;
-  for (int tk = t_lo; tk <= t_hi; ++tk) {
-    const int delta = tk > tq ? tk - tq : tq - tk;
+  // Frames tq - delta and tq + delta see the same disks: each distance is
+  // computed once and its runs are written for both frames.
+  for (int delta = 0; delta <= dmw; ++delta) {
+    const bool below = tq - delta >= 0, above = delta > 0 && tq + delta <= T - 1;
+    if (!below && !above) continue;  // wave-uniform
+    const int nfr = (below ? 1 : 0) + (above ? 1 : 0);
     const int thr = (valid && delta <= dm) ? r2[trow * T + delta] : -1;
     const int rad = thr >= 0 ? mask_reach<L1>(thr) : -1;
     const int top = thr >= 0 ? max(0, hq - rad) : 0x7fffffff;
@@ -404,11 +408,14 @@ __global__ __launch_bounds__(256) void csr_runs_kernel(const int16_t* __restrict
         }
         const int LO = wave_min_u(lo), HI = wave_max_u(hi);
         if (HI >= LO) {
-          count += HI - LO + 1;
+          count += (HI - LO + 1) * nfr;
           if (lane == tr - trc) myrun = LO | (HI << 16);
         }
       }
-      if (trc + lane < g.nh) rrow[(tk - t_lo) * g.nh + trc + lane] = myrun;
+      if (trc + lane < g.nh) {
+        if (below) rrow[(tq - delta - t_lo) * g.nh + trc + lane] = myrun;
+        if (above) rrow[(tq + delta - t_lo) * g.nh + trc + lane] = myrun;
+      }
     }
   }
   if (lane == 0) {
