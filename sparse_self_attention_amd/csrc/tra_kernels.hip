@@ -138,11 +138,14 @@ __device__ __forceinline__ void entropy_store(double Hd, const EntropyArgs& ea, 
   lvout[idx] = static_cast<int16_t>(kf);
 }
 
-// bf16 inputs.  grid (ceil(N/256), BH), 256 threads: 4 waves x 64 queries.
-// Pooled keys stream through LDS in chunks of 32 rows; each chunk gives a
-// 32(keys) x 32(queries) score block per MFMA column block, lane = query.
+// bf16 inputs.  grid (ceil(N/256), BH), 256 threads: 4 waves x 64 queries,
+// each wave two blocks of 32 queries (lane % 32 = query; both lanes of a
+// query hold half of its pooled keys).  Pooled keys stream through LDS in
+// chunks of 32 rows; each K fragment read from LDS feeds the score MFMAs of
+// both query blocks.
+constexpr int ENT_WAVES = 4, ENT_QB = 2, ENT_QPW = ENT_WAVES * 32 * ENT_QB;
 template <int D>
-__global__ __launch_bounds__(512) void entropy_bf16_kernel(
+__global__ __launch_bounds__(256, 3) void entropy_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kbar,
     const float* __restrict__ pool_w, int N, int NP, EntropyArgs ea, float* __restrict__ Hout,
     int16_t* __restrict__ lvout) {
@@ -154,37 +157,49 @@ __global__ __launch_bounds__(512) void entropy_bf16_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5, col = lane & 31;
-  // Eight waves of 32 queries (lane % 32 = query; both lanes of a query hold
-  // half of its pooled keys).
-  const int n = blockIdx.x * 256 + wave * 32 + col;
-  bf16x8 qf[KS];
-  {
-    const uint16_t* p = q + (static_cast<size_t>(bh) * N + min(n, N - 1)) * D;
+  const int n0 = blockIdx.x * ENT_QPW + wave * 32 * ENT_QB + col;  // query block qb: n0 + 32 * qb
+  bf16x8 qf[ENT_QB][KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(p + 16 * ks + 8 * h);
+  for (int qb = 0; qb < ENT_QB; ++qb) {
+    const uint16_t* p = q + (static_cast<size_t>(bh) * N + min(n0 + 32 * qb, N - 1)) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[qb][ks] = *reinterpret_cast<const bf16x8*>(p + 16 * ks + 8 * h);
   }
   const float c1 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
-  float m = TRA_NEG_INF, A = 0.f, Bm = 0.f;
+  float m[ENT_QB], A[ENT_QB], Bm[ENT_QB];
+#pragma unroll
+  for (int qb = 0; qb < ENT_QB; ++qb) {
+    m[qb] = TRA_NEG_INF;
+    A[qb] = 0.f;
+    Bm[qb] = 0.f;
+  }
 
-  // Pooled keys stream in chunks of 32 rows (one 1 KB DMA segment per wave,
-  // the chunk's weights through wave 0), one chunk ahead of use, through
-  // range-checked buffer resources: rows past NP read as zero (weight 0).
-  // Lane l of segment s fills LDS bytes s*1KB + 16*l of the chunk, that is
-  // row r and physical 16-byte chunk pc of the swizzled layout below; it
+  // Pooled keys stream in chunks of 32 rows (1 KB DMA segments, spread over
+  // the waves; the chunk's weights through wave 0), one chunk ahead of use,
+  // through range-checked buffer resources: rows past NP read as zero (weight
+  // 0).  Lane l of segment s fills LDS bytes s*1KB + 16*l of the chunk, that
+  // is row r and physical 16-byte chunk pc of the swizzled layout below; it
   // fetches the logical chunk pc ^ swz(r) of that row.
   constexpr int SEGS = 32 * D * 2 / 1024;  // 1 KB segments per chunk
+  constexpr int SPW = (SEGS + ENT_WAVES - 1) / ENT_WAVES;
+  static_assert(SEGS % ENT_WAVES == 0, "every wave streams the same number of segments");
   const i32x4 krs = make_rsrc(kbar + static_cast<size_t>(bh) * NP * D, static_cast<uint32_t>(NP * D * 2));
   const i32x4 wrs = make_rsrc(pool_w, static_cast<uint32_t>(NP * 4));
-  const int sbyte = wave * 1024 + lane * 16;
-  const int srow = sbyte / (2 * D), spc = (sbyte % (2 * D)) / 16;
-  const uint32_t soff = static_cast<uint32_t>(srow * 2 * D + ((spc ^ swz<NCH>(srow)) * 16));
+  uint32_t soff[SPW];
+#pragma unroll
+  for (int i = 0; i < SPW; ++i) {
+    const int sbyte = (wave + ENT_WAVES * i) * 1024 + lane * 16;
+    const int srow = sbyte / (2 * D), spc = (sbyte % (2 * D)) / 16;
+    soff[i] = static_cast<uint32_t>(srow * 2 * D + ((spc ^ swz<NCH>(srow)) * 16));
+  }
   const uint32_t kb_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(&kb_lds[0][0])));
   const uint32_t w_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(&w_lds[0][0])));
   auto stream = [&](int ci) {
     const int b = ci & 1;
-    if (wave < SEGS)
-      lds_dma16_buf(krs, static_cast<uint32_t>(ci) * 32 * D * 2 + soff,
-                    __builtin_amdgcn_readfirstlane(kb_base + b * 32 * D * 2 + wave * 1024));
+#pragma unroll
+    for (int i = 0; i < SPW; ++i)
+      lds_dma16_buf(krs, static_cast<uint32_t>(ci) * 32 * D * 2 + soff[i],
+                    __builtin_amdgcn_readfirstlane(kb_base + b * 32 * D * 2 + (wave + ENT_WAVES * i) * 1024));
     if (wave == 0)
       lds_dma4_buf(wrs, static_cast<uint32_t>(ci) * 32 * 4 + lane * 4,
                    __builtin_amdgcn_readfirstlane(w_base + b * 64 * 4));
@@ -197,11 +212,14 @@ __global__ __launch_bounds__(512) void entropy_bf16_kernel(
     if (ci + 1 < nchunks) stream(ci + 1);
     const uint16_t* kc = kb_lds[ci & 1];
     const float* wc = w_lds[ci & 1];
-    f32x16 acc = {0.f};
+    f32x16 acc[ENT_QB];
+#pragma unroll
+    for (int qb = 0; qb < ENT_QB; ++qb) acc[qb] = (f32x16){0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const bf16x8 af = *reinterpret_cast<const bf16x8*>(&kc[col * D + (((2 * ks + h) ^ swz<NCH>(col)) << 3)]);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], acc, 0, 0, 0);
+#pragma unroll
+      for (int qb = 0; qb < ENT_QB; ++qb) acc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[qb][ks], acc[qb], 0, 0, 0);
     }
     float w[16];
 #pragma unroll
@@ -215,48 +233,59 @@ __global__ __launch_bounds__(512) void entropy_bf16_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int r = 8 * (i >> 2) + 4 * h + (i & 3);
-        if (ci * 32 + r >= NP) acc[i] = -3.0e38f;
+        if (ci * 32 + r >= NP) {
+#pragma unroll
+          for (int qb = 0; qb < ENT_QB; ++qb) acc[qb][i] = -3.0e38f;
+        }
       }
     }
-    float mx = fmaxf(fmaxf(acc[0], acc[1]), acc[2]);
 #pragma unroll
-    for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, acc[i]), acc[i + 1]);
-    mx = fmaxf(mx, acc[15]);
-    const float mnew = fmaxf(m, mx * c1);
-    float sA = 0.f, sB = 0.f;
+    for (int qb = 0; qb < ENT_QB; ++qb) {
+      const f32x16& sc = acc[qb];
+      float mx = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float t = fmaf(acc[i], c1, -mnew);
-      const float e = __builtin_amdgcn_exp2f(t) * w[i];
-      sA += e;
-      sB = fmaf(e, t, sB);
+      for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sc[i]), sc[i + 1]);
+      mx = fmaxf(mx, sc[15]);
+      const float mnew = fmaxf(m[qb], mx * c1);
+      float sA = 0.f, sB = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float t = fmaf(sc[i], c1, -mnew);
+        const float e = __builtin_amdgcn_exp2f(t) * w[i];
+        sA += e;
+        sB = fmaf(e, t, sB);
+      }
+      if (A[qb] > 0.f) {
+        const float alpha = __builtin_amdgcn_exp2f(m[qb] - mnew);
+        Bm[qb] = alpha * fmaf(m[qb] - mnew, A[qb], Bm[qb]) + sB;
+        A[qb] = fmaf(A[qb], alpha, sA);
+      } else {
+        Bm[qb] = sB;
+        A[qb] = sA;
+      }
+      m[qb] = mnew;
     }
-    if (A > 0.f) {
-      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-      Bm = alpha * fmaf(m - mnew, A, Bm) + sB;
-      A = fmaf(A, alpha, sA);
-    } else {
-      Bm = sB;
-      A = sA;
-    }
-    m = mnew;
   }
-  const float mp = __shfl_xor(m, 32), Ap = __shfl_xor(A, 32), Bp = __shfl_xor(Bm, 32);
-  if (h == 0 && n < N) {
-    const double M = fmax(static_cast<double>(m), static_cast<double>(mp));
-    double At = 0.0, Bt = 0.0;
-    if (A > 0.f) {
-      const double s0 = exp2(static_cast<double>(m) - M);
-      At += s0 * A;
-      Bt += s0 * (static_cast<double>(Bm) + (static_cast<double>(m) - M) * A);
+#pragma unroll
+  for (int qb = 0; qb < ENT_QB; ++qb) {
+    const int n = n0 + 32 * qb;
+    const float mp = __shfl_xor(m[qb], 32), Ap = __shfl_xor(A[qb], 32), Bp = __shfl_xor(Bm[qb], 32);
+    if (h == 0 && n < N) {
+      const double M = fmax(static_cast<double>(m[qb]), static_cast<double>(mp));
+      double At = 0.0, Bt = 0.0;
+      if (A[qb] > 0.f) {
+        const double s0 = exp2(static_cast<double>(m[qb]) - M);
+        At += s0 * A[qb];
+        Bt += s0 * (static_cast<double>(Bm[qb]) + (static_cast<double>(m[qb]) - M) * A[qb]);
+      }
+      if (Ap > 0.f) {
+        const double s1 = exp2(static_cast<double>(mp) - M);
+        At += s1 * Ap;
+        Bt += s1 * (static_cast<double>(Bp) + (static_cast<double>(mp) - M) * Ap);
+      }
+      const double Hd = log(At) - 0.6931471805599453 * Bt / At;
+      entropy_store(Hd, ea, static_cast<size_t>(bh) * N + n, Hout, lvout);
     }
-    if (Ap > 0.f) {
-      const double s1 = exp2(static_cast<double>(mp) - M);
-      At += s1 * Ap;
-      Bt += s1 * (static_cast<double>(Bp) + (static_cast<double>(mp) - M) * Ap);
-    }
-    const double Hd = log(At) - 0.6931471805599453 * Bt / At;
-    entropy_store(Hd, ea, static_cast<size_t>(bh) * N + n, Hout, lvout);
   }
 }
 
@@ -1492,9 +1521,9 @@ hipError_t launch_entropy(int dtype, int d, const void* q, const void* kbar, con
   if (dtype == 1) {
     const auto* qq = static_cast<const uint16_t*>(q);
     const auto* kb = static_cast<const uint16_t*>(kbar);
-    const dim3 block16(512);  // eight waves of 32 queries
-    if (d == 128) entropy_bf16_kernel<128><<<grid, block16, 0, s>>>(qq, kb, pool_w, N, n_pool, ea, H_out, lv_out);
-    else entropy_bf16_kernel<64><<<grid, block16, 0, s>>>(qq, kb, pool_w, N, n_pool, ea, H_out, lv_out);
+    const dim3 grid16((N + ENT_QPW - 1) / ENT_QPW, BH), block16(ENT_WAVES * 64);
+    if (d == 128) entropy_bf16_kernel<128><<<grid16, block16, 0, s>>>(qq, kb, pool_w, N, n_pool, ea, H_out, lv_out);
+    else entropy_bf16_kernel<64><<<grid16, block16, 0, s>>>(qq, kb, pool_w, N, n_pool, ea, H_out, lv_out);
   } else {
     const auto* qq = static_cast<const float*>(q);
     const auto* kb = static_cast<const float*>(kbar);
