@@ -18,3 +18,13 @@ def gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="session")
+def oracle_pool():
+    """Worker processes that run the unchanged oracle on pieces of a full-size
+    workload (heads, blocks of queries)."""
+    from oracle import runner
+    pool = runner.make_pool()
+    yield pool
+    pool.shutdown(wait=True, cancel_futures=True)

@@ -16,6 +16,9 @@ import torch
 
 import oracle as O
 import sparse_self_attention_amd as tra
+from oracle import runner
+
+import ref_tiles
 from workloads import make_inputs
 
 MAX_ABS = 2e-2
@@ -35,52 +38,86 @@ def gpu_run(cfg, device, inputs=None):
     return {"q": q, "k": k, "v": v, "o": o, "plan": plan, "export": plan.export()}
 
 
-def check_head(cfg, run, b, h, tile_sample=None, query_sample=None, rng=None):
-    """Compares one head; returns a metrics dict (asserts on failure)."""
+def check_head(cfg, run, b, h, tile_sample=None, query_sample=None, rng=None, oracle_plan=None,
+               tile_lists="oracle", pool=None):
+    """Compares one head; returns a metrics dict (asserts on failure).
+
+    tile_lists: "oracle" compares each query tile's list with the oracle's
+    query-by-query definition (`tile_sample` rows, default all); "reference"
+    compares every row of the head with the vectorised reference lists
+    (tests/ref_tiles.py, pinned to the oracle's definition on the CPU).
+    oracle_plan: the oracle's pooled keys, entropies, levels and excused set of
+    this head when already computed (oracle.runner.head_plans).
+    pool: an oracle.runner pool that computes the reference outputs."""
     p = cfg.params()
     bh = b * cfg.heads + h
     exp = run["export"]
-    qh = run["q"][b, h].double().cpu().numpy()
-    kh = run["k"][b, h].double().cpu().numpy()
-    vh = run["v"][b, h].double().cpu().numpy()
     og = run["o"][b, h].double().cpu().numpy()
     lv_g = exp["levels"][bh].astype(np.int64)
     R2 = O.radius_table(p, cfg.T)
     assert np.array_equal(exp["r2"].astype(np.int64), R2)
     out = {"bh": bh}
     if p["radius_override"] < 0:
-        pools = O.Geometry(cfg.T, cfg.H, cfg.W, cfg.pool_h, cfg.pool_w)
-        kbar_o = O.pool_keys(kh, pools, cfg.dtype)
-        kbar_g = exp["kbar"][bh]
-        kbar_g = bf16_bits_to_f64(kbar_g) if cfg.dtype == "bf16" else kbar_g.astype(np.float64)
-        assert np.array_equal(kbar_g, kbar_o), "pooled keys differ"
-        H_o = O.entropy(qh, kbar_o, pools.block_sizes())
-        lv_o = O.levels(H_o, p)
-        E = O.excused_queries(H_o, p)
-        out["entropy_max_abs_err"] = float(np.max(np.abs(exp["entropy"][bh].astype(np.float64) - H_o)))
-        out["excused"] = E.tolist()
-        assert len(E) <= EXCUSE_FRACTION * cfg.N, f"{len(E)} queries near a boundary"
-        bad = np.nonzero(lv_g != lv_o)[0]
-        out["level_mismatch"] = bad.tolist()
-        assert set(bad.tolist()) <= set(E.tolist()), f"levels differ outside the excused set: {bad[:10]}"
+        if oracle_plan is None:
+            qh = run["q"][b, h].double().cpu().numpy()
+            kh = run["k"][b, h].double().cpu().numpy()
+            pools = O.Geometry(cfg.T, cfg.H, cfg.W, cfg.pool_h, cfg.pool_w)
+            kbar_o = O.pool_keys(kh, pools, cfg.dtype)
+            H_o = O.entropy(qh, kbar_o, pools.block_sizes())
+            oracle_plan = {"kbar": kbar_o, "H": H_o, "levels": O.levels(H_o, p),
+                           "excused": O.excused_queries(H_o, p)}
+        check_levels(cfg, exp, bh, oracle_plan, out)
     else:
         assert np.all(lv_g == -1)
-    tiles = O.Geometry(cfg.T, cfg.H, cfg.W, cfg.tile_h, cfg.tile_w)
     row_ptr = exp["row_ptr"].astype(np.int64)
     col_idx = exp["col_idx"].astype(np.int64)
+    tiles = O.Geometry(cfg.T, cfg.H, cfg.W, cfg.tile_h, cfg.tile_w)
     base = bh * tiles.count
-    tile_ids = range(tiles.count) if tile_sample is None else tile_sample
-    for a in tile_ids:
-        got = col_idx[row_ptr[base + a]:row_ptr[base + a + 1]]
-        ref = O.query_tile_row(a, lv_g, R2, tiles, p)
-        assert np.array_equal(got, ref), f"tile list of query tile {a} differs"
+    if tile_lists == "reference":
+        rp_r, ci_r = ref_tiles.csr(lv_g, R2, cfg.T, cfg.H, cfg.W, p)
+        rows_h = row_ptr[base:base + tiles.count + 1]
+        assert np.array_equal(rows_h - rows_h[0], rp_r), "tile-list lengths differ"
+        assert np.array_equal(col_idx[rows_h[0]:rows_h[-1]], ci_r), "tile-list columns differ"
+        out["tile_rows_compared"] = tiles.count
+    else:
+        tile_ids = range(tiles.count) if tile_sample is None else tile_sample
+        for a in tile_ids:
+            got = col_idx[row_ptr[base + a]:row_ptr[base + a + 1]]
+            ref = O.query_tile_row(a, lv_g, R2, tiles, p)
+            assert np.array_equal(got, ref), f"tile list of query tile {a} differs"
+        out["tile_rows_compared"] = len(tile_ids)
     queries = np.arange(cfg.N) if query_sample is None else np.asarray(query_sample)
-    o_ref = O.attention_rows(qh, kh, vh, queries, lv_g, R2, cfg.T, cfg.H, cfg.W, p)
+    if pool is not None:
+        done, o_ref, _, _, _ = runner.attention_rows(pool, cfg, run["q"][b, h], run["k"][b, h], run["v"][b, h],
+                                                     queries, lv_g, R2)
+        assert np.array_equal(done, queries)
+    else:
+        qh, kh, vh = (run[x][b, h].double().cpu().numpy() for x in "qkv")
+        o_ref = O.attention_rows(qh, kh, vh, queries, lv_g, R2, cfg.T, cfg.H, cfg.W, p)
     err = np.abs(og[queries] - o_ref)
+    out["queries_compared"] = len(queries)
     out["o_max_abs"] = float(err.max())
     out["o_mean_abs"] = float(err.mean())
     assert np.all(np.isfinite(og[queries]))
     assert out["o_max_abs"] <= MAX_ABS and out["o_mean_abs"] <= MEAN_ABS, out
+    return out
+
+
+def check_levels(cfg, exp, bh, oracle_plan, out=None):
+    """Pooled keys bit-exact; levels equal to the oracle's outside the excused
+    set (queries within 1e-5 nat of a level boundary, at most 0.1% of them)."""
+    out = {} if out is None else out
+    kbar_g = exp["kbar"][bh]
+    kbar_g = bf16_bits_to_f64(kbar_g) if cfg.dtype == "bf16" else kbar_g.astype(np.float64)
+    assert np.array_equal(kbar_g, oracle_plan["kbar"]), "pooled keys differ"
+    E = np.asarray(oracle_plan["excused"])
+    out["entropy_max_abs_err"] = float(np.max(np.abs(exp["entropy"][bh].astype(np.float64) - oracle_plan["H"])))
+    out["excused"] = E.tolist()
+    assert len(E) <= EXCUSE_FRACTION * cfg.N, f"{len(E)} queries near a boundary"
+    lv_g = exp["levels"][bh].astype(np.int64)
+    bad = np.nonzero(lv_g != oracle_plan["levels"])[0]
+    out["level_mismatch"] = bad.tolist()
+    assert set(bad.tolist()) <= set(E.tolist()), f"levels differ outside the excused set: {bad[:10]}"
     return out
 
 

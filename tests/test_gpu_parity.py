@@ -9,7 +9,10 @@ import oracle as O
 import sparse_self_attention_amd as tra
 from workloads import CONFIGS, make_inputs, perturb, small_workload
 
-from parity_util import check_csr_properties, check_group_lists, check_head, gpu_run
+from oracle import runner
+
+import ref_tiles
+from parity_util import check_csr_properties, check_group_lists, check_head, check_levels, gpu_run
 
 pytestmark = pytest.mark.gpu
 
@@ -132,34 +135,56 @@ def test_plan_mismatch_rejected(gpu):
 
 
 # ---------------------------------------------------------------------------
-# Full-size workloads, in the launch configuration the benchmark times:
-# every head runs on the GPU; two heads are compared against the oracle (all
-# levels, sampled tile lists and sampled outputs), the rest by properties.
+# Full-size workloads, in the launch configuration the benchmark times.  Every
+# head runs on the GPU and, per workload:
+#   - pooled keys and levels of every head against the oracle's (the oracle
+#     runs per head in a pool of worker processes);
+#   - every tile list of two heads against the vectorised reference lists;
+#   - O of at least 2,000 queries of those two heads (one query in every tile
+#     on the border of every frame, the rest random) against the oracle.
 # ---------------------------------------------------------------------------
+FULL_QUERIES = 2000
+
+
+def check_full_size(cfg, run, pool, heads_o=None, rng_seed=11):
+    exp = run["export"]
+    check_csr_properties(cfg, run)
+    assert torch.isfinite(run["o"].float()).all()
+    excused = 0
+    if cfg.radius_override < 0:
+        plans = runner.head_plans(pool, cfg, run["q"], run["k"], range(cfg.heads))
+        for h in range(cfg.heads):
+            m = check_levels(cfg, exp, h, plans[h])
+            excused += len(m["excused"])
+        _say(cfg.name, "levels of all", cfg.heads, "heads equal outside", excused, "excused queries",
+             f"({excused / (cfg.heads * cfg.N):.2e} of all)")
+        assert excused <= 1e-3 * cfg.heads * cfg.N
+    else:
+        plans = {}
+    rng = np.random.default_rng(rng_seed)
+    for h in (heads_o if heads_o is not None else (0, cfg.heads - 1)):
+        qs = ref_tiles.query_sample(cfg.T, cfg.H, cfg.W, FULL_QUERIES, rng)
+        m = check_head(cfg, run, 0, h, query_sample=qs, oracle_plan=plans.get(h), tile_lists="reference",
+                       pool=pool)
+        _say(cfg.name, "head", h, "tile rows", m["tile_rows_compared"], "queries", m["queries_compared"],
+             "H err", m.get("entropy_max_abs_err"), "O", m["o_max_abs"], m["o_mean_abs"],
+             "excused", m.get("excused", [])[:20], "mismatched", m.get("level_mismatch", []))
+    return excused
+
+
 @pytest.mark.parametrize("name", ["wan21_1p3b_480p", "wan21_14b_720p", "hunyuan_720p", "long_video_2x"])
-def test_full_size_workload(gpu, name):
+def test_full_size_workload(gpu, oracle_pool, name):
     cfg = CONFIGS[name]
     _say("case: full size", name)
     run = gpu_run(cfg, gpu)
-    check_csr_properties(cfg, run)
-    assert torch.isfinite(run["o"].float()).all()
-    rng = np.random.default_rng(11)
-    tiles = O.Geometry(cfg.T, cfg.H, cfg.W, 8, 8)
-    excused = 0
-    for h in (0, cfg.heads - 1):
-        tile_sample = rng.choice(tiles.count, size=12, replace=False)
-        tile_sample = np.concatenate([tile_sample, [0, tiles.count - 1]])  # corners incl. ragged
-        qs = np.concatenate([rng.choice(cfg.N, size=48, replace=False), [0, cfg.N - 1]])
-        m = check_head(cfg, run, 0, h, tile_sample=tile_sample, query_sample=qs)
-        excused += len(m["excused"])
-        _say(name, "head", h, "H err", m["entropy_max_abs_err"], "O", m["o_max_abs"], m["o_mean_abs"],
-             "excused", m["excused"][:20], "mismatched", m["level_mismatch"])
+    check_full_size(cfg, run, oracle_pool)
     retained, listed = run["plan"].stats()
     _say(name, "density", retained / (cfg.heads * cfg.N ** 2), "tile efficiency", retained / listed)
 
 
-def test_plan_reuse_path(gpu):
-    """Plan from call 1 reused for calls 2..4 with 1% perturbed Q and K."""
+def test_plan_reuse_path(gpu, oracle_pool):
+    """Plan from call 1 reused for calls 2..4 with 1% perturbed Q and K: O of
+    2,000+ queries of two heads per call against the oracle under the plan."""
     cfg = CONFIGS["wan21_14b_720p"]
     _say("case: reuse path")
     q, k, v = make_inputs(cfg, device=gpu)
@@ -171,14 +196,13 @@ def test_plan_reuse_path(gpu):
         qc, kc = perturb(q, call, 0), perturb(k, call, 1)
         o = tra.attention(qc, kc, v, plan)
         torch.cuda.synchronize()
-        h = int(rng.integers(cfg.heads))
-        qs = rng.choice(cfg.N, size=32, replace=False)
-        ref = O.attention_rows(qc[0, h].double().cpu().numpy(), kc[0, h].double().cpu().numpy(),
-                               v[0, h].double().cpu().numpy(), qs, exp["levels"][h].astype(np.int64),
-                               R2, cfg.T, cfg.H, cfg.W, cfg.params())
-        err = np.abs(o[0, h].double().cpu().numpy()[qs] - ref)
-        _say("call", call, "head", h, err.max(), err.mean())
-        assert err.max() <= 2e-2 and err.mean() <= 2e-3
+        for h in (int(rng.integers(cfg.heads // 2)), int(cfg.heads // 2 + rng.integers(cfg.heads // 2))):
+            qs = ref_tiles.query_sample(cfg.T, cfg.H, cfg.W, FULL_QUERIES, rng)
+            done, ref, _, _, _ = runner.attention_rows(oracle_pool, cfg, qc[0, h], kc[0, h], v[0, h], qs,
+                                                       exp["levels"][h].astype(np.int64), R2)
+            err = np.abs(o[0, h].double().cpu().numpy()[qs] - ref)
+            _say("call", call, "head", h, "queries", len(qs), err.max(), err.mean())
+            assert err.max() <= 2e-2 and err.mean() <= 2e-3
 
 
 def test_plan_drift(gpu):
@@ -236,20 +260,13 @@ def test_generator_small_full_parity(gpu, gen, r, dtype):
 
 
 @pytest.mark.parametrize("gen,r", [(1, 24.0), (2, 40.0), (3, -1.0)])
-def test_generator_full_size_sampled(gpu, gen, r):
+def test_generator_full_size(gpu, oracle_pool, gen, r):
     base = CONFIGS["wan21_14b_720p"]
     from dataclasses import replace
     cfg = replace(base, radius_override=r, generator=gen)
     _say("case: generator full size", gen, r)
     run = gpu_run(cfg, gpu)
-    check_csr_properties(cfg, run)
-    rng = np.random.default_rng(41)
-    tiles = O.Geometry(cfg.T, cfg.H, cfg.W, 8, 8)
-    for h in (0, cfg.heads - 1):
-        ts = np.concatenate([rng.choice(tiles.count, size=10, replace=False), [0, tiles.count - 1]])
-        qs = np.concatenate([rng.choice(cfg.N, size=24, replace=False), [0, cfg.N - 1]])
-        m = check_head(cfg, run, 0, h, tile_sample=ts, query_sample=qs)
-        _say("head", h, "O", m["o_max_abs"], m["o_mean_abs"])
+    check_full_size(cfg, run, oracle_pool, rng_seed=41)
     retained, listed = run["plan"].stats()
     _say("density", retained / (cfg.heads * cfg.N ** 2), "tile efficiency", retained / listed)
 
@@ -327,39 +344,94 @@ def test_vote_threshold_full_size_sampled(gpu, theta, block):
     _say("pairs", retained, "listed", listed, "density", retained / (cfg.heads * cfg.N ** 2))
 
 
-@pytest.mark.parametrize("gen,r", [(0, 4.5), (1, 5.0), (2, 7.0), (3, 3.0), (3, 9.0), (3, 50.0)])
-def test_key_sets_exact(gpu, gen, r):
-    """Every query's key set, exactly: with Q = 0 all retained keys weigh the
-    same, and V[j] = e_(j % 64) + e_(64 + j // 64), so row n of O is the
-    histogram of its keys' residues and 64-blocks divided by their number.
-    A grid with ragged tile rows and columns in every frame puts keys at the
-    corners of edge tiles, where out-of-grid positions hold wrapped data."""
-    cfg = small_workload(T=4, H=13, W=21, heads=1, radius_override=r, generator=gen)
+# ---------------------------------------------------------------------------
+# Exact key sets.  With Q = 0 every retained key weighs the same, so row n of
+# O is the mean of V over the keys query n retains.  V encodes each key j in
+# two 64-wide one-hot blocks, e_(j % 64) + e_(64 + j // 64) (N <= 4096), so
+# O[n] * |S_n| is the integer histogram of the key set's residues and 64-blocks
+# (every count <= 64).  The probabilities are exactly 1 and their sums exact,
+# so the only rounding is the bf16 output's (8-bit significand, relative error
+# <= 2^-8): O[n] * |S_n| stays within 64 * 2^-8 = 0.25 of each count and
+# rint() recovers it exactly.  A missing, extra or displaced key changes two
+# counts by one.  A second V encodes the keys through a random permutation,
+# so that two different key sets with equal histograms under one encoding are
+# told apart by the other.
+# ---------------------------------------------------------------------------
+def _onehot_values(N, perm, gpu):
+    j = perm if perm is not None else np.arange(N)
+    v = torch.zeros((N, 128), dtype=torch.float32)
+    v[np.arange(N), torch.from_numpy(j % 64)] = 1.0
+    v[np.arange(N), torch.from_numpy(64 + j // 64)] = 1.0
+    return v.to(torch.bfloat16).reshape(1, 1, N, 128).to(gpu)
+
+
+def _check_key_sets(cfg, plan, lv, gpu, seed):
     p = cfg.params()
     N = cfg.N
     assert N <= 64 * 64
-    q = torch.zeros((1, 1, N, 128), dtype=torch.bfloat16, device=gpu)
-    g = torch.Generator(device="cpu").manual_seed(5)
-    k = torch.randn((1, 1, N, 128), generator=g).to(torch.bfloat16).to(gpu)
-    idx = torch.arange(N)
-    v = torch.zeros((N, 128), dtype=torch.float32)
-    v[idx, idx % 64] = 1.0
-    v[idx, 64 + idx // 64] = 1.0
-    v = v.to(torch.bfloat16).reshape(1, 1, N, 128).to(gpu)
-    plan = tra.plan(q, k, grid=(cfg.T, cfg.H, cfg.W), **p)
-    o = tra.attention(q, k, v, plan)
-    torch.cuda.synchronize()
-    o = o[0, 0].double().cpu().numpy()
     R2 = O.radius_table(p, cfg.T)
+    mask = O.dense_mask(lv, R2, cfg.T, cfg.H, cfg.W, p)  # oracle's brute-force N x N mask
+    size = mask.sum(axis=1).astype(np.float64)
+    q = torch.zeros((1, 1, N, 128), dtype=torch.bfloat16, device=gpu)
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    k = torch.randn((1, 1, N, 128), generator=g).to(torch.bfloat16).to(gpu)
+    perm = np.random.default_rng(seed).permutation(N)
     worst = 0.0
-    for n in range(N):
-        keys = O.retained_keys(n, -1, R2, cfg.T, cfg.H, cfg.W, p)
-        want = np.zeros(128)
-        np.add.at(want, keys % 64, 1.0)
-        np.add.at(want, 64 + keys // 64, 1.0)
-        want /= len(keys)
-        worst = max(worst, float(np.abs(o[n] - want).max()))
-    _say("generator", gen, "radius", r, "worst histogram error", worst)
-    # bf16 output of values k/|S| <= 1: a key counted twice or missing moves an
-    # entry by 1/|S| >= 1/|N|, far above the rounding (< 2^-8 relative).
-    assert worst < 0.5 / N + 4e-3
+    for enc in (None, perm):
+        v = _onehot_values(N, enc, gpu)
+        o = tra.attention(q, k, v, plan)
+        torch.cuda.synchronize()
+        scaled = o[0, 0].double().cpu().numpy() * size[:, None]
+        got = np.rint(scaled).astype(np.int64)
+        want = np.rint(mask.astype(np.float64) @ v[0, 0].double().cpu().numpy()).astype(np.int64)
+        bad = np.nonzero(np.any(got != want, axis=1))[0]
+        assert len(bad) == 0, f"{len(bad)} queries with a different key set, first {bad[:8].tolist()}"
+        worst = max(worst, float(np.abs(scaled - got).max()))
+    return int(size.max()), worst
+
+
+KEYSET_CASES = [
+    # (T, H, W, generator, radius): static radii up to production size (the
+    # 30 x 45 frame is ragged in both directions: 4 x 6 tiles, the last of each
+    # row and column cut)
+    (4, 13, 21, 0, 4.5), (3, 30, 45, 0, 12.5), (3, 30, 45, 0, 40.0),
+    (4, 13, 21, 1, 5.0), (3, 30, 45, 1, 24.0),
+    (4, 13, 21, 2, 7.0), (3, 30, 45, 2, 40.0),
+    (4, 13, 21, 3, 3.0), (4, 13, 21, 3, 9.0), (3, 30, 45, 3, 50.0), (3, 30, 45, 3, 700.0),
+]
+
+
+@pytest.mark.parametrize("case", KEYSET_CASES)
+def test_key_sets_exact(gpu, case):
+    """Every query's key set, exactly, for fixed radii of every generator."""
+    T, H, W, gen, r = case
+    cfg = small_workload(T=T, H=H, W=W, heads=1, radius_override=r, generator=gen)
+    _say("case: key sets", case)
+    q = torch.zeros((1, 1, cfg.N, 128), dtype=torch.bfloat16, device=gpu)
+    plan = tra.plan(q, q, grid=(T, H, W), **cfg.params())
+    lv = np.full(cfg.N, -1, dtype=np.int64)
+    largest, worst = _check_key_sets(cfg, plan, lv, gpu, seed=5)
+    _say("largest key set", largest, "worst distance from an integer count", worst)
+
+
+@pytest.mark.parametrize("T,H,W,gen", [(3, 30, 45, 0), (4, 13, 21, 0), (3, 30, 45, 3)])
+def test_key_sets_exact_mixed_levels(gpu, T, H, W, gen):
+    """Every query's key set, exactly, when neighbouring queries hold unrelated
+    budget levels (each query tile then mixes small and large disks).  The
+    plan takes its levels from chosen per-query entropies, spread over the
+    whole budget range [16, N]."""
+    N = T * H * W
+    cfg = small_workload(T=T, H=H, W=W, heads=1, generator=gen, budget_min=16.0, budget_max=float(N),
+                         c=0.0, decay=0.5)
+    p = cfg.params()
+    rng = np.random.default_rng(7 + gen)
+    Hq = rng.uniform(math.log(16.0) - 0.5, math.log(N) + 0.5, size=N).astype(np.float32)
+    _say("case: key sets, mixed levels", (T, H, W), "generator", gen)
+    ent = torch.from_numpy(Hq).reshape(1, 1, N).to(gpu)
+    plan = tra.plan_from_entropy(ent, grid=(T, H, W), head_dim=128, dtype=torch.bfloat16, **p)
+    lv = plan.export()["levels"][0].astype(np.int64)
+    assert np.array_equal(lv, O.levels(Hq.astype(np.float64), p))
+    k_lo, k_hi = O.level_range(p)
+    assert len(np.unique(lv)) > (k_hi - k_lo) // 2  # many distinct levels
+    largest, worst = _check_key_sets(cfg, plan, lv, gpu, seed=9)
+    _say("levels", k_lo, "..", k_hi, "largest key set", largest, "worst distance from an integer count", worst)
