@@ -34,7 +34,13 @@
  *     asynchronous on that stream except where noted.
  *   - Errors are reported by status code only; a failing call writes no
  *     output and *out stays NULL.  tra_last_error() gives a message for the
- *     last failure on the calling thread.
+ *     last failure on the calling thread.  A failed allocation returns
+ *     TRA_ERR_OOM, a failed kernel launch or runtime call TRA_ERR_HIP.
+ *   - Fault injection (tests of the error paths): with the environment
+ *     variable TRA_FAULT=alloc[:n] the n-th device or pinned-host allocation
+ *     (default the first) of each call fails as if out of memory; with
+ *     TRA_FAULT=launch[:n] the n-th kernel launch of each call fails (the
+ *     kernel is not launched).
  *   - Supported on the device: dtype TRA_BF16 with head_dim 64 or 128 (bf16
  *     matrix cores), dtype TRA_F32 with head_dim 64 or 128 (fp32 vector path),
  *     8 x 8 tiles (tile_h = tile_w = 8).  T, H, W <= 32767;
@@ -58,7 +64,8 @@ typedef enum {
   TRA_ERR_PLAN_MISMATCH = 4, /* tensors do not match the plan's shape          */
   TRA_ERR_OOM = 5,           /* device or host allocation failed               */
   TRA_ERR_OVERFLOW = 6,      /* a count exceeds the 32-bit index range         */
-  TRA_ERR_HIP = 7            /* a HIP runtime call failed                       */
+  TRA_ERR_HIP = 7,           /* a HIP runtime call or kernel launch failed     */
+  TRA_ERR_PLAN_INVALID = 8   /* the plan's last build failed: rebuild it first  */
 } tra_status;
 
 typedef enum { TRA_F32 = 0, TRA_BF16 = 1 } tra_dtype;
@@ -167,7 +174,10 @@ tra_status tra_radius_table(const tra_shape* shape, const tra_params* params, in
                             double* r0sq, int32_t* n_levels, int32_t* k_lo);
 
 /*
- * Build a plan from q and k (steps entropy -> level -> radius -> tile lists):
+ * Build a plan from q and k (steps entropy -> level -> radius -> tile lists;
+ * [TRA] section 2: Intuition I for entropy -> budget, Intuition II for budget
+ * -> radius shrinking with temporal distance, "Exécution Efficace" for the
+ * token masks turned into block-sparse tile lists):
  *   Kbar_b = mean of the keys of pool rectangle b, rounded once to the dtype;
  *   H_i    = entropy of softmax_j(q_i . Kbar_{b(j)} / sqrt(d)) over all N keys;
  *   k_i    = clamped level of H_i;
@@ -176,18 +186,29 @@ tra_status tra_radius_table(const tra_shape* shape, const tra_params* params, in
  *   (h_i-h_j)^2 + (w_i-w_j)^2 <= R2[k_i][|t_i-t_j|].
  * The CSR's columns are ascending key-tile ids (tile id = (t*ceil(H/tile_h) +
  * h/tile_h)*ceil(W/tile_w) + w/tile_w) within each head.
- * Synchronises `stream` once (to size the tile lists).  *out receives the plan.
+ * Synchronises `stream` once (to size the tile lists).  *out receives the plan,
+ * which owns all its device memory (including the scratch of tra_plan_stats
+ * and tra_plan_drift); on failure nothing is kept and *out stays NULL.
+ * Errors: TRA_ERR_INVALID_ARG / SHAPE / DTYPE for inputs the device path does
+ * not take (see tra_params_validate), TRA_ERR_OOM, TRA_ERR_HIP,
+ * TRA_ERR_OVERFLOW when the tile lists would hold 2^31 entries or more.
  */
 tra_status tra_plan_create(const tra_shape* shape, const tra_params* params, const void* q,
                            const void* k, void* stream, tra_plan** out);
 
 /*
- * Block-sparse attention with the plan's exact per-token mask:
+ * Block-sparse attention with the plan's exact per-token mask ([TRA] section
+ * 2, "Exécution Efficace": the block-sparse backend fed by the tile lists;
+ * [BLOG] sections 4.1 and 9: scale 1/sqrt(d), masked keys excluded as -inf
+ * before the softmax):
  *   O_i = sum_{j retained by i} softmax_j(q_i . k_j / sqrt(d)) v_j
  * q, k, v, o: device [B, heads, N, d] of the plan's dtype; o must not alias
  * q, k or v.  q and k may differ from the tensors the plan was built from (plan
  * reuse).  Only listed tiles are visited.  The self key is always retained, so
- * every row is well defined.
+ * every row is well defined.  Asynchronous on `stream`; allocates nothing.
+ * The C ABI sees only pointers: tensors of another shape or dtype than the
+ * plan's cannot be detected here (call tra_plan_matches first, as the Python
+ * binding does).  TRA_ERR_PLAN_INVALID if the plan's last rebuild failed.
  */
 tra_status tra_attention(const tra_plan* plan, const void* q, const void* k, const void* v,
                          void* o, void* stream);
@@ -196,8 +217,9 @@ tra_status tra_attention(const tra_plan* plan, const void* q, const void* k, con
  * Re-run the planning steps of tra_plan_create on new q and k into an existing
  * plan (the refresh of a warm-up step), reusing its device buffers; the tile
  * list buffer grows when needed.  The shape and parameters are the plan's.
- * Synchronises `stream` once.  On failure the plan must not be used for
- * attention until a rebuild succeeds.
+ * Synchronises `stream` once.  On failure the plan is marked invalid: every
+ * call that reads it (attention, export, stats, drift) returns
+ * TRA_ERR_PLAN_INVALID until a rebuild succeeds.
  */
 tra_status tra_plan_rebuild(tra_plan* plan, const void* q, const void* k, void* stream);
 
@@ -236,7 +258,9 @@ tra_status tra_plan_export_groups(const tra_plan* plan, int64_t* n_groups, int64
                                   int32_t* glen, int32_t* glist, void* stream);
 
 /*
- * Exact pair counts of a plan (synchronises `stream`):
+ * Exact pair counts of a plan (synchronises `stream`; counters live in the
+ * plan, so nothing is allocated, and two stats or drift calls on one plan
+ * must not overlap):
  *   retained  sum over queries of the keys each attends to (the FLOPs that
  *             count: 4*d per pair): the keys it retains; with vote_threshold
  *             > 1 only those inside its tile's listed tiles (the votes of the
@@ -250,10 +274,11 @@ tra_status tra_plan_stats(const tra_plan* plan, int64_t* retained, int64_t* list
  * Plan drift (plans are reused across denoising steps, [TRA] section 2
  * "Reutilisation Inter-Etapes"): the number of queries whose budget level
  * would change if the plan were rebuilt from q and k.  Runs the pooling and
- * entropy steps on q and k into temporary device memory (allocated and freed
- * by this call) and compares the levels with the plan's; the plan is not
- * modified.  Under radius_override every level is -1 and the drift is 0.
- * Synchronises `stream`.
+ * entropy steps on q and k into scratch memory the plan owns (nothing is
+ * allocated per call; two stats or drift calls on one plan must not overlap)
+ * and compares the levels with the plan's; the plan's tile lists and levels
+ * are not modified.  Under radius_override every level is -1 and the drift is
+ * 0.  Synchronises `stream`.
  */
 tra_status tra_plan_drift(const tra_plan* plan, const void* q, const void* k, int64_t* changed,
                           void* stream);
@@ -288,6 +313,8 @@ tra_status tra_plan_create_from_entropy(const tra_shape* shape, const tra_params
  * tra_plan_create_from_entropy).  Pooled keys keep their last values. */
 tra_status tra_plan_rebuild_from_entropy(tra_plan* plan, const float* entropy, void* stream);
 
+/* Frees the plan.  hipFree waits for the device's outstanding work before it
+ * releases memory, so destroying a plan synchronises the device. */
 void tra_plan_destroy(tra_plan* plan);
 
 /*

@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -23,6 +24,70 @@ tra_status fail(tra_status s, const std::string& msg) {
   return s;
 }
 
+// Fault injection for tests of the error paths.  TRA_FAULT=alloc[:n] makes the
+// n-th device or pinned-host allocation (default the first) of an API call
+// fail as if the runtime were out of memory; TRA_FAULT=launch[:n] makes the
+// n-th kernel launch fail.  Read at the start of every call that allocates or
+// launches; unset (the normal case) it costs one getenv per call.
+enum { FAULT_NONE = 0, FAULT_ALLOC = 1, FAULT_LAUNCH = 2 };
+struct FaultState {
+  int kind = FAULT_NONE, at = 0, count = 0;
+};
+thread_local FaultState g_fault;
+
+void fault_arm() {
+  g_fault = FaultState{};
+  const char* f = std::getenv("TRA_FAULT");
+  if (!f || !*f) return;
+  int kind = FAULT_NONE;
+  const char* rest = f;
+  if (std::strncmp(f, "alloc", 5) == 0) {
+    kind = FAULT_ALLOC;
+    rest = f + 5;
+  } else if (std::strncmp(f, "launch", 6) == 0) {
+    kind = FAULT_LAUNCH;
+    rest = f + 6;
+  } else {
+    return;
+  }
+  int at = 1;
+  if (*rest == ':') at = std::atoi(rest + 1);
+  else if (*rest) return;
+  if (at < 1) return;
+  g_fault.kind = kind;
+  g_fault.at = at;
+}
+
+bool fault_hit(int kind) { return g_fault.kind == kind && ++g_fault.count == g_fault.at; }
+
+hipError_t dev_alloc(void** p, size_t bytes) {
+  *p = nullptr;
+  if (fault_hit(FAULT_ALLOC)) return hipErrorOutOfMemory;
+  return hipMalloc(p, bytes);
+}
+
+template <typename T>
+hipError_t dev_alloc(T** p, size_t bytes) {
+  void* v = nullptr;
+  const hipError_t e = dev_alloc(&v, bytes);
+  *p = static_cast<T*>(v);
+  return e;
+}
+
+template <typename T>
+hipError_t host_alloc(T** p, size_t bytes) {
+  *p = nullptr;
+  if (fault_hit(FAULT_ALLOC)) return hipErrorOutOfMemory;
+  void* v = nullptr;
+  const hipError_t e = hipHostMalloc(&v, bytes);
+  *p = static_cast<T*>(v);
+  return e;
+}
+
+// True when fault injection refuses the next kernel launch (which then does
+// not happen).
+bool launch_refused() { return fault_hit(FAULT_LAUNCH); }
+
 #define TRA_HIP(call)                                                                    \
   do {                                                                                   \
     hipError_t e_ = (call);                                                              \
@@ -31,6 +96,13 @@ tra_status fail(tra_status s, const std::string& msg) {
         return fail(TRA_ERR_OOM, std::string(#call) + ": " + hipGetErrorString(e_));     \
       return fail(TRA_ERR_HIP, std::string(#call) + ": " + hipGetErrorString(e_));       \
     }                                                                                    \
+  } while (0)
+
+// A kernel launch through one of the tra::launch_* wrappers.
+#define TRA_LAUNCH(call)                                                                  \
+  do {                                                                                   \
+    if (launch_refused()) return fail(TRA_ERR_HIP, std::string("injected launch failure: ") + #call); \
+    TRA_HIP(call);                                                                       \
   } while (0)
 
 bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -227,9 +299,19 @@ struct tra_plan {
   int64_t col2_cap = 0;
   unsigned long long* kept_votes = nullptr;  // device
   int64_t retained_votes = 0;
-  int64_t* totals_host = nullptr; // pinned
+  int64_t* totals_host = nullptr; // pinned, 8 entries
   int64_t nnz = 0;
   int32_t max_row_len = 0;
+  // Scratch owned by the plan for tra_plan_stats and tra_plan_drift, so that
+  // neither allocates per call: two pair counters and a level-difference
+  // counter, and (entropy plans) the pooled keys and levels of the inputs a
+  // drift query measures.
+  unsigned long long* counters = nullptr;  // device, 4 entries
+  void* kbar2 = nullptr;
+  int16_t* lv2 = nullptr;
+  // Set by a build that completed; cleared when a build starts, so a plan
+  // whose last build failed is refused by the calls that read it.
+  bool valid = false;
 };
 
 namespace {
@@ -238,7 +320,7 @@ void release(tra_plan* p) {
   if (!p) return;
   void* bufs[] = {p->kbar, p->H, p->lv, p->r2, p->dmax, p->r2c, p->r2off, p->pool_w,
                   p->counts, p->row_ptr, p->col_idx, p->runs, p->rowwin, p->glist, p->glen, p->gptr, p->totals, p->votes,
-                  p->row_ptr2, p->col_idx2, p->kept_votes};
+                  p->row_ptr2, p->col_idx2, p->kept_votes, p->counters, p->kbar2, p->lv2};
   for (void* b : bufs)
     if (b) (void)hipFree(b);
   if (p->totals_host) (void)hipHostFree(p->totals_host);
@@ -249,29 +331,30 @@ void release(tra_plan* p) {
 // come from the pooled-key entropy of (q, k), or, when `Hin` is not NULL, from
 // the given per-query entropies.
 tra_status build(tra_plan* p, const void* q, const void* k, const float* Hin, hipStream_t st) {
+  p->valid = false;
   const tra_shape& s = p->shape;
   const int d = s.head_dim;
   if (p->params.radius_override < 0.0) {
     tra::EntropyArgs ea{p->params.a, p->params.c, p->params.levels_per_nat, p->table.k_lo, p->table.k_hi};
     if (Hin) {
-      TRA_HIP(tra::launch_levels_from_entropy(Hin, p->n_queries, ea, p->H, p->lv, st));
+      TRA_LAUNCH(tra::launch_levels_from_entropy(Hin, p->n_queries, ea, p->H, p->lv, st));
     } else {
-      TRA_HIP(tra::launch_pool(s.dtype, d, k, p->kbar, p->BH, p->pool, st));
-      TRA_HIP(tra::launch_entropy(s.dtype, d, q, p->kbar, p->pool_w, p->BH, static_cast<int>(p->N),
+      TRA_LAUNCH(tra::launch_pool(s.dtype, d, k, p->kbar, p->BH, p->pool, st));
+      TRA_LAUNCH(tra::launch_entropy(s.dtype, d, q, p->kbar, p->pool_w, p->BH, static_cast<int>(p->N),
                                   p->pool.count, ea, p->H, p->lv, st));
     }
   } else {
-    TRA_HIP(tra::launch_fill_levels(p->lv, p->H, p->n_queries, st));
+    TRA_LAUNCH(tra::launch_fill_levels(p->lv, p->H, p->n_queries, st));
   }
   const bool window = p->params.generator == TRA_GEN_WINDOW_1D;
   if (window) {
-    TRA_HIP(tra::launch_window_csr(false, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, nullptr,
+    TRA_LAUNCH(tra::launch_window_csr(false, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, nullptr,
                                    p->counts, nullptr, st));
   } else {
-    TRA_HIP(tra::launch_csr_runs(p->params.generator == TRA_GEN_MANHATTAN, p->lv, p->r2, p->dmax, s.T, p->row_base,
+    TRA_LAUNCH(tra::launch_csr_runs(p->params.generator == TRA_GEN_MANHATTAN, p->lv, p->r2, p->dmax, s.T, p->row_base,
                                  p->BH, p->tiles, p->DM, p->counts, p->runs, p->rowwin, st));
   }
-  TRA_HIP(tra::launch_scan(p->counts, p->n_rows, p->row_ptr, p->totals, st));
+  TRA_LAUNCH(tra::launch_scan(p->counts, p->n_rows, p->row_ptr, p->totals, st));
   TRA_HIP(hipMemcpyAsync(p->totals_host, p->totals, 3 * sizeof(int64_t), hipMemcpyDeviceToHost, st));
   TRA_HIP(hipStreamSynchronize(st));
   if (p->totals_host[2]) return fail(TRA_ERR_OVERFLOW, "CSR has 2^31 or more entries");
@@ -282,14 +365,14 @@ tra_status build(tra_plan* p, const void* q, const void* k, const float* Hin, hi
     p->col_idx = nullptr;
     p->col_cap = 0;
     const int64_t cap = p->nnz + p->nnz / 8 + 64;
-    TRA_HIP(hipMalloc(&p->col_idx, cap * sizeof(int32_t)));
+    TRA_HIP(dev_alloc(&p->col_idx, cap * sizeof(int32_t)));
     p->col_cap = cap;
   }
   if (window) {
-    TRA_HIP(tra::launch_window_csr(true, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, p->row_ptr,
+    TRA_LAUNCH(tra::launch_window_csr(true, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, p->row_ptr,
                                    p->counts, p->col_idx, st));
   } else {
-    TRA_HIP(tra::launch_csr_expand(p->BH, p->tiles, p->DM, p->runs, p->rowwin, p->row_ptr, p->col_idx, st));
+    TRA_LAUNCH(tra::launch_csr_expand(p->BH, p->tiles, p->DM, p->runs, p->rowwin, p->row_ptr, p->col_idx, st));
   }
   const int theta = p->params.vote_threshold;
   const bool l1 = p->params.generator == TRA_GEN_MANHATTAN;
@@ -300,13 +383,13 @@ tra_status build(tra_plan* p, const void* q, const void* k, const float* Hin, hi
       if (p->votes) TRA_HIP(hipFree(p->votes));
       p->votes = nullptr;
       p->votes_cap = 0;
-      TRA_HIP(hipMalloc(&p->votes, p->col_cap * sizeof(int16_t)));
+      TRA_HIP(dev_alloc(&p->votes, p->col_cap * sizeof(int16_t)));
       p->votes_cap = p->col_cap;
     }
     TRA_HIP(hipMemsetAsync(p->kept_votes, 0, sizeof(unsigned long long), st));
-    TRA_HIP(tra::launch_votes(l1, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, p->row_ptr, p->col_idx,
+    TRA_LAUNCH(tra::launch_votes(l1, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, p->row_ptr, p->col_idx,
                               theta, p->votes, p->counts, p->kept_votes, st));
-    TRA_HIP(tra::launch_scan(p->counts, p->n_rows, p->row_ptr2, p->totals + 8, st));
+    TRA_LAUNCH(tra::launch_scan(p->counts, p->n_rows, p->row_ptr2, p->totals + 8, st));
     TRA_HIP(hipMemcpyAsync(p->totals_host, p->totals + 8, 2 * sizeof(int64_t), hipMemcpyDeviceToHost, st));
     TRA_HIP(hipMemcpyAsync(p->totals_host + 2, p->kept_votes, sizeof(int64_t), hipMemcpyDeviceToHost, st));
     TRA_HIP(hipStreamSynchronize(st));
@@ -316,10 +399,10 @@ tra_status build(tra_plan* p, const void* q, const void* k, const float* Hin, hi
       p->col_idx2 = nullptr;
       p->col2_cap = 0;
       const int64_t cap = nnz2 + nnz2 / 8 + 64;
-      TRA_HIP(hipMalloc(&p->col_idx2, cap * sizeof(int32_t)));
+      TRA_HIP(dev_alloc(&p->col_idx2, cap * sizeof(int32_t)));
       p->col2_cap = cap;
     }
-    TRA_HIP(tra::launch_vote_compact(p->n_rows, p->row_ptr, p->col_idx, p->votes, theta, p->row_ptr2, p->col_idx2,
+    TRA_LAUNCH(tra::launch_vote_compact(p->n_rows, p->row_ptr, p->col_idx, p->votes, theta, p->row_ptr2, p->col_idx2,
                                      st));
     std::swap(p->row_ptr, p->row_ptr2);
     std::swap(p->col_idx, p->col_idx2);
@@ -333,24 +416,25 @@ tra_status build(tra_plan* p, const void* q, const void* k, const float* Hin, hi
       if (p->glist) TRA_HIP(hipFree(p->glist));
       p->glist = nullptr;
       p->glist_cap = 0;
-      TRA_HIP(hipMalloc(&p->glist, p->col_cap * 2 * sizeof(int32_t)));
+      TRA_HIP(dev_alloc(&p->glist, p->col_cap * 2 * sizeof(int32_t)));
       p->glist_cap = p->col_cap;
     }
     if (window) {
-      TRA_HIP(tra::launch_window_groups(false, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, nullptr,
+      TRA_LAUNCH(tra::launch_window_groups(false, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, nullptr,
                                         nullptr, p->glen, st));
-      TRA_HIP(tra::launch_scan(p->glen, p->n_groups, p->gptr, p->totals + 4, st));
-      TRA_HIP(tra::launch_window_groups(true, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, p->gptr,
+      TRA_LAUNCH(tra::launch_scan(p->glen, p->n_groups, p->gptr, p->totals + 4, st));
+      TRA_LAUNCH(tra::launch_window_groups(true, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, p->gptr,
                                         p->glist, p->glen, st));
     } else {
       const int32_t* frp = theta > 1 ? p->row_ptr : nullptr;
-      TRA_HIP(tra::launch_group_lists(false, p->BH, p->tiles, p->DM, p->runs, p->rowwin, frp, p->col_idx, nullptr,
+      TRA_LAUNCH(tra::launch_group_lists(false, p->BH, p->tiles, p->DM, p->runs, p->rowwin, frp, p->col_idx, nullptr,
                                       nullptr, p->glen, st));
-      TRA_HIP(tra::launch_scan(p->glen, p->n_groups, p->gptr, p->totals + 4, st));
-      TRA_HIP(tra::launch_group_lists(true, p->BH, p->tiles, p->DM, p->runs, p->rowwin, frp, p->col_idx, p->gptr,
+      TRA_LAUNCH(tra::launch_scan(p->glen, p->n_groups, p->gptr, p->totals + 4, st));
+      TRA_LAUNCH(tra::launch_group_lists(true, p->BH, p->tiles, p->DM, p->runs, p->rowwin, frp, p->col_idx, p->gptr,
                                       p->glist, p->glen, st));
     }
   }
+  p->valid = true;
   return TRA_OK;
 }
 
@@ -410,36 +494,41 @@ tra_status create_plan(const tra_shape* shape, const tra_params* params, Table&&
                       std::string(#call) + ": " + hipGetErrorString(e_)));                     \
   } while (0)
 
-  TRA_HIP_P(hipGetDevice(&p->device));
   const size_t es = dtype_size(shape->dtype);
-  TRA_HIP_P(hipMalloc(&p->kbar, static_cast<size_t>(p->BH) * p->pool.count * shape->head_dim * es));
-  TRA_HIP_P(hipMalloc(&p->H, p->n_queries * sizeof(float)));
-  TRA_HIP_P(hipMalloc(&p->lv, p->n_queries * sizeof(int16_t)));
-  TRA_HIP_P(hipMalloc(&p->r2, p->table.r2.size() * sizeof(int32_t)));
-  TRA_HIP_P(hipMalloc(&p->dmax, p->table.dmax.size() * sizeof(int32_t)));
-  TRA_HIP_P(hipMalloc(&p->r2c, p->table.r2c.size() * sizeof(int32_t)));
-  TRA_HIP_P(hipMalloc(&p->r2off, p->table.r2off.size() * sizeof(int32_t)));
-  TRA_HIP_P(hipMalloc(&p->pool_w, static_cast<size_t>(p->pool.count) * sizeof(float)));
-  TRA_HIP_P(hipMalloc(&p->counts, p->n_rows * sizeof(int32_t)));
-  TRA_HIP_P(hipMalloc(&p->row_ptr, (p->n_rows + 1) * sizeof(int32_t)));
-  TRA_HIP_P(hipMalloc(&p->totals, 12 * sizeof(int64_t)));
+  TRA_HIP_P(dev_alloc(&p->kbar, static_cast<size_t>(p->BH) * p->pool.count * shape->head_dim * es));
+  TRA_HIP_P(dev_alloc(&p->H, p->n_queries * sizeof(float)));
+  TRA_HIP_P(dev_alloc(&p->lv, p->n_queries * sizeof(int16_t)));
+  TRA_HIP_P(dev_alloc(&p->r2, p->table.r2.size() * sizeof(int32_t)));
+  TRA_HIP_P(dev_alloc(&p->dmax, p->table.dmax.size() * sizeof(int32_t)));
+  TRA_HIP_P(dev_alloc(&p->r2c, p->table.r2c.size() * sizeof(int32_t)));
+  TRA_HIP_P(dev_alloc(&p->r2off, p->table.r2off.size() * sizeof(int32_t)));
+  TRA_HIP_P(dev_alloc(&p->pool_w, static_cast<size_t>(p->pool.count) * sizeof(float)));
+  TRA_HIP_P(dev_alloc(&p->counts, p->n_rows * sizeof(int32_t)));
+  TRA_HIP_P(dev_alloc(&p->row_ptr, (p->n_rows + 1) * sizeof(int32_t)));
+  TRA_HIP_P(dev_alloc(&p->totals, 12 * sizeof(int64_t)));
   if (params->vote_threshold > 1) {
-    TRA_HIP_P(hipMalloc(&p->row_ptr2, (p->n_rows + 1) * sizeof(int32_t)));
-    TRA_HIP_P(hipMalloc(&p->kept_votes, sizeof(unsigned long long)));
+    TRA_HIP_P(dev_alloc(&p->row_ptr2, (p->n_rows + 1) * sizeof(int32_t)));
+    TRA_HIP_P(dev_alloc(&p->kept_votes, sizeof(unsigned long long)));
   }
   for (int32_t dm : p->table.dmax) p->DM = std::max(p->DM, static_cast<int>(dm));
   if (params->generator != TRA_GEN_WINDOW_1D) {  // the window builds its lists without runs
     const int64_t run_entries = p->n_rows * (2 * p->DM + 1) * p->tiles.nh;
     if (run_entries > (int64_t(1) << 32)) return fin(fail(TRA_ERR_SHAPE, "tile-list run buffer too large"));
-    TRA_HIP_P(hipMalloc(&p->runs, run_entries * sizeof(int32_t)));
-    TRA_HIP_P(hipMalloc(&p->rowwin, p->n_rows * sizeof(int32_t)));
+    TRA_HIP_P(dev_alloc(&p->runs, run_entries * sizeof(int32_t)));
+    TRA_HIP_P(dev_alloc(&p->rowwin, p->n_rows * sizeof(int32_t)));
   }
   if (shape->dtype == TRA_BF16) {
     p->n_groups = tra::group_count(p->BH, p->tiles);
-    TRA_HIP_P(hipMalloc(&p->glen, p->n_groups * sizeof(int32_t)));
-    TRA_HIP_P(hipMalloc(&p->gptr, (p->n_groups + 1) * sizeof(int32_t)));
+    TRA_HIP_P(dev_alloc(&p->glen, p->n_groups * sizeof(int32_t)));
+    TRA_HIP_P(dev_alloc(&p->gptr, (p->n_groups + 1) * sizeof(int32_t)));
   }
-  TRA_HIP_P(hipHostMalloc(&p->totals_host, 4 * sizeof(int64_t)));
+  TRA_HIP_P(host_alloc(&p->totals_host, 8 * sizeof(int64_t)));
+  TRA_HIP_P(dev_alloc(&p->counters, 4 * sizeof(unsigned long long)));
+  if (params->radius_override < 0.0) {
+    TRA_HIP_P(dev_alloc(&p->kbar2, static_cast<size_t>(p->BH) * p->pool.count * shape->head_dim * es));
+    TRA_HIP_P(dev_alloc(&p->lv2, p->n_queries * sizeof(int16_t)));
+  }
+  TRA_HIP_P(hipGetDevice(&p->device));
 
   std::vector<float> w(p->pool.count);
   for (int b = 0; b < p->pool.count; ++b) {
@@ -474,12 +563,62 @@ tra_status check_entropy_ptr(const float* H) {
 
 }  // namespace
 
+namespace tra {
+
+size_t drift_scratch_bytes(const tra_plan* p) {
+  if (p->params.radius_override >= 0.0) return 0;
+  const size_t kbar = static_cast<size_t>(p->BH) * p->pool.count * p->shape.head_dim * dtype_size(p->shape.dtype);
+  const size_t lv = static_cast<size_t>(p->n_queries) * sizeof(int16_t);
+  return scratch_round(kbar) + scratch_round(lv) + scratch_round(sizeof(unsigned long long));
+}
+
+void drift_scratch_layout(const tra_plan* p, unsigned char* base, void** kbar, int16_t** lv,
+                          unsigned long long** counter) {
+  const size_t kb = static_cast<size_t>(p->BH) * p->pool.count * p->shape.head_dim * dtype_size(p->shape.dtype);
+  const size_t lb = static_cast<size_t>(p->n_queries) * sizeof(int16_t);
+  *kbar = base;
+  *lv = reinterpret_cast<int16_t*>(base + scratch_round(kb));
+  *counter = reinterpret_cast<unsigned long long*>(base + scratch_round(kb) + scratch_round(lb));
+}
+
+int plan_device(const tra_plan* p) { return p->device; }
+
+tra_status report(tra_status s, const std::string& msg) { return fail(s, msg); }
+
+tra_status drift_with_scratch(const tra_plan* plan, const void* q, const void* k, void* kbar, int16_t* lv,
+                              unsigned long long* counter, int64_t* changed, void* stream) {
+  if (!plan || !changed) return fail(TRA_ERR_INVALID_ARG, "plan and changed must not be NULL");
+  if (!plan->valid) return fail(TRA_ERR_PLAN_INVALID, "the plan's last build failed");
+  tra_status st = check_qk(q, k);
+  if (st != TRA_OK) return st;
+  *changed = 0;
+  if (plan->params.radius_override >= 0.0) return TRA_OK;
+  fault_arm();
+  const tra_shape& s = plan->shape;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  int64_t* host = plan->totals_host + 6;  // the plan's pinned word for the count
+  const EntropyArgs ea{plan->params.a, plan->params.c, plan->params.levels_per_nat, plan->table.k_lo,
+                       plan->table.k_hi};
+  TRA_LAUNCH(launch_clear_counters(counter, 1, hs));
+  TRA_LAUNCH(launch_pool(s.dtype, s.head_dim, k, kbar, plan->BH, plan->pool, hs));
+  TRA_LAUNCH(launch_entropy(s.dtype, s.head_dim, q, kbar, plan->pool_w, plan->BH, static_cast<int>(plan->N),
+                            plan->pool.count, ea, nullptr, lv, hs));
+  TRA_LAUNCH(launch_level_diff(plan->lv, lv, plan->n_queries, counter, hs));
+  TRA_HIP(hipMemcpyAsync(host, counter, sizeof(unsigned long long), hipMemcpyDeviceToHost, hs));
+  TRA_HIP(hipStreamSynchronize(hs));
+  *changed = *host;
+  return TRA_OK;
+}
+
+}  // namespace tra
+
 extern "C" {
 
 tra_status tra_plan_create(const tra_shape* shape, const tra_params* params, const void* q,
                            const void* k, void* stream, tra_plan** out) {
   if (!out) return fail(TRA_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
+  fault_arm();
   tra_status st = check_shape(shape);
   if (st != TRA_OK) return st;
   Table tab;
@@ -504,6 +643,7 @@ tra_status tra_plan_create_from_entropy(const tra_shape* shape, const tra_params
                                         const float* entropy, void* stream, tra_plan** out) {
   if (!out) return fail(TRA_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
+  fault_arm();
   tra_status st = check_shape(shape);
   if (st != TRA_OK) return st;
   Table tab;
@@ -528,6 +668,7 @@ tra_status tra_plan_rebuild_from_entropy(tra_plan* plan, const float* entropy, v
   if (!plan) return fail(TRA_ERR_INVALID_ARG, "plan is NULL");
   const tra_status st = check_entropy_ptr(entropy);
   if (st != TRA_OK) return st;
+  fault_arm();
   return build(plan, nullptr, nullptr, entropy, static_cast<hipStream_t>(stream));
 }
 
@@ -547,7 +688,8 @@ tra_status tra_dense_attention(const tra_shape* shape, const void* q, const void
     return fail(TRA_ERR_INVALID_ARG, "entropy must be 4-byte aligned");
   const int BH = shape->B * shape->heads;
   const int N = shape->T * shape->H * shape->W;
-  TRA_HIP(tra::launch_dense(shape->dtype, shape->head_dim, q, k, v, o, entropy, BH, N,
+  fault_arm();
+  TRA_LAUNCH(tra::launch_dense(shape->dtype, shape->head_dim, q, k, v, o, entropy, BH, N,
                             static_cast<hipStream_t>(stream)));
   return TRA_OK;
 }
@@ -560,11 +702,13 @@ tra_status tra_attention(const tra_plan* plan, const void* q, const void* k, con
        reinterpret_cast<uintptr_t>(o)) & 15)
     return fail(TRA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
   if (o == q || o == k || o == v) return fail(TRA_ERR_INVALID_ARG, "o must not alias q, k or v");
+  if (!plan->valid) return fail(TRA_ERR_PLAN_INVALID, "the plan's last build failed");
+  fault_arm();
   const tra_shape& s = plan->shape;
   const tra::RadiusTable tab{plan->r2, plan->dmax, plan->r2c, plan->r2off,
                              static_cast<int>(plan->table.r2c.size()), s.T,
                              metric_of(plan->params)};
-  TRA_HIP(tra::launch_attention(s.dtype, s.head_dim, q, k, v, o, plan->lv, tab, plan->row_base,
+  TRA_LAUNCH(tra::launch_attention(s.dtype, s.head_dim, q, k, v, o, plan->lv, tab, plan->row_base,
                                 plan->BH, plan->tiles, plan->row_ptr, plan->col_idx,
                                 plan->gptr, plan->glist, plan->glen, plan->params.block_mask != 0,
                                 plan->params.vote_threshold == 1, static_cast<hipStream_t>(stream)));
@@ -575,6 +719,7 @@ tra_status tra_plan_rebuild(tra_plan* plan, const void* q, const void* k, void* 
   if (!plan) return fail(TRA_ERR_INVALID_ARG, "plan is NULL");
   const tra_status st = check_qk(q, k);
   if (st != TRA_OK) return st;
+  fault_arm();
   return build(plan, q, k, nullptr, static_cast<hipStream_t>(stream));
 }
 
@@ -604,6 +749,7 @@ tra_status tra_plan_get_info(const tra_plan* plan, tra_plan_info* info) {
 tra_status tra_plan_export(const tra_plan* plan, int16_t* levels, float* entropy, int32_t* r2,
                            int32_t* row_ptr, int32_t* col_idx, void* kbar, void* stream) {
   if (!plan) return fail(TRA_ERR_INVALID_ARG, "plan is NULL");
+  if (!plan->valid) return fail(TRA_ERR_PLAN_INVALID, "the plan's last build failed");
   hipStream_t hs = static_cast<hipStream_t>(stream);
   TRA_HIP(hipStreamSynchronize(hs));
   if (levels) TRA_HIP(hipMemcpy(levels, plan->lv, plan->n_queries * sizeof(int16_t), hipMemcpyDeviceToHost));
@@ -623,6 +769,7 @@ tra_status tra_plan_export(const tra_plan* plan, int16_t* levels, float* entropy
 tra_status tra_plan_export_groups(const tra_plan* plan, int64_t* n_groups, int64_t* n_entries, int32_t* gptr,
                                   int32_t* glen, int32_t* glist, void* stream) {
   if (!plan) return fail(TRA_ERR_INVALID_ARG, "plan is NULL");
+  if (!plan->valid) return fail(TRA_ERR_PLAN_INVALID, "the plan's last build failed");
   if (plan->shape.dtype != TRA_BF16) return fail(TRA_ERR_DTYPE, "group lists exist for bf16 plans only");
   hipStream_t hs = static_cast<hipStream_t>(stream);
   TRA_HIP(hipStreamSynchronize(hs));
@@ -641,23 +788,23 @@ tra_status tra_plan_export_groups(const tra_plan* plan, int64_t* n_groups, int64
 
 tra_status tra_plan_stats(const tra_plan* plan, int64_t* retained, int64_t* listed, void* stream) {
   if (!plan) return fail(TRA_ERR_INVALID_ARG, "plan is NULL");
+  if (!plan->valid) return fail(TRA_ERR_PLAN_INVALID, "the plan's last build failed");
+  fault_arm();
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  unsigned long long* dev = nullptr;
-  TRA_HIP(hipMalloc(&dev, 2 * sizeof(unsigned long long)));
-  unsigned long long host[2] = {0, 0};
-  hipError_t e = hipMemsetAsync(dev, 0, 2 * sizeof(unsigned long long), hs);
-  if (e == hipSuccess)
-    e = tra::launch_stats(metric_of(plan->params), plan->lv, plan->r2, plan->shape.T, plan->row_base, plan->BH, plan->tiles,
-                          plan->row_ptr, plan->col_idx, dev, hs);
-  if (e == hipSuccess) e = hipMemcpyAsync(host, dev, sizeof(host), hipMemcpyDeviceToHost, hs);
-  if (e == hipSuccess) e = hipStreamSynchronize(hs);
-  (void)hipFree(dev);
-  if (e != hipSuccess) return fail(TRA_ERR_HIP, std::string("tra_plan_stats: ") + hipGetErrorString(e));
+  // The plan's own counters and pinned words (a plan is not used by two
+  // stats or drift calls at once).
+  tra_plan* p = const_cast<tra_plan*>(plan);
+  TRA_LAUNCH(tra::launch_clear_counters(p->counters, 2, hs));
+  TRA_LAUNCH(tra::launch_stats(metric_of(plan->params), plan->lv, plan->r2, plan->shape.T, plan->row_base, plan->BH,
+                               plan->tiles, plan->row_ptr, plan->col_idx, p->counters, hs));
+  TRA_HIP(hipMemcpyAsync(p->totals_host + 4, p->counters, 2 * sizeof(unsigned long long), hipMemcpyDeviceToHost, hs));
+  TRA_HIP(hipStreamSynchronize(hs));
+  uint64_t host[2] = {static_cast<uint64_t>(p->totals_host[4]), static_cast<uint64_t>(p->totals_host[5])};
   // Pairs the attention visits under the plan's semantics: block-only masks
   // keep every pair of a listed tile pair; a vote threshold keeps the votes
   // of the listed tiles.
   if (plan->params.block_mask) host[0] = host[1];
-  else if (plan->params.vote_threshold > 1) host[0] = static_cast<unsigned long long>(plan->retained_votes);
+  else if (plan->params.vote_threshold > 1) host[0] = static_cast<uint64_t>(plan->retained_votes);
   if (retained) *retained = static_cast<int64_t>(host[0]);
   if (listed) *listed = static_cast<int64_t>(host[1]);
   return TRA_OK;
@@ -665,46 +812,14 @@ tra_status tra_plan_stats(const tra_plan* plan, int64_t* retained, int64_t* list
 
 tra_status tra_plan_drift(const tra_plan* plan, const void* q, const void* k, int64_t* changed,
                           void* stream) {
-  if (!plan || !changed) return fail(TRA_ERR_INVALID_ARG, "plan and changed must not be NULL");
-  if (!q || !k) return fail(TRA_ERR_INVALID_ARG, "q and k must be device pointers");
-  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k)) & 15)
-    return fail(TRA_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
-  *changed = 0;
-  if (plan->params.radius_override >= 0.0) return TRA_OK;
-  const tra_shape& s = plan->shape;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  const size_t kbar_bytes = static_cast<size_t>(plan->BH) * plan->pool.count * s.head_dim * dtype_size(s.dtype);
-  void* kbar = nullptr;
-  float* H = nullptr;
-  int16_t* lv = nullptr;
-  unsigned long long* dev = nullptr;
-  hipError_t e = hipMalloc(&kbar, kbar_bytes);
-  if (e == hipSuccess) e = hipMalloc(&H, plan->n_queries * sizeof(float));
-  if (e == hipSuccess) e = hipMalloc(&lv, plan->n_queries * sizeof(int16_t));
-  if (e == hipSuccess) e = hipMalloc(&dev, sizeof(unsigned long long));
-  unsigned long long host = 0;
-  if (e == hipSuccess) e = hipMemsetAsync(dev, 0, sizeof(unsigned long long), hs);
-  if (e == hipSuccess) e = tra::launch_pool(s.dtype, s.head_dim, k, kbar, plan->BH, plan->pool, hs);
-  if (e == hipSuccess) {
-    const tra::EntropyArgs ea{plan->params.a, plan->params.c, plan->params.levels_per_nat, plan->table.k_lo,
-                              plan->table.k_hi};
-    e = tra::launch_entropy(s.dtype, s.head_dim, q, kbar, plan->pool_w, plan->BH, static_cast<int>(plan->N),
-                            plan->pool.count, ea, H, lv, hs);
-  }
-  if (e == hipSuccess) e = tra::launch_level_diff(plan->lv, lv, plan->n_queries, dev, hs);
-  if (e == hipSuccess) e = hipMemcpyAsync(&host, dev, sizeof(host), hipMemcpyDeviceToHost, hs);
-  if (e == hipSuccess) e = hipStreamSynchronize(hs);
-  for (void* b : {kbar, static_cast<void*>(H), static_cast<void*>(lv), static_cast<void*>(dev)})
-    if (b) (void)hipFree(b);
-  if (e != hipSuccess)
-    return fail(e == hipErrorOutOfMemory ? TRA_ERR_OOM : TRA_ERR_HIP, std::string("tra_plan_drift: ") + hipGetErrorString(e));
-  *changed = static_cast<int64_t>(host);
-  return TRA_OK;
+  if (!plan) return fail(TRA_ERR_INVALID_ARG, "plan is NULL");
+  tra_plan* p = const_cast<tra_plan*>(plan);
+  return tra::drift_with_scratch(plan, q, k, p->kbar2, p->lv2, p->counters + 2, changed, stream);
 }
 
 void tra_plan_destroy(tra_plan* plan) {
-  if (!plan) return;
-  (void)hipDeviceSynchronize();
+  // hipFree waits for the device's outstanding work before it releases
+  // memory, so no explicit synchronisation is needed here.
   release(plan);
 }
 
@@ -790,18 +905,19 @@ tra_status tra_schedule_create(const tra_shape* shape, const tra_params* params,
     return fail(e == hipErrorOutOfMemory ? TRA_ERR_OOM : TRA_ERR_HIP, std::string("tra_schedule_create: ") +
                                                                          hipGetErrorString(e));
   };
-  hipError_t e = hipMalloc(&s->Hd, s->n_queries * sizeof(float));
+  fault_arm();
+  hipError_t e = dev_alloc(&s->Hd, s->n_queries * sizeof(float));
   if (e != hipSuccess) return fin(e);
   if (tracks_drift(s)) {
     const tra::Grid pool = tra::make_grid(shape->T, shape->H, shape->W, params->pool_h, params->pool_w);
     const size_t kb = static_cast<size_t>(shape->B) * shape->heads * pool.count * shape->head_dim *
                       dtype_size(shape->dtype);
-    if ((e = hipMalloc(&s->kbar, kb)) != hipSuccess) return fin(e);
-    if ((e = hipMalloc(&s->Hp, s->n_queries * sizeof(float))) != hipSuccess) return fin(e);
-    if ((e = hipMalloc(&s->lv_ref, s->n_queries * sizeof(int16_t))) != hipSuccess) return fin(e);
-    if ((e = hipMalloc(&s->lv_now, s->n_queries * sizeof(int16_t))) != hipSuccess) return fin(e);
-    if ((e = hipMalloc(&s->cnt, sizeof(unsigned long long))) != hipSuccess) return fin(e);
-    if ((e = hipHostMalloc(&s->cnt_host, sizeof(unsigned long long))) != hipSuccess) return fin(e);
+    if ((e = dev_alloc(&s->kbar, kb)) != hipSuccess) return fin(e);
+    if ((e = dev_alloc(&s->Hp, s->n_queries * sizeof(float))) != hipSuccess) return fin(e);
+    if ((e = dev_alloc(&s->lv_ref, s->n_queries * sizeof(int16_t))) != hipSuccess) return fin(e);
+    if ((e = dev_alloc(&s->lv_now, s->n_queries * sizeof(int16_t))) != hipSuccess) return fin(e);
+    if ((e = dev_alloc(&s->cnt, sizeof(unsigned long long))) != hipSuccess) return fin(e);
+    if ((e = host_alloc(&s->cnt_host, sizeof(unsigned long long))) != hipSuccess) return fin(e);
   }
   *out = s;
   return TRA_OK;
@@ -841,7 +957,7 @@ tra_status tra_schedule_step(tra_schedule* s, const void* q, const void* k, cons
     if (tracks_drift(s)) {
       TRA_HIP(pooled_levels(s, q, k, s->lv_now, hs));
       TRA_HIP(hipMemsetAsync(s->cnt, 0, sizeof(unsigned long long), hs));
-      TRA_HIP(tra::launch_level_diff(s->lv_ref, s->lv_now, s->n_queries, s->cnt, hs));
+      TRA_LAUNCH(tra::launch_level_diff(s->lv_ref, s->lv_now, s->n_queries, s->cnt, hs));
       TRA_HIP(hipMemcpyAsync(s->cnt_host, s->cnt, sizeof(unsigned long long), hipMemcpyDeviceToHost, hs));
       TRA_HIP(hipStreamSynchronize(hs));
       drift = static_cast<int64_t>(*s->cnt_host);
@@ -865,8 +981,7 @@ tra_status tra_schedule_plan(const tra_schedule* s, const tra_plan** plan) {
 }
 
 void tra_schedule_destroy(tra_schedule* s) {
-  if (!s) return;
-  (void)hipDeviceSynchronize();
+  // As for plans: hipFree itself waits for outstanding work.
   release_schedule(s);
 }
 
@@ -880,6 +995,7 @@ const char* tra_status_string(tra_status s) {
     case TRA_ERR_OOM: return "TRA_ERR_OOM";
     case TRA_ERR_OVERFLOW: return "TRA_ERR_OVERFLOW";
     case TRA_ERR_HIP: return "TRA_ERR_HIP";
+    case TRA_ERR_PLAN_INVALID: return "TRA_ERR_PLAN_INVALID";
   }
   return "TRA_ERR_UNKNOWN";
 }

@@ -5,6 +5,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <string>
+
+#include "tra.h"
+
 namespace tra {
 
 // Geometry of one head's T x H x W grid cut into th x tw rectangles per frame.
@@ -113,6 +117,8 @@ hipError_t launch_vote_compact(int64_t n_rows, const int32_t* row_ptr, const int
 // plus a compact radius table of n_r2c entries; 0 if it exceeds the device limit.
 size_t attention_lds_bytes(int d, int n_r2c);
 
+// Sets n <= 64 counters to zero (a kernel, so that callers may capture it).
+hipError_t launch_clear_counters(unsigned long long* p, int n, hipStream_t s);
 // Count of positions where two level arrays differ, added to *out.
 hipError_t launch_level_diff(const int16_t* a, const int16_t* b, int64_t n, unsigned long long* out,
                              hipStream_t s);
@@ -129,5 +135,20 @@ hipError_t launch_levels_from_entropy(const float* Hin, int64_t n, const Entropy
 hipError_t launch_stats(int metric, const int16_t* lv, const int32_t* r2, int T, int row_base, int BH,
                         const Grid& tiles, const int32_t* row_ptr, const int32_t* col_idx,
                         unsigned long long* out2, hipStream_t s);
+
+// Plan drift (tra_plan_drift) with its scratch in the given device memory:
+// the pooled keys of k (drift_scratch_bytes' first part), the levels of (q, k)
+// and one counter.  Used with the plan's own scratch and with the library's
+// static scratch.
+size_t drift_scratch_bytes(const tra_plan* p);
+// The three parts inside drift_scratch_bytes(p) bytes at `base` (each 256-byte aligned).
+void drift_scratch_layout(const tra_plan* p, unsigned char* base, void** kbar, int16_t** lv,
+                          unsigned long long** counter);
+inline size_t scratch_round(size_t bytes) { return (bytes + 255) & ~static_cast<size_t>(255); }
+tra_status drift_with_scratch(const tra_plan* plan, const void* q, const void* k, void* kbar, int16_t* lv,
+                              unsigned long long* counter, int64_t* changed, void* stream);
+int plan_device(const tra_plan* p);
+// Records `msg` as the calling thread's last error (tra_last_error) and returns s.
+tra_status report(tra_status s, const std::string& msg);
 
 }  // namespace tra

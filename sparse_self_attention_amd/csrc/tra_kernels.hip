@@ -134,7 +134,7 @@ __device__ __forceinline__ void entropy_store(double Hd, const EntropyArgs& ea, 
   const double L = static_cast<double>(ea.levels_per_nat) * (ea.a * Hd + ea.c);
   double kf = floor(L);
   kf = fmin(fmax(kf, static_cast<double>(ea.k_lo)), static_cast<double>(ea.k_hi));
-  Hout[idx] = static_cast<float>(Hd);
+  if (Hout) Hout[idx] = static_cast<float>(Hd);  // the entropy itself is optional (export only)
   lvout[idx] = static_cast<int16_t>(kf);
 }
 
@@ -1713,6 +1713,14 @@ __global__ __launch_bounds__(256) void level_diff_kernel(const int16_t* __restri
   if ((threadIdx.x & 63) == 0 && cnt) atomicAdd(out, cnt);
 }
 
+__global__ __launch_bounds__(64) void clear_u64_kernel(unsigned long long* __restrict__ p, int n) {
+  if (static_cast<int>(threadIdx.x) < n) p[threadIdx.x] = 0;
+}
+hipError_t launch_clear_counters(unsigned long long* p, int n, hipStream_t s) {
+  if (n < 1 || n > 64) return hipErrorInvalidValue;
+  clear_u64_kernel<<<1, 64, 0, s>>>(p, n);
+  return hipGetLastError();
+}
 hipError_t launch_level_diff(const int16_t* a, const int16_t* b, int64_t n, unsigned long long* out,
                              hipStream_t s) {
   const int64_t blocks = (n + 255) / 256;

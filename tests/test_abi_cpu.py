@@ -197,3 +197,78 @@ def test_schedule_rejects_bad_arguments_before_any_device_call():
                                         ctypes.byref(tra._SchedParams(1, 0, -1.0)), ctypes.byref(out))) \
         == "TRA_ERR_DTYPE"
     assert name(lib.tra_schedule_step(None, None, None, None, None, None, None)) == "TRA_ERR_INVALID_ARG"
+
+
+# ---------------------------------------------------------------------------
+# Failure handling forced from the host (TRA_FAULT), with no device work: the
+# injected failure comes before any runtime call that would need a GPU.
+# ---------------------------------------------------------------------------
+@pytest.fixture
+def fault(monkeypatch):
+    def arm(value):
+        monkeypatch.setenv("TRA_FAULT", value)
+    yield arm
+
+
+def _name(st):
+    return tra.load_library().tra_status_string(st).decode()
+
+
+def test_injected_allocation_failure_in_plan_create(fault):
+    lib = tra.load_library()
+    fault("alloc")
+    out = ctypes.c_void_p(1234)
+    prm = tra._make_params({})
+    q = ctypes.c_void_p(4096)
+    st = lib.tra_plan_create(ctypes.byref(_shape()), ctypes.byref(prm), q, q, None, ctypes.byref(out))
+    assert _name(st) == "TRA_ERR_OOM"
+    assert out.value is None
+    assert b"out of memory" in lib.tra_last_error().lower() or b"alloc" in lib.tra_last_error()
+    fault("alloc:1")
+    st = lib.tra_plan_create_from_entropy(ctypes.byref(_shape()), ctypes.byref(prm), q, None, ctypes.byref(out))
+    assert _name(st) == "TRA_ERR_OOM" and out.value is None
+
+
+def test_injected_allocation_failure_in_schedule_create(fault):
+    lib = tra.load_library()
+    fault("alloc")
+    out = ctypes.c_void_p(1234)
+    st = lib.tra_schedule_create(ctypes.byref(_shape()), ctypes.byref(tra._make_params({})),
+                                 ctypes.byref(tra._SchedParams(2, 0, 0.1)), ctypes.byref(out))
+    assert _name(st) == "TRA_ERR_OOM" and out.value is None
+
+
+def test_injected_launch_failure_is_distinct(fault):
+    lib = tra.load_library()
+    fault("launch")
+    P = ctypes.c_void_p
+    st = lib.tra_dense_attention(ctypes.byref(_shape()), P(4096), P(8192), P(12288), P(16384), None, None)
+    assert _name(st) == "TRA_ERR_HIP"
+    assert b"injected launch failure" in lib.tra_last_error()
+
+
+@pytest.mark.parametrize("value", ["", "none", "alloc:0", "launch:x", "allocate"])
+def test_unrecognised_fault_settings_inject_nothing(fault, value):
+    """A malformed TRA_FAULT arms nothing: the call then fails for its real
+    reason on this machine (no GPU), not with an injected status."""
+    lib = tra.load_library()
+    fault(value)
+    P = ctypes.c_void_p
+    lib.tra_dense_attention(ctypes.byref(_shape()), P(4096), P(8192), P(12288), P(16384), None, None)
+    assert b"injected" not in lib.tra_last_error()
+
+
+def test_plan_invalid_status_string():
+    assert _name(8) == "TRA_ERR_PLAN_INVALID"
+
+
+def test_null_plan_is_rejected_by_every_plan_call():
+    lib = tra.load_library()
+    P = ctypes.c_void_p
+    n, m = ctypes.c_int64(), ctypes.c_int64()
+    assert _name(lib.tra_attention(None, P(4096), P(4096), P(4096), P(8192), None)) == "TRA_ERR_INVALID_ARG"
+    assert _name(lib.tra_plan_stats(None, ctypes.byref(n), ctypes.byref(m), None)) == "TRA_ERR_INVALID_ARG"
+    assert _name(lib.tra_plan_drift(None, P(4096), P(4096), ctypes.byref(n), None)) == "TRA_ERR_INVALID_ARG"
+    assert _name(lib.tra_plan_export(None, None, None, None, None, None, None, None)) == "TRA_ERR_INVALID_ARG"
+    assert _name(lib.tra_plan_rebuild(None, P(4096), P(4096), None)) == "TRA_ERR_INVALID_ARG"
+    lib.tra_plan_destroy(None)  # a no-op
