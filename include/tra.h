@@ -50,6 +50,7 @@
 #ifndef TRA_H
 #define TRA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -282,6 +283,21 @@ tra_status tra_plan_stats(const tra_plan* plan, int64_t* retained, int64_t* list
  */
 tra_status tra_plan_drift(const tra_plan* plan, const void* q, const void* k, int64_t* changed,
                           void* stream);
+
+/*
+ * tra_plan_drift for callers that cannot allocate device memory (code under
+ * stream capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same count, computed in a static device buffer of the library instead of the
+ * plan's scratch.  That buffer holds tra_drift_noalloc_max_bytes() bytes (32
+ * MiB) per GPU, kept until the process ends; a plan whose drift needs more
+ * (pooled keys plus 2 bytes per query, each part rounded to 256 bytes) is
+ * refused with TRA_ERR_SHAPE.  Calls that overlap on one GPU share the buffer
+ * and race: serialise them.  Must be called with the plan's device current.
+ * Synchronises `stream`.
+ */
+tra_status tra_plan_drift_noalloc(const tra_plan* plan, const void* q, const void* k, int64_t* changed,
+                                  void* stream);
+size_t tra_drift_noalloc_max_bytes(void);
 
 /*
  * Dense warm-up pass ([TRA] section 2, "Le Pipeline TRA", entropy-to-budget

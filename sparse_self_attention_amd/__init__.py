@@ -21,7 +21,7 @@ import torch
 
 __all__ = ["TraError", "Plan", "plan", "plan_from_entropy", "attention", "dense_attention", "Schedule",
            "STEP_MODES", "radius_table",
-           "validate", "library_path",
+           "validate", "library_path", "drift_noalloc_max_bytes",
            "load_library", "DEFAULT_PARAMS", "EXPORTED_SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -77,6 +77,8 @@ _SIGS = {
     "tra_plan_stats": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int64),
                                       ctypes.POINTER(ctypes.c_int64), _P]),
     "tra_plan_drift": (ctypes.c_int, [_P, _P, _P, ctypes.POINTER(ctypes.c_int64), _P]),
+    "tra_plan_drift_noalloc": (ctypes.c_int, [_P, _P, _P, ctypes.POINTER(ctypes.c_int64), _P]),
+    "tra_drift_noalloc_max_bytes": (ctypes.c_size_t, []),
     "tra_plan_create_from_entropy": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.POINTER(_Params), _P, _P,
                                                     ctypes.POINTER(_P)]),
     "tra_plan_rebuild_from_entropy": (ctypes.c_int, [_P, _P, _P]),
@@ -277,6 +279,18 @@ class Plan:
                                              _stream(self.device)), "tra_plan_drift")
         return n.value
 
+    def drift_noalloc(self, q, k):
+        """`drift` computed in the library's static scratch: allocates no device
+        memory (for callers that cannot allocate).  Calls that overlap on one
+        GPU share that scratch and must not run concurrently."""
+        self._check_tensor(q, "q")
+        self._check_tensor(k, "k")
+        n = ctypes.c_int64()
+        _check(load_library().tra_plan_drift_noalloc(self.handle, _dev_ptr(q, "q"), _dev_ptr(k, "k"),
+                                                     ctypes.byref(n), _stream(self.device)),
+               "tra_plan_drift_noalloc")
+        return n.value
+
     def rebuild_from_entropy(self, entropy):
         """Re-plan from per-query entropies ([B, heads, N] float32 device tensor)."""
         _check_entropy(entropy, self.shape)
@@ -299,6 +313,11 @@ class Plan:
             self.destroy()
         except Exception:
             pass
+
+
+def drift_noalloc_max_bytes():
+    """Size of the static scratch `Plan.drift_noalloc` works in (bytes per GPU)."""
+    return int(load_library().tra_drift_noalloc_max_bytes())
 
 
 def plan(q, k, grid, **params):

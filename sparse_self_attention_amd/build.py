@@ -10,7 +10,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libtra.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("tra_api.cpp", "tra_kernels.hip", "tra_dense.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("tra_api.cpp", "tra_kernels.hip", "tra_dense.hip", "tra_noalloc.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("TRA_OFFLOAD_ARCH", "gfx950")
 
