@@ -45,7 +45,10 @@
  *     matrix cores), dtype TRA_F32 with head_dim 64 or 128 (fp32 vector path),
  *     8 x 8 tiles (tile_h = tile_w = 8).  T, H, W <= 32767;
  *     B*heads*T*H*W < 2^31; for TRA_BF16 one head's K (T*H*W*head_dim*2 bytes)
- *     below 2^31.  Larger shapes fail with TRA_ERR_SHAPE.
+ *     below 2^31.  Larger shapes fail with TRA_ERR_SHAPE.  The radius table's
+ *     active entries plus two words per level row must fit 64 KB (the
+ *     tile-list kernel stages them in LDS); larger tables fail with
+ *     TRA_ERR_INVALID_ARG.
  */
 #ifndef TRA_H
 #define TRA_H

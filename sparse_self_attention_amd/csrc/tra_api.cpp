@@ -243,6 +243,8 @@ tra_status check_params(const tra_shape* s, const tra_params* p, Table* tab) {
     t.r2off[r] = static_cast<int32_t>(t.r2c.size());
     for (int dl = 0; dl <= t.dmax[r]; ++dl) t.r2c.push_back(t.r2[static_cast<size_t>(r) * T + dl]);
   }
+  if ((2 * static_cast<size_t>(t.n_levels) + t.r2c.size()) * sizeof(int32_t) > 65536)
+    return fail(TRA_ERR_INVALID_ARG, "radius table too large for the tile-list kernel's LDS");
   if (s->dtype == TRA_BF16 && tra::attention_lds_bytes(s->head_dim, static_cast<int>(t.r2c.size())) > 163840)
     return fail(TRA_ERR_INVALID_ARG, "radius table too large for the attention kernel's LDS");
   if (tab) *tab = std::move(t);
@@ -327,6 +329,11 @@ void release(tra_plan* p) {
   delete p;
 }
 
+tra::RadiusTable radius_table_of(const tra_plan* p) {
+  return tra::RadiusTable{p->r2, p->dmax, p->r2c, p->r2off, static_cast<int>(p->table.r2c.size()), p->shape.T,
+                          metric_of(p->params)};
+}
+
 // Steps entropy -> level -> tile lists into the plan's buffers.  The levels
 // come from the pooled-key entropy of (q, k), or, when `Hin` is not NULL, from
 // the given per-query entropies.
@@ -341,7 +348,7 @@ tra_status build(tra_plan* p, const void* q, const void* k, const float* Hin, hi
     } else {
       TRA_LAUNCH(tra::launch_pool(s.dtype, d, k, p->kbar, p->BH, p->pool, st));
       TRA_LAUNCH(tra::launch_entropy(s.dtype, d, q, p->kbar, p->pool_w, p->BH, static_cast<int>(p->N),
-                                  p->pool.count, ea, p->H, p->lv, st));
+                                     p->pool.count, ea, p->H, p->lv, st));
     }
   } else {
     TRA_LAUNCH(tra::launch_fill_levels(p->lv, p->H, p->n_queries, st));
@@ -351,8 +358,9 @@ tra_status build(tra_plan* p, const void* q, const void* k, const float* Hin, hi
     TRA_LAUNCH(tra::launch_window_csr(false, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, nullptr,
                                    p->counts, nullptr, st));
   } else {
-    TRA_LAUNCH(tra::launch_csr_runs(p->params.generator == TRA_GEN_MANHATTAN, p->lv, p->r2, p->dmax, s.T, p->row_base,
-                                 p->BH, p->tiles, p->DM, p->counts, p->runs, p->rowwin, st));
+    TRA_LAUNCH(tra::launch_csr_runs(p->params.generator == TRA_GEN_MANHATTAN, p->lv, radius_table_of(p),
+                                    p->table.n_levels, p->row_base, p->BH, p->tiles, p->DM, p->counts, p->runs,
+                                    p->rowwin, st));
   }
   TRA_LAUNCH(tra::launch_scan(p->counts, p->n_rows, p->row_ptr, p->totals, st));
   TRA_HIP(hipMemcpyAsync(p->totals_host, p->totals, 3 * sizeof(int64_t), hipMemcpyDeviceToHost, st));
@@ -705,9 +713,7 @@ tra_status tra_attention(const tra_plan* plan, const void* q, const void* k, con
   if (!plan->valid) return fail(TRA_ERR_PLAN_INVALID, "the plan's last build failed");
   fault_arm();
   const tra_shape& s = plan->shape;
-  const tra::RadiusTable tab{plan->r2, plan->dmax, plan->r2c, plan->r2off,
-                             static_cast<int>(plan->table.r2c.size()), s.T,
-                             metric_of(plan->params)};
+  const tra::RadiusTable tab = radius_table_of(plan);
   TRA_LAUNCH(tra::launch_attention(s.dtype, s.head_dim, q, k, v, o, plan->lv, tab, plan->row_base,
                                 plan->BH, plan->tiles, plan->row_ptr, plan->col_idx,
                                 plan->gptr, plan->glist, plan->glen, plan->params.block_mask != 0,

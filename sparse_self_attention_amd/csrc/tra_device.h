@@ -21,11 +21,15 @@ __device__ __forceinline__ float bf16_to_float(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// Integer square root floor(sqrt(x)) for 0 <= x < 2^31.
+// Integer square root floor(sqrt(x)) for 0 <= x < 2^31.  The hardware square
+// root (v_sqrt_f32, about 1 ulp) of float(x) (exact below 2^24, within 2^-24
+// relative above) lands within 0.02 of sqrt(x), so its truncation is off by at
+// most one either way, and one exact integer correction in each direction
+// gives the floor.
 __device__ __forceinline__ int isqrt_i(int x) {
   // r <= 46341 here, so r*r and (r+1)*(r+1) stay below 2^31 + 2^17 and are
   // compared as unsigned 32-bit values.
-  unsigned r = static_cast<unsigned>(sqrtf(static_cast<float>(x)));
+  unsigned r = static_cast<unsigned>(__builtin_amdgcn_sqrtf(static_cast<float>(x)));
   const unsigned ux = static_cast<unsigned>(x);
   r -= (r * r > ux);
   r += ((r + 1) * (r + 1) <= ux);

@@ -383,70 +383,103 @@ __device__ __forceinline__ int mask_half_width(int thr, int dh) {
   return rem >= 0 ? isqrt_i(rem) : -1;
 }
 
+// One wave per query tile (8 x 8 tiles: 64 queries).  The wave's four rows of
+// 16 lanes take four (temporal distance, key-tile row) pairs at a time; in a
+// pair, lane i folds the footprints of queries i, 16 + i, 32 + i and 48 + i
+// in registers, and one reduction over the 16 lanes of the row gives the
+// run.  The radius table is staged in LDS (dynamic): per level row its
+// largest active distance and the offset of its active entries in the
+// compact table, then the compact table itself.
 template <bool L1>
 __global__ __launch_bounds__(256) void csr_runs_kernel(const int16_t* __restrict__ lv,
-                                                      const int32_t* __restrict__ r2,
-                                                      const int32_t* __restrict__ dmax, int T,
+                                                      const int32_t* __restrict__ r2c,
+                                                      const int32_t* __restrict__ r2off,
+                                                      const int32_t* __restrict__ dmax, int n_levels,
+                                                      int n_r2c, int T,
                                                       int row_base, Grid g, int tw_shift, int DM,
                                                       int32_t* __restrict__ counts,
                                                       int32_t* __restrict__ runs,
                                                       int32_t* __restrict__ rowwin) {
+  extern __shared__ int32_t tab_s[];
+  int32_t* dmax_s = tab_s;
+  int32_t* off_s = tab_s + n_levels;
+  int32_t* r2c_s = tab_s + 2 * n_levels;
+  for (int i = threadIdx.x; i < n_levels; i += 256) {
+    dmax_s[i] = dmax[i];
+    off_s[i] = r2off[i];
+  }
+  for (int i = threadIdx.x; i < n_r2c; i += 256) r2c_s[i] = r2c[i];
+  __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tile = blockIdx.x * 4 + wave;
-  if (tile >= g.count) return;  // wave-uniform
+  if (tile >= g.count) return;  // wave-uniform, after the block's only barrier
   const int bh = blockIdx.y;
   const size_t N = static_cast<size_t>(g.T) * g.H * g.W;
   const int64_t row = static_cast<int64_t>(bh) * g.count + tile;
   const int tq = tile / g.per_frame, rem = tile % g.per_frame;
-  const int hq = (rem / g.nw) * g.th + (lane >> tw_shift);
-  const int wq = (rem % g.nw) * g.tw + (lane & (g.tw - 1));
-  const bool valid = hq < g.H && wq < g.W;
-  int trow = 0, dm = -1;
-  if (valid) {
-    trow = lv[static_cast<size_t>(bh) * N + (static_cast<size_t>(tq) * g.H + hq) * g.W + wq] - row_base;
-    dm = dmax[trow];
+  const int h0 = (rem / g.nw) * g.th, w0 = (rem % g.nw) * g.tw;
+  const int li = lane & 15, grp = lane >> 4;
+  // This lane's four queries (tile-local index 16*k + li, row-major in the
+  // 8 x 8 tile): coordinates, table offset and largest active distance
+  // (dm = -1 for positions outside the grid).
+  int hq[4], wq[4], toff[4], dm[4];
+  int dmx = -1;
+#pragma unroll
+  for (int k4 = 0; k4 < 4; ++k4) {
+    const int qi = 16 * k4 + li;
+    hq[k4] = h0 + (qi >> tw_shift);
+    wq[k4] = w0 + (qi & (g.tw - 1));
+    toff[k4] = 0;
+    dm[k4] = -1;
+    if (hq[k4] < g.H && wq[k4] < g.W) {
+      const int trow =
+          lv[static_cast<size_t>(bh) * N + (static_cast<size_t>(tq) * g.H + hq[k4]) * g.W + wq[k4]] - row_base;
+      toff[k4] = off_s[trow];
+      dm[k4] = dmax_s[trow];
+    }
+    dmx = max(dmx, dm[k4]);
   }
-  const int dmw = wave_max_u(dm);
+  const int dmw = wave_max_u(dmx);
   const int t_lo = max(0, tq - dmw), t_hi = min(T - 1, tq + dmw);
   int32_t* rrow = runs + row * static_cast<int64_t>((2 * DM + 1) * g.nh);
   int count = 0;
-  // Frames tq - delta and tq + delta see the same disks: each distance is
-  // computed once and its runs are written for both frames.
-  for (int delta = 0; delta <= dmw; ++delta) {
-    const bool below = tq - delta >= 0, above = delta > 0 && tq + delta <= T - 1;
-    if (!below && !above) continue;  // wave-uniform
-    const int nfr = (below ? 1 : 0) + (above ? 1 : 0);
-    const int thr = (valid && delta <= dm) ? r2[trow * T + delta] : -1;
-    const int rad = thr >= 0 ? mask_reach<L1>(thr) : -1;
-    const int top = thr >= 0 ? max(0, hq - rad) : 0x7fffffff;
-    const int bot = thr >= 0 ? min(g.H - 1, hq + rad) : -1;
-    const int TOP = wave_min_u(top), BOT = wave_max_u(bot);
-    const int tr_first = BOT < TOP ? g.nh : TOP / g.th, tr_last = BOT < TOP ? -1 : BOT / g.th;
-    // Tile rows in chunks of 64: lane j keeps the run of row (chunk + j).
-    for (int trc = 0; trc < g.nh; trc += 64) {
-      int32_t myrun = RUN_EMPTY;
-      const int tr_end = min(trc + 63, tr_last);
-      for (int tr = max(trc, tr_first); tr <= tr_end; ++tr) {
-        const int r0 = tr * g.th, r1 = min(g.H, r0 + g.th) - 1;
-        const int dh = max(0, max(r0 - hq, hq - r1));
-        const int a = thr >= 0 ? mask_half_width<L1>(thr, dh) : -1;
-        int lo = 0x7fffffff, hi = -1;
-        if (a >= 0) {
-          lo = max(0, wq - a) >> tw_shift;
-          hi = min(g.W - 1, wq + a) >> tw_shift;
-        }
-        const int LO = wave_min_u(lo), HI = wave_max_u(hi);
-        if (HI >= LO) {
-          count += (HI - LO + 1) * nfr;
-          if (lane == tr - trc) myrun = LO | (HI << 16);
-        }
-      }
-      if (trc + lane < g.nh) {
-        if (below) rrow[(tq - delta - t_lo) * g.nh + trc + lane] = myrun;
-        if (above) rrow[(tq + delta - t_lo) * g.nh + trc + lane] = myrun;
+  // Pairs (delta, key-tile row), delta-major; frames tq - delta and tq +
+  // delta see the same disks, so each pair's run is written for both.
+  const int npairs = (dmw + 1) * g.nh;
+  for (int p0 = 0; p0 < npairs; p0 += 4) {
+    const int p = p0 + grp;
+    const bool live = p < npairs;
+    const int delta = live ? p / g.nh : 0, tr = live ? p % g.nh : 0;
+    const int r0 = tr * g.th, r1 = min(g.H, r0 + g.th) - 1;
+    int lo = 0x7fffffff, hi = -1;
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+      const int thr = (live && delta <= dm[k4]) ? r2c_s[toff[k4] + delta] : -1;
+      const int dh = max(0, max(r0 - hq[k4], hq[k4] - r1));
+      const int a = thr >= 0 ? mask_half_width<L1>(thr, dh) : -1;
+      if (a >= 0) {
+        lo = min(lo, max(0, wq[k4] - a) >> tw_shift);
+        hi = max(hi, min(g.W - 1, wq[k4] + a) >> tw_shift);
       }
     }
+    // Min / max over the 16 lanes of this row (DPP inside rows of 16).
+    lo = min(lo, __builtin_amdgcn_update_dpp(0, lo, 0xB1, 0xF, 0xF, false));
+    hi = max(hi, __builtin_amdgcn_update_dpp(0, hi, 0xB1, 0xF, 0xF, false));
+    lo = min(lo, __builtin_amdgcn_update_dpp(0, lo, 0x4E, 0xF, 0xF, false));
+    hi = max(hi, __builtin_amdgcn_update_dpp(0, hi, 0x4E, 0xF, 0xF, false));
+    lo = min(lo, __builtin_amdgcn_update_dpp(0, lo, 0x124, 0xF, 0xF, false));
+    hi = max(hi, __builtin_amdgcn_update_dpp(0, hi, 0x124, 0xF, 0xF, false));
+    lo = min(lo, __builtin_amdgcn_update_dpp(0, lo, 0x128, 0xF, 0xF, false));
+    hi = max(hi, __builtin_amdgcn_update_dpp(0, hi, 0x128, 0xF, 0xF, false));
+    if (live && li == 0) {
+      const bool below = tq - delta >= 0, above = delta > 0 && tq + delta <= T - 1;
+      const int32_t run = hi >= lo ? (lo | (hi << 16)) : RUN_EMPTY;
+      if (hi >= lo) count += (hi - lo + 1) * ((below ? 1 : 0) + (above ? 1 : 0));
+      if (below) rrow[(tq - delta - t_lo) * g.nh + tr] = run;
+      if (above) rrow[(tq + delta - t_lo) * g.nh + tr] = run;
+    }
   }
+  count = wave_sum_u(count);
   if (lane == 0) {
     counts[row] = count;
     rowwin[row] = t_lo | (max(0, t_hi - t_lo + 1) << 16);
@@ -1544,16 +1577,18 @@ static int log2i(int x) {
   return s;
 }
 
-hipError_t launch_csr_runs(bool l1, const int16_t* lv, const int32_t* r2, const int32_t* dmax, int T,
-                           int row_base, int BH, const Grid& tiles, int DM, int32_t* counts,
-                           int32_t* runs, int32_t* rowwin, hipStream_t s) {
+hipError_t launch_csr_runs(bool l1, const int16_t* lv, const RadiusTable& tab, int n_levels, int row_base,
+                           int BH, const Grid& tiles, int DM, int32_t* counts, int32_t* runs, int32_t* rowwin,
+                           hipStream_t s) {
   const dim3 grid((tiles.count + 3) / 4, BH), block(256);
+  const size_t lds = (2 * static_cast<size_t>(n_levels) + tab.n_r2c) * sizeof(int32_t);
+  if (lds > 65536) return hipErrorInvalidValue;  // the parameter check bounds the table well below this
   if (l1)
-    csr_runs_kernel<true><<<grid, block, 0, s>>>(lv, r2, dmax, T, row_base, tiles, log2i(tiles.tw), DM,
-                                                 counts, runs, rowwin);
+    csr_runs_kernel<true><<<grid, block, lds, s>>>(lv, tab.r2c, tab.r2off, tab.dmax, n_levels, tab.n_r2c, tab.T,
+                                                   row_base, tiles, log2i(tiles.tw), DM, counts, runs, rowwin);
   else
-    csr_runs_kernel<false><<<grid, block, 0, s>>>(lv, r2, dmax, T, row_base, tiles, log2i(tiles.tw), DM,
-                                                  counts, runs, rowwin);
+    csr_runs_kernel<false><<<grid, block, lds, s>>>(lv, tab.r2c, tab.r2off, tab.dmax, n_levels, tab.n_r2c, tab.T,
+                                                    row_base, tiles, log2i(tiles.tw), DM, counts, runs, rowwin);
   return hipGetLastError();
 }
 

@@ -74,6 +74,10 @@ def _validate(**kw):
     (dict(generator=3, vote_threshold=2), "TRA_ERR_INVALID_ARG"),
     (dict(generator=1), "TRA_ERR_INVALID_ARG"),  # the static generators need radius_override >= 0
     (dict(generator=2, radius_override=-1.0), "TRA_ERR_INVALID_ARG"),
+    # every frame active (decay 1) over 2,000 frames at 88 levels: the radius
+    # table's active entries (88 x 2,000) exceed what the tile-list kernel stages
+    (dict(grid=(2000, 4, 4), heads=1, dtype=torch.float32, decay=1.0, budget_max=float(2 ** 20)),
+     "TRA_ERR_INVALID_ARG"),
 ])
 def test_validation_rejects(kw, code):
     with pytest.raises(tra.TraError) as ei:
