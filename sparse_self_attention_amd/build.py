@@ -23,6 +23,29 @@ def command(out=LIB):
             "-o", out] + SOURCES
 
 
+SANITIZE_FLAGS = [
+    # host code only: the device code is built as usual
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer", "-g",
+]
+
+
+def build_sanitized(out, verbose=True):
+    """libtra with its host code built under AddressSanitizer and
+    UndefinedBehaviorSanitizer (for host-only checks on a machine without a
+    GPU; the executable that loads it must be linked with -fsanitize too)."""
+    cmd = command(out)
+    cmd = cmd[:1] + SANITIZE_FLAGS + cmd[1:]
+    cmd = [c if c != "-O3" else "-O1" for c in cmd]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building the sanitized library")
+    return out
+
+
 def build(verbose=True):
     tmp = LIB + ".tmp"
     cmd = command(tmp)

@@ -992,7 +992,12 @@ void tra_schedule_destroy(tra_schedule* s) {
 }
 
 const char* tra_status_string(tra_status s) {
-  switch (s) {
+  // Callers may pass any integer (ABI users, bindings); a value outside the
+  // enumerators is read as an int, never as the enum.
+  static_assert(sizeof(tra_status) == sizeof(int), "tra_status is int-sized");
+  int v = 0;
+  std::memcpy(&v, &s, sizeof v);
+  switch (v) {
     case TRA_OK: return "TRA_OK";
     case TRA_ERR_INVALID_ARG: return "TRA_ERR_INVALID_ARG";
     case TRA_ERR_SHAPE: return "TRA_ERR_SHAPE";
