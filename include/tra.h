@@ -332,6 +332,27 @@ tra_status tra_plan_create_from_entropy(const tra_shape* shape, const tra_params
  * tra_plan_create_from_entropy).  Pooled keys keep their last values. */
 tra_status tra_plan_rebuild_from_entropy(tra_plan* plan, const float* entropy, void* stream);
 
+/*
+ * Rebuild a plan from saved contents (checkpoint / resume of a plan that a
+ * reuse schedule keeps across denoising steps: "Token Radius Attention for
+ * Efficient Video Generation", summary page, section 2, "Reutilisation
+ * Inter-Etapes").  All arrays are HOST memory, in tra_plan_export's layout:
+ *   levels   int16 [B*heads*N]   budget level of each query (required); every
+ *            value must lie in [k_lo, k_lo + n_levels - 1] of the radius
+ *            table these params give, or be -1 under radius_override
+ *   entropy  float [B*heads*N]   stored for export only (NULL: zeros)
+ *   kbar     pooled keys [B*heads*n_pool*head_dim] of the dtype, stored for
+ *            export and drift (NULL: zeros)
+ * The radius table is recomputed from the params, and the tile lists (CSR,
+ * votes, group lists) are built from the levels by the same kernels as
+ * tra_plan_create, so a plan exported and imported with the same shape and
+ * params attends exactly like the original.  TRA_ERR_INVALID_ARG (nothing
+ * allocated) for a NULL levels array or a level outside the table; the
+ * usual statuses otherwise.  Synchronises `stream`.
+ */
+tra_status tra_plan_import(const tra_shape* shape, const tra_params* params, const int16_t* levels,
+                           const float* entropy, const void* kbar, void* stream, tra_plan** out);
+
 /* Frees the plan.  hipFree waits for the device's outstanding work before it
  * releases memory, so destroying a plan synchronises the device. */
 void tra_plan_destroy(tra_plan* plan);

@@ -19,7 +19,7 @@ import os
 
 import torch
 
-__all__ = ["TraError", "Plan", "plan", "plan_from_entropy", "attention", "dense_attention", "Schedule",
+__all__ = ["TraError", "Plan", "plan", "plan_from_entropy", "import_plan", "attention", "dense_attention", "Schedule",
            "STEP_MODES", "radius_table",
            "validate", "library_path", "drift_noalloc_max_bytes",
            "load_library", "DEFAULT_PARAMS", "EXPORTED_SYMBOLS"]
@@ -79,6 +79,8 @@ _SIGS = {
     "tra_plan_drift": (ctypes.c_int, [_P, _P, _P, ctypes.POINTER(ctypes.c_int64), _P]),
     "tra_plan_drift_noalloc": (ctypes.c_int, [_P, _P, _P, ctypes.POINTER(ctypes.c_int64), _P]),
     "tra_drift_noalloc_max_bytes": (ctypes.c_size_t, []),
+    "tra_plan_import": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.POINTER(_Params), _P, _P, _P, _P,
+                                       ctypes.POINTER(_P)]),
     "tra_plan_create_from_entropy": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.POINTER(_Params), _P, _P,
                                                     ctypes.POINTER(_P)]),
     "tra_plan_rebuild_from_entropy": (ctypes.c_int, [_P, _P, _P]),
@@ -366,6 +368,31 @@ def plan_from_entropy(entropy, grid, head_dim, dtype=torch.bfloat16, **params):
                                                        _dev_ptr(entropy, "entropy"), _stream(entropy.device),
                                                        ctypes.byref(h)), "tra_plan_create_from_entropy")
     return Plan(h, shape, tuple(grid), prm, entropy.device)
+
+
+def import_plan(saved, B, heads, grid, head_dim, dtype=torch.bfloat16, device="cuda", **params):
+    """Plan rebuilt from `Plan.export()` output (its levels, entropy and pooled
+    keys; the tile lists are rebuilt from the levels)."""
+    import numpy as np
+    shape = _make_shape(B, heads, grid, head_dim, _DTYPES[dtype])
+    prm = _make_params(params)
+    N = shape.T * shape.H * shape.W
+    lv = np.ascontiguousarray(saved["levels"], dtype=np.int16).reshape(-1)
+    if lv.size != B * heads * N:
+        raise ValueError(f"levels must hold {B * heads * N} entries")
+    ent = saved.get("entropy")
+    ent = None if ent is None else np.ascontiguousarray(ent, dtype=np.float32).reshape(-1)
+    kb = saved.get("kbar")
+    kb = None if kb is None else np.ascontiguousarray(kb, dtype=np.uint16 if shape.dtype == 1 else np.float32)
+    if ent is not None and ent.size != lv.size:
+        raise ValueError("entropy must match levels")
+    dev = torch.device(device)
+    h = _P()
+    _check(load_library().tra_plan_import(
+        ctypes.byref(shape), ctypes.byref(prm), lv.ctypes.data_as(_P),
+        None if ent is None else ent.ctypes.data_as(_P), None if kb is None else kb.ctypes.data_as(_P),
+        _stream(dev), ctypes.byref(h)), "tra_plan_import")
+    return Plan(h, shape, tuple(grid), prm, dev)
 
 
 def dense_attention(q, k, v, grid, out=None, entropy=False):

@@ -13,6 +13,7 @@ LIB = os.path.join(HERE, "libtra.so")
 SOURCES = [os.path.join(HERE, "csrc", f) for f in ("tra_api.cpp", "tra_kernels.hip", "tra_dense.hip", "tra_noalloc.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("TRA_OFFLOAD_ARCH", "gfx950")
+ROCM_LIB = "/opt/rocm/lib"
 
 
 def command(out=LIB):
@@ -20,7 +21,9 @@ def command(out=LIB):
             # packed fp32 VALU forms are kept out of every kernel
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-            "-o", out] + SOURCES
+            "-o", out] + SOURCES + [
+            # profiler ranges around the plan stages and calls (rocprofv3 --marker-trace)
+            "-L", ROCM_LIB, "-Wl,-rpath," + ROCM_LIB, "-lrocprofiler-sdk-roctx"]
 
 
 SANITIZE_FLAGS = [

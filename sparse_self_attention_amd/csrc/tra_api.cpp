@@ -15,6 +15,8 @@
 
 #include "tra_internal.h"
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -34,6 +36,15 @@ struct FaultState {
   int kind = FAULT_NONE, at = 0, count = 0;
 };
 thread_local FaultState g_fault;
+
+// A named range on the profiler's marker timeline (rocprofv3 --marker-trace)
+// for the scope's host-side work, kernel launches included.
+struct Range {
+  explicit Range(const char* name) { roctxRangePushA(name); }
+  ~Range() { roctxRangePop(); }
+  Range(const Range&) = delete;
+  Range& operator=(const Range&) = delete;
+};
 
 void fault_arm() {
   g_fault = FaultState{};
@@ -334,6 +345,8 @@ tra::RadiusTable radius_table_of(const tra_plan* p) {
                           metric_of(p->params)};
 }
 
+tra_status build_lists(tra_plan* p, hipStream_t st);
+
 // Steps entropy -> level -> tile lists into the plan's buffers.  The levels
 // come from the pooled-key entropy of (q, k), or, when `Hin` is not NULL, from
 // the given per-query entropies.
@@ -341,18 +354,32 @@ tra_status build(tra_plan* p, const void* q, const void* k, const float* Hin, hi
   p->valid = false;
   const tra_shape& s = p->shape;
   const int d = s.head_dim;
-  if (p->params.radius_override < 0.0) {
-    tra::EntropyArgs ea{p->params.a, p->params.c, p->params.levels_per_nat, p->table.k_lo, p->table.k_hi};
-    if (Hin) {
-      TRA_LAUNCH(tra::launch_levels_from_entropy(Hin, p->n_queries, ea, p->H, p->lv, st));
+  Range r_all("tra.plan");
+  {
+    Range r("tra.plan.levels");
+    if (p->params.radius_override < 0.0) {
+      tra::EntropyArgs ea{p->params.a, p->params.c, p->params.levels_per_nat, p->table.k_lo, p->table.k_hi};
+      if (Hin) {
+        TRA_LAUNCH(tra::launch_levels_from_entropy(Hin, p->n_queries, ea, p->H, p->lv, st));
+      } else {
+        TRA_LAUNCH(tra::launch_pool(s.dtype, d, k, p->kbar, p->BH, p->pool, st));
+        TRA_LAUNCH(tra::launch_entropy(s.dtype, d, q, p->kbar, p->pool_w, p->BH, static_cast<int>(p->N),
+                                       p->pool.count, ea, p->H, p->lv, st));
+      }
     } else {
-      TRA_LAUNCH(tra::launch_pool(s.dtype, d, k, p->kbar, p->BH, p->pool, st));
-      TRA_LAUNCH(tra::launch_entropy(s.dtype, d, q, p->kbar, p->pool_w, p->BH, static_cast<int>(p->N),
-                                     p->pool.count, ea, p->H, p->lv, st));
+      TRA_LAUNCH(tra::launch_fill_levels(p->lv, p->H, p->n_queries, st));
     }
-  } else {
-    TRA_LAUNCH(tra::launch_fill_levels(p->lv, p->H, p->n_queries, st));
   }
+  const tra_status ls = build_lists(p, st);
+  if (ls != TRA_OK) return ls;
+  p->valid = true;
+  return TRA_OK;
+}
+
+// Tile lists (CSR, votes, group lists) from the levels in p->lv.
+tra_status build_lists(tra_plan* p, hipStream_t st) {
+  Range r_lists("tra.plan.tile_lists");
+  const tra_shape& s = p->shape;
   const bool window = p->params.generator == TRA_GEN_WINDOW_1D;
   if (window) {
     TRA_LAUNCH(tra::launch_window_csr(false, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, nullptr,
@@ -387,6 +414,7 @@ tra_status build(tra_plan* p, const void* q, const void* k, const float* Hin, hi
   if (theta > 1) {
     // Token voting with a threshold: votes per entry, then the entries with at
     // least theta votes form the plan's CSR.
+    Range r("tra.plan.votes");
     if (p->nnz > p->votes_cap) {
       if (p->votes) TRA_HIP(hipFree(p->votes));
       p->votes = nullptr;
@@ -420,6 +448,7 @@ tra_status build(tra_plan* p, const void* q, const void* k, const float* Hin, hi
     p->retained_votes = p->totals_host[2];
   }
   if (s.dtype == TRA_BF16) {
+    Range r("tra.plan.group_lists");
     if (p->nnz > p->glist_cap) {
       if (p->glist) TRA_HIP(hipFree(p->glist));
       p->glist = nullptr;
@@ -442,7 +471,6 @@ tra_status build(tra_plan* p, const void* q, const void* k, const float* Hin, hi
                                       p->glist, p->glen, st));
     }
   }
-  p->valid = true;
   return TRA_OK;
 }
 
@@ -680,6 +708,57 @@ tra_status tra_plan_rebuild_from_entropy(tra_plan* plan, const float* entropy, v
   return build(plan, nullptr, nullptr, entropy, static_cast<hipStream_t>(stream));
 }
 
+tra_status tra_plan_import(const tra_shape* shape, const tra_params* params, const int16_t* levels,
+                           const float* entropy, const void* kbar, void* stream, tra_plan** out) {
+  if (!out) return fail(TRA_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  fault_arm();
+  tra_status st = check_shape(shape);
+  if (st != TRA_OK) return st;
+  Table tab;
+  st = check_params(shape, params, &tab);
+  if (st != TRA_OK) return st;
+  if (!levels) return fail(TRA_ERR_INVALID_ARG, "levels is NULL");
+  // Every level must name a row of the radius table (-1 under radius_override).
+  const int64_t nq = static_cast<int64_t>(shape->B) * shape->heads * shape->T * shape->H * shape->W;
+  const bool fixed = params->radius_override >= 0.0;
+  const int lo = fixed ? -1 : tab.k_lo, hi = fixed ? -1 : tab.k_lo + tab.n_levels - 1;
+  for (int64_t i = 0; i < nq; ++i)
+    if (levels[i] < lo || levels[i] > hi)
+      return fail(TRA_ERR_INVALID_ARG, "level " + std::to_string(levels[i]) + " of query " + std::to_string(i) +
+                                           " outside [" + std::to_string(lo) + ", " + std::to_string(hi) + "]");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  Range r("tra.plan.import");
+  tra_plan* p = nullptr;
+  st = create_plan(shape, params, std::move(tab), hs, &p);
+  if (st != TRA_OK) return st;
+  auto fin = [&](tra_status s2) {
+    if (s2 != TRA_OK) release(p);
+    return s2;
+  };
+#define TRA_HIP_I(call)                                                                       \
+  do {                                                                                        \
+    hipError_t e_ = (call);                                                                   \
+    if (e_ != hipSuccess)                                                                     \
+      return fin(fail(TRA_ERR_HIP, std::string(#call) + ": " + hipGetErrorString(e_)));       \
+  } while (0)
+  // create_plan queued the clearing of the pooled keys on hs; copies go after it.
+  TRA_HIP_I(hipStreamSynchronize(hs));
+  TRA_HIP_I(hipMemcpy(p->lv, levels, nq * sizeof(int16_t), hipMemcpyHostToDevice));
+  if (entropy) TRA_HIP_I(hipMemcpy(p->H, entropy, nq * sizeof(float), hipMemcpyHostToDevice));
+  else TRA_HIP_I(hipMemsetAsync(p->H, 0, nq * sizeof(float), hs));
+  if (kbar)
+    TRA_HIP_I(hipMemcpy(p->kbar, kbar,
+                        static_cast<size_t>(p->BH) * p->pool.count * shape->head_dim * dtype_size(shape->dtype),
+                        hipMemcpyHostToDevice));
+#undef TRA_HIP_I
+  st = build_lists(p, hs);
+  if (st != TRA_OK) return fin(st);
+  p->valid = true;
+  *out = p;
+  return TRA_OK;
+}
+
 tra_status tra_dense_attention(const tra_shape* shape, const void* q, const void* k, const void* v,
                                void* o, float* entropy, void* stream) {
   tra_status st = check_shape(shape);
@@ -697,6 +776,7 @@ tra_status tra_dense_attention(const tra_shape* shape, const void* q, const void
   const int BH = shape->B * shape->heads;
   const int N = shape->T * shape->H * shape->W;
   fault_arm();
+  Range r("tra.dense_attention");
   TRA_LAUNCH(tra::launch_dense(shape->dtype, shape->head_dim, q, k, v, o, entropy, BH, N,
                             static_cast<hipStream_t>(stream)));
   return TRA_OK;
@@ -712,6 +792,7 @@ tra_status tra_attention(const tra_plan* plan, const void* q, const void* k, con
   if (o == q || o == k || o == v) return fail(TRA_ERR_INVALID_ARG, "o must not alias q, k or v");
   if (!plan->valid) return fail(TRA_ERR_PLAN_INVALID, "the plan's last build failed");
   fault_arm();
+  Range r("tra.attention");
   const tra_shape& s = plan->shape;
   const tra::RadiusTable tab = radius_table_of(plan);
   TRA_LAUNCH(tra::launch_attention(s.dtype, s.head_dim, q, k, v, o, plan->lv, tab, plan->row_base,

@@ -109,6 +109,22 @@ int main(void) {
   plan = (tra_plan*)fake;
   EXPECT(tra_plan_create_from_entropy(&wan, &p, (const float*)fake, NULL, &plan) == TRA_ERR_OOM);
   EXPECT(plan == NULL);
+  {
+    /* a plan imported from levels: every level is checked first */
+    const size_t nq = (size_t)wan.B * wan.heads * wan.T * wan.H * wan.W;
+    int16_t* lv = (int16_t*)malloc(sizeof(int16_t) * nq);
+    EXPECT(tra_radius_table(&wan, &p, NULL, NULL, &n_levels, &k_lo) == TRA_OK);
+    for (size_t i = 0; i < nq; ++i) lv[i] = (int16_t)k_lo;
+    plan = (tra_plan*)fake;
+    EXPECT(tra_plan_import(&wan, &p, lv, NULL, NULL, NULL, &plan) == TRA_ERR_OOM);
+    EXPECT(plan == NULL);
+    lv[nq - 1] = (int16_t)(k_lo - 1);
+    plan = (tra_plan*)fake;
+    EXPECT(tra_plan_import(&wan, &p, lv, NULL, NULL, NULL, &plan) == TRA_ERR_INVALID_ARG);
+    EXPECT(plan == NULL);
+    EXPECT(tra_plan_import(&wan, &p, NULL, NULL, NULL, NULL, &plan) == TRA_ERR_INVALID_ARG);
+    free(lv);
+  }
   tra_schedule* sched = (tra_schedule*)fake;
   const tra_schedule_params sp = {2, 0, 0.1};
   EXPECT(tra_schedule_create(&wan, &p, &sp, &sched) == TRA_ERR_OOM);

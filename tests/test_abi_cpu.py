@@ -176,6 +176,40 @@ def test_plan_from_entropy_rejects_bad_arguments_before_any_device_call():
     assert name(lib.tra_plan_rebuild_from_entropy(None, ctypes.c_void_p(4096), None)) == "TRA_ERR_INVALID_ARG"
 
 
+def test_plan_import_rejects_bad_levels_before_any_device_call():
+    """tra_plan_import checks every level against the radius table on the host
+    and allocates nothing when one is outside it."""
+    import numpy as np
+    lib = tra.load_library()
+    out = ctypes.c_void_p()
+    name = lambda st: lib.tra_status_string(st).decode()
+    sh = _shape(grid=(2, 8, 8))
+    n = sh.B * sh.heads * sh.T * sh.H * sh.W
+    prm = tra._make_params({})
+    r2, _, k_lo = tra.radius_table((2, 8, 8))
+    k_hi = k_lo + r2.shape[0] - 1
+    P = ctypes.c_void_p
+    assert name(lib.tra_plan_import(ctypes.byref(sh), ctypes.byref(prm), None, None, None, None,
+                                    ctypes.byref(out))) == "TRA_ERR_INVALID_ARG"
+    assert name(lib.tra_plan_import(ctypes.byref(sh), ctypes.byref(prm), P(4096), None, None, None,
+                                    None)) == "TRA_ERR_INVALID_ARG"
+    for bad in (k_lo - 1, k_hi + 1, -1):
+        lv = np.full(n, k_lo, dtype=np.int16)
+        lv[n - 1] = bad
+        assert name(lib.tra_plan_import(ctypes.byref(sh), ctypes.byref(prm), lv.ctypes.data_as(P), None, None,
+                                        None, ctypes.byref(out))) == "TRA_ERR_INVALID_ARG"
+        assert out.value is None
+    # under radius_override every level must be -1
+    fixed = tra._make_params({"radius_override": 3.0})
+    lv = np.zeros(n, dtype=np.int16)
+    assert name(lib.tra_plan_import(ctypes.byref(sh), ctypes.byref(fixed), lv.ctypes.data_as(P), None, None,
+                                    None, ctypes.byref(out))) == "TRA_ERR_INVALID_ARG"
+    bad_prm = tra._make_params({"decay": 0.0})
+    lv = np.full(n, k_lo, dtype=np.int16)
+    assert name(lib.tra_plan_import(ctypes.byref(sh), ctypes.byref(bad_prm), lv.ctypes.data_as(P), None, None,
+                                    None, ctypes.byref(out))) == "TRA_ERR_INVALID_ARG"
+
+
 def test_binding_dense_checks_shapes_on_host():
     q = torch.zeros((1, 1, 2 * 8 * 8, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
