@@ -270,11 +270,19 @@ def main():
     achieved = flops_call / (attn_ms * 1e-3) / 1e12
     elem = 2 if cfg.dtype == "bf16" else 4
     # Algorithmic bytes of the planning steps: read Q and K, write the levels
-    # (2 B per query) and the tile lists (4 B per entry and per row offset).
-    # The fp32 entropy the plan also keeps (for export) is not counted.
+    # (2 B per query) and the tile lists the pass builds: for bf16 plans
+    # without a vote threshold the group lists the attention kernel reads
+    # (8 B per entry, 8 B per group: offset and length), otherwise the CSR
+    # (4 B per entry and per row offset).  The fp32 entropy the plan also
+    # keeps (for export) is not counted.
+    if cfg.dtype == "bf16" and variant.get("vote_threshold", 1) <= 1:
+        _, glen, _ = plan.export_groups()
+        list_bytes = 8 * int(glen.sum()) + 8 * len(glen)
+    else:
+        list_bytes = 4 * (info["nnz"] + info["n_rows"] + 1)
     plan_bytes = (2 * cfg.heads * cfg.N * cfg.head_dim * elem
                   + cfg.heads * cfg.N * 2
-                  + 4 * (info["nnz"] + info["n_rows"] + 1))
+                  + list_bytes)
     result = {
         "metric": "ms/call + retained-FLOP TFLOPS (% bf16 MFMA peak), Wan2.1-14B 720p, 1 GPU",
         "value": value,

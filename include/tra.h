@@ -190,9 +190,16 @@ tra_status tra_radius_table(const tra_shape* shape, const tra_params* params, in
  *   (h_i-h_j)^2 + (w_i-w_j)^2 <= R2[k_i][|t_i-t_j|].
  * The CSR's columns are ascending key-tile ids (tile id = (t*ceil(H/tile_h) +
  * h/tile_h)*ceil(W/tile_w) + w/tile_w) within each head.
- * Synchronises `stream` once (to size the tile lists).  *out receives the plan,
- * which owns all its device memory (including the scratch of tra_plan_stats
- * and tra_plan_drift); on failure nothing is kept and *out stays NULL.
+ * bf16 plans without a vote threshold build only what the attention kernel
+ * reads (levels, per-row runs and counts, and the merged lists of 2 x 2 query
+ * tile groups, in a buffer sized at creation for the worst case): the build
+ * is asynchronous on `stream`.  Their CSR is completed from the counts and
+ * runs on first use by tra_plan_export (row_ptr / col_idx), tra_plan_stats
+ * or tra_plan_get_info, which then synchronise.  Other plans (fp32, vote
+ * threshold) build the CSR at once and synchronise `stream` once to size it.
+ * *out receives the plan, which owns all its device memory (including the
+ * scratch of tra_plan_stats and tra_plan_drift); on failure nothing is kept
+ * and *out stays NULL.
  * Errors: TRA_ERR_INVALID_ARG / SHAPE / DTYPE for inputs the device path does
  * not take (see tra_params_validate), TRA_ERR_OOM, TRA_ERR_HIP,
  * TRA_ERR_OVERFLOW when the tile lists would hold 2^31 entries or more.
@@ -221,7 +228,8 @@ tra_status tra_attention(const tra_plan* plan, const void* q, const void* k, con
  * Re-run the planning steps of tra_plan_create on new q and k into an existing
  * plan (the refresh of a warm-up step), reusing its device buffers; the tile
  * list buffer grows when needed.  The shape and parameters are the plan's.
- * Synchronises `stream` once.  On failure the plan is marked invalid: every
+ * Synchronises `stream` once, except for the asynchronous builds described
+ * at tra_plan_create.  On failure the plan is marked invalid: every
  * call that reads it (attention, export, stats, drift) returns
  * TRA_ERR_PLAN_INVALID until a rebuild succeeds.
  */
@@ -231,6 +239,9 @@ tra_status tra_plan_rebuild(tra_plan* plan, const void* q, const void* k, void* 
  * tra_attention trusts its caller on shapes; bindings call this first. */
 tra_status tra_plan_matches(const tra_plan* plan, const tra_shape* shape);
 
+/* Sizes of the plan.  For a plan whose CSR is completed on first use (see
+ * tra_plan_create) this completes it on the null stream, after the plan's
+ * last build, and synchronises. */
 tra_status tra_plan_get_info(const tra_plan* plan, tra_plan_info* info);
 
 /*

@@ -325,6 +325,14 @@ struct tra_plan {
   // Set by a build that completed; cleared when a build starts, so a plan
   // whose last build failed is refused by the calls that read it.
   bool valid = false;
+  // bf16 plans without a vote threshold build only what the attention kernel
+  // reads (levels, the per-row runs and counts, the group lists, into a
+  // group-list buffer sized for the worst case at creation), so a build
+  // neither allocates nor waits for the device.  Their CSR is completed from
+  // the counts and runs on first use (export, stats, info).
+  bool lazy_csr = false;
+  bool csr_ready = false;
+  hipEvent_t built = nullptr;  // recorded at the end of each lazy build
 };
 
 namespace {
@@ -337,6 +345,7 @@ void release(tra_plan* p) {
   for (void* b : bufs)
     if (b) (void)hipFree(b);
   if (p->totals_host) (void)hipHostFree(p->totals_host);
+  if (p->built) (void)hipEventDestroy(p->built);
   delete p;
 }
 
@@ -376,9 +385,70 @@ tra_status build(tra_plan* p, const void* q, const void* k, const float* Hin, hi
   return TRA_OK;
 }
 
+// Group lists only (lazy-CSR plans): runs and per-row counts, then the
+// merged lists of the groups, with no host round trip.
+tra_status build_group_lists_only(tra_plan* p, hipStream_t st) {
+  const tra_shape& s = p->shape;
+  p->csr_ready = false;
+  if (p->params.generator == TRA_GEN_WINDOW_1D) {
+    TRA_LAUNCH(tra::launch_window_groups(false, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, nullptr,
+                                      nullptr, p->glen, st));
+    TRA_LAUNCH(tra::launch_scan(p->glen, p->n_groups, p->gptr, p->totals + 4, st));
+    TRA_LAUNCH(tra::launch_window_groups(true, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, p->gptr,
+                                      p->glist, p->glen, st));
+  } else {
+    TRA_LAUNCH(tra::launch_csr_runs(p->params.generator == TRA_GEN_MANHATTAN, p->lv, radius_table_of(p),
+                                    p->table.n_levels, p->row_base, p->BH, p->tiles, p->DM, p->counts, p->runs,
+                                    p->rowwin, st));
+    TRA_LAUNCH(tra::launch_group_lists(false, p->BH, p->tiles, p->DM, p->runs, p->rowwin, nullptr, nullptr, nullptr,
+                                    nullptr, p->glen, st));
+    TRA_LAUNCH(tra::launch_scan(p->glen, p->n_groups, p->gptr, p->totals + 4, st));
+    TRA_LAUNCH(tra::launch_group_lists(true, p->BH, p->tiles, p->DM, p->runs, p->rowwin, nullptr, nullptr, p->gptr,
+                                    p->glist, p->glen, st));
+  }
+  TRA_HIP(hipEventRecord(p->built, st));
+  return TRA_OK;
+}
+
+// Completes the CSR of a lazy-CSR plan (on `st`, after its last build), once
+// per build.  Synchronises `st`.
+tra_status ensure_csr(tra_plan* p, hipStream_t st) {
+  if (!p->lazy_csr || p->csr_ready) return TRA_OK;
+  Range r("tra.plan.csr");
+  const tra_shape& s = p->shape;
+  const bool window = p->params.generator == TRA_GEN_WINDOW_1D;
+  TRA_HIP(hipStreamWaitEvent(st, p->built, 0));
+  if (window)
+    TRA_LAUNCH(tra::launch_window_csr(false, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, nullptr,
+                                   p->counts, nullptr, st));
+  TRA_LAUNCH(tra::launch_scan(p->counts, p->n_rows, p->row_ptr, p->totals, st));
+  TRA_HIP(hipMemcpyAsync(p->totals_host, p->totals, 3 * sizeof(int64_t), hipMemcpyDeviceToHost, st));
+  TRA_HIP(hipStreamSynchronize(st));
+  if (p->totals_host[2]) return fail(TRA_ERR_OVERFLOW, "CSR has 2^31 or more entries");
+  p->nnz = p->totals_host[0];
+  p->max_row_len = static_cast<int32_t>(p->totals_host[1]);
+  if (p->nnz > p->col_cap) {
+    if (p->col_idx) TRA_HIP(hipFree(p->col_idx));
+    p->col_idx = nullptr;
+    p->col_cap = 0;
+    const int64_t cap = p->nnz + p->nnz / 8 + 64;
+    TRA_HIP(dev_alloc(&p->col_idx, cap * sizeof(int32_t)));
+    p->col_cap = cap;
+  }
+  if (window)
+    TRA_LAUNCH(tra::launch_window_csr(true, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, p->row_ptr,
+                                   p->counts, p->col_idx, st));
+  else
+    TRA_LAUNCH(tra::launch_csr_expand(p->BH, p->tiles, p->DM, p->runs, p->rowwin, p->row_ptr, p->col_idx, st));
+  TRA_HIP(hipStreamSynchronize(st));
+  p->csr_ready = true;
+  return TRA_OK;
+}
+
 // Tile lists (CSR, votes, group lists) from the levels in p->lv.
 tra_status build_lists(tra_plan* p, hipStream_t st) {
   Range r_lists("tra.plan.tile_lists");
+  if (p->lazy_csr) return build_group_lists_only(p, st);
   const tra_shape& s = p->shape;
   const bool window = p->params.generator == TRA_GEN_WINDOW_1D;
   if (window) {
@@ -557,6 +627,17 @@ tra_status create_plan(const tra_shape* shape, const tra_params* params, Table&&
     p->n_groups = tra::group_count(p->BH, p->tiles);
     TRA_HIP_P(dev_alloc(&p->glen, p->n_groups * sizeof(int32_t)));
     TRA_HIP_P(dev_alloc(&p->gptr, (p->n_groups + 1) * sizeof(int32_t)));
+    // A group's list holds at most every key tile of the frames within the
+    // table's reach of its own frame.
+    const int64_t per_group =
+        static_cast<int64_t>(std::min(shape->T, 2 * p->DM + 1)) * p->tiles.per_frame;
+    const int64_t bound = p->n_groups * per_group;
+    if (params->vote_threshold <= 1 && bound * 8 <= (int64_t(1) << 32)) {
+      p->lazy_csr = true;
+      TRA_HIP_P(dev_alloc(&p->glist, bound * 2 * sizeof(int32_t)));
+      p->glist_cap = bound;
+      TRA_HIP_P(hipEventCreateWithFlags(&p->built, hipEventDisableTiming));
+    }
   }
   TRA_HIP_P(host_alloc(&p->totals_host, 8 * sizeof(int64_t)));
   TRA_HIP_P(dev_alloc(&p->counters, 4 * sizeof(unsigned long long)));
@@ -821,6 +902,11 @@ tra_status tra_plan_matches(const tra_plan* plan, const tra_shape* shape) {
 
 tra_status tra_plan_get_info(const tra_plan* plan, tra_plan_info* info) {
   if (!plan || !info) return fail(TRA_ERR_INVALID_ARG, "plan and info must not be NULL");
+  if (plan->valid) {  // nnz and the longest row come with the CSR (null stream)
+    fault_arm();
+    const tra_status st = ensure_csr(const_cast<tra_plan*>(plan), nullptr);
+    if (st != TRA_OK) return st;
+  }
   info->n_queries = plan->n_queries;
   info->n_rows = plan->n_rows;
   info->nnz = plan->nnz;
@@ -838,6 +924,11 @@ tra_status tra_plan_export(const tra_plan* plan, int16_t* levels, float* entropy
   if (!plan) return fail(TRA_ERR_INVALID_ARG, "plan is NULL");
   if (!plan->valid) return fail(TRA_ERR_PLAN_INVALID, "the plan's last build failed");
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (row_ptr || col_idx) {
+    fault_arm();
+    const tra_status st = ensure_csr(const_cast<tra_plan*>(plan), hs);
+    if (st != TRA_OK) return st;
+  }
   TRA_HIP(hipStreamSynchronize(hs));
   if (levels) TRA_HIP(hipMemcpy(levels, plan->lv, plan->n_queries * sizeof(int16_t), hipMemcpyDeviceToHost));
   if (entropy) TRA_HIP(hipMemcpy(entropy, plan->H, plan->n_queries * sizeof(float), hipMemcpyDeviceToHost));
@@ -881,6 +972,8 @@ tra_status tra_plan_stats(const tra_plan* plan, int64_t* retained, int64_t* list
   // The plan's own counters and pinned words (a plan is not used by two
   // stats or drift calls at once).
   tra_plan* p = const_cast<tra_plan*>(plan);
+  const tra_status cs = ensure_csr(p, hs);
+  if (cs != TRA_OK) return cs;
   TRA_LAUNCH(tra::launch_clear_counters(p->counters, 2, hs));
   TRA_LAUNCH(tra::launch_stats(metric_of(plan->params), plan->lv, plan->r2, plan->shape.T, plan->row_base, plan->BH,
                                plan->tiles, plan->row_ptr, plan->col_idx, p->counters, hs));
