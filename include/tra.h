@@ -251,7 +251,9 @@ tra_status tra_plan_get_info(const tra_plan* plan, tra_plan_info* info);
  *   r2       int32 [n_levels*T]           radius table
  *   row_ptr  int32 [n_rows + 1]           CSR offsets (global over all heads)
  *   col_idx  int32 [nnz]                  key tile ids (per head)
- *   kbar     [B*heads*n_pool*head_dim] of the dtype: pooled keys
+ *   kbar     [B*heads*n_pool*head_dim] of the dtype: pooled keys, rectangle
+ *            (t*ceil(H/pool_h) + r)*ceil(W/pool_w) + c in raster order (the
+ *            plan stores the full rectangles first; export reorders)
  * Synchronises `stream`.
  */
 tra_status tra_plan_export(const tra_plan* plan, int16_t* levels, float* entropy, int32_t* r2,

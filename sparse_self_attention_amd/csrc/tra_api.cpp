@@ -373,7 +373,7 @@ tra_status build(tra_plan* p, const void* q, const void* k, const float* Hin, hi
       } else {
         TRA_LAUNCH(tra::launch_pool(s.dtype, d, k, p->kbar, p->BH, p->pool, st));
         TRA_LAUNCH(tra::launch_entropy(s.dtype, d, q, p->kbar, p->pool_w, p->BH, static_cast<int>(p->N),
-                                       p->pool.count, ea, p->H, p->lv, st));
+                                       p->pool, ea, p->H, p->lv, st));
       }
     } else {
       TRA_LAUNCH(tra::launch_fill_levels(p->lv, p->H, p->n_queries, st));
@@ -647,11 +647,12 @@ tra_status create_plan(const tra_shape* shape, const tra_params* params, Table&&
   }
   TRA_HIP_P(hipGetDevice(&p->device));
 
-  std::vector<float> w(p->pool.count);
+  std::vector<float> w(p->pool.count);  // in the pooled keys' storage order
   for (int b = 0; b < p->pool.count; ++b) {
     const int rem = b % p->pool.per_frame;
     const int h0 = (rem / p->pool.nw) * p->pool.th, w0 = (rem % p->pool.nw) * p->pool.tw;
-    w[b] = static_cast<float>(std::min(p->pool.th, shape->H - h0) * std::min(p->pool.tw, shape->W - w0));
+    w[tra::pool_pos(p->pool, b)] =
+        static_cast<float>(std::min(p->pool.th, shape->H - h0) * std::min(p->pool.tw, shape->W - w0));
   }
   TRA_HIP_P(hipMemcpy(p->r2, p->table.r2.data(), p->table.r2.size() * sizeof(int32_t), hipMemcpyHostToDevice));
   TRA_HIP_P(hipMemcpy(p->dmax, p->table.dmax.data(), p->table.dmax.size() * sizeof(int32_t), hipMemcpyHostToDevice));
@@ -719,7 +720,7 @@ tra_status drift_with_scratch(const tra_plan* plan, const void* q, const void* k
   TRA_LAUNCH(launch_clear_counters(counter, 1, hs));
   TRA_LAUNCH(launch_pool(s.dtype, s.head_dim, k, kbar, plan->BH, plan->pool, hs));
   TRA_LAUNCH(launch_entropy(s.dtype, s.head_dim, q, kbar, plan->pool_w, plan->BH, static_cast<int>(plan->N),
-                            plan->pool.count, ea, nullptr, lv, hs));
+                            plan->pool, ea, nullptr, lv, hs));
   TRA_LAUNCH(launch_level_diff(plan->lv, lv, plan->n_queries, counter, hs));
   TRA_HIP(hipMemcpyAsync(host, counter, sizeof(unsigned long long), hipMemcpyDeviceToHost, hs));
   TRA_HIP(hipStreamSynchronize(hs));
@@ -828,10 +829,16 @@ tra_status tra_plan_import(const tra_shape* shape, const tra_params* params, con
   TRA_HIP_I(hipMemcpy(p->lv, levels, nq * sizeof(int16_t), hipMemcpyHostToDevice));
   if (entropy) TRA_HIP_I(hipMemcpy(p->H, entropy, nq * sizeof(float), hipMemcpyHostToDevice));
   else TRA_HIP_I(hipMemsetAsync(p->H, 0, nq * sizeof(float), hs));
-  if (kbar)
-    TRA_HIP_I(hipMemcpy(p->kbar, kbar,
-                        static_cast<size_t>(p->BH) * p->pool.count * shape->head_dim * dtype_size(shape->dtype),
-                        hipMemcpyHostToDevice));
+  if (kbar) {
+    // ABI order (raster over the pool rectangles) -> storage order
+    const size_t row = static_cast<size_t>(shape->head_dim) * dtype_size(shape->dtype);
+    std::vector<char> tmp(static_cast<size_t>(p->BH) * p->pool.count * row);
+    for (int bh = 0; bh < p->BH; ++bh)
+      for (int b = 0; b < p->pool.count; ++b)
+        std::memcpy(&tmp[(static_cast<size_t>(bh) * p->pool.count + tra::pool_pos(p->pool, b)) * row],
+                    static_cast<const char*>(kbar) + (static_cast<size_t>(bh) * p->pool.count + b) * row, row);
+    TRA_HIP_I(hipMemcpy(p->kbar, tmp.data(), tmp.size(), hipMemcpyHostToDevice));
+  }
 #undef TRA_HIP_I
   st = build_lists(p, hs);
   if (st != TRA_OK) return fin(st);
@@ -936,11 +943,16 @@ tra_status tra_plan_export(const tra_plan* plan, int16_t* levels, float* entropy
   if (row_ptr) TRA_HIP(hipMemcpy(row_ptr, plan->row_ptr, (plan->n_rows + 1) * sizeof(int32_t), hipMemcpyDeviceToHost));
   if (col_idx && plan->nnz > 0)
     TRA_HIP(hipMemcpy(col_idx, plan->col_idx, plan->nnz * sizeof(int32_t), hipMemcpyDeviceToHost));
-  if (kbar)
-    TRA_HIP(hipMemcpy(kbar, plan->kbar,
-                      static_cast<size_t>(plan->BH) * plan->pool.count * plan->shape.head_dim *
-                          dtype_size(plan->shape.dtype),
-                      hipMemcpyDeviceToHost));
+  if (kbar) {
+    // storage order (full rectangles first) -> ABI order (raster)
+    const size_t row = static_cast<size_t>(plan->shape.head_dim) * dtype_size(plan->shape.dtype);
+    std::vector<char> tmp(static_cast<size_t>(plan->BH) * plan->pool.count * row);
+    TRA_HIP(hipMemcpy(tmp.data(), plan->kbar, tmp.size(), hipMemcpyDeviceToHost));
+    for (int bh = 0; bh < plan->BH; ++bh)
+      for (int b = 0; b < plan->pool.count; ++b)
+        std::memcpy(static_cast<char*>(kbar) + (static_cast<size_t>(bh) * plan->pool.count + b) * row,
+                    &tmp[(static_cast<size_t>(bh) * plan->pool.count + tra::pool_pos(plan->pool, b)) * row], row);
+  }
   return TRA_OK;
 }
 
@@ -1056,7 +1068,7 @@ hipError_t pooled_levels(tra_schedule* s, const void* q, const void* k, int16_t*
   if (e != hipSuccess) return e;
   const tra::EntropyArgs ea{p->params.a, p->params.c, p->params.levels_per_nat, p->table.k_lo, p->table.k_hi};
   return tra::launch_entropy(s->shape.dtype, s->shape.head_dim, q, s->kbar, p->pool_w, p->BH,
-                             static_cast<int>(p->N), p->pool.count, ea, s->Hp, lv, hs);
+                             static_cast<int>(p->N), p->pool, ea, s->Hp, lv, hs);
 }
 
 }  // namespace

@@ -30,6 +30,22 @@ inline Grid make_grid(int T, int H, int W, int th, int tw) {
   return g;
 }
 
+// Storage order of the pooled keys: the full rectangles of every frame first
+// (frame-major, raster order inside the frame), then the rectangles cut by the
+// bottom or right edge (frame-major, raster order).  The entropy kernels then
+// read runs of equal-weight keys.  full_count() is the number of full ones.
+__host__ __device__ inline int pool_full_count(const Grid& g) { return g.T * (g.H / g.th) * (g.W / g.tw); }
+// Position of rectangle b (raster index t*per_frame + r*nw + c).
+__host__ __device__ inline int pool_pos(const Grid& g, int b) {
+  const int nhf = g.H / g.th, nwf = g.W / g.tw;
+  const int F = nhf * nwf, G = g.per_frame - F, wr = g.nw - nwf;
+  const int t = b / g.per_frame, rem = b % g.per_frame;
+  const int r = rem / g.nw, c = rem % g.nw;
+  if (r < nhf && c < nwf) return t * F + r * nwf + c;
+  const int idx = r < nhf ? r * wr + (c - nwf) : nhf * wr + (r - nhf) * g.nw + c;
+  return g.T * F + t * G + idx;
+}
+
 // Radius table on the device: the full table (n_levels x T, -1 = inactive
 // frame), the largest active frame distance per level row, and a compact copy
 // holding only the active entries of each row (row r at r2off[r], dmax[r] + 1
@@ -57,8 +73,9 @@ struct EntropyArgs {
 // Launchers (tra_kernels.hip).  All enqueue on `s` and return the launch status.
 hipError_t launch_pool(int dtype, int d, const void* k, void* kbar, int BH, const Grid& pool,
                        hipStream_t s);
+// kbar and pool_w in pool_pos order; pool is the pooling grid.
 hipError_t launch_entropy(int dtype, int d, const void* q, const void* kbar, const float* pool_w,
-                          int BH, int N, int n_pool, const EntropyArgs& ea, float* H_out,
+                          int BH, int N, const Grid& pool, const EntropyArgs& ea, float* H_out,
                           int16_t* lv_out, hipStream_t s);
 hipError_t launch_fill_levels(int16_t* lv, float* H, int64_t n, hipStream_t s);
 // Tile lists: per query tile the runs of key-tile columns per (frame, tile

@@ -72,7 +72,8 @@ __device__ double round_mean(double S, int n) {
 }
 
 // ---------------------------------------------------------------------------
-// Key pooling.  grid (pool.count, BH), 256 threads.
+// Key pooling.  grid (pool.count, BH), 256 threads; rectangle b is stored at
+// pool_pos(b) (full rectangles first).
 // ---------------------------------------------------------------------------
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void pool_kernel(const void* __restrict__ k,
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const void* __restrict__ k,
   for (int dd = threadIdx.x; dd < D; dd += 256) {
     double s = 0.0;
     for (int gi = 0; gi < GROUPS; ++gi) s += red[gi][dd];
-    const size_t out = (static_cast<size_t>(bh) * g.count + b) * D + dd;
+    const size_t out = (static_cast<size_t>(bh) * g.count + pool_pos(g, b)) * D + dd;
     if constexpr (BF16) {
       const float r = static_cast<float>(round_mean<8>(s, cnt));  // exact: a bf16 value
       static_cast<uint16_t*>(kbar)[out] = static_cast<uint16_t>(__float_as_uint(r) >> 16);
@@ -147,8 +148,8 @@ constexpr int ENT_WAVES = 4, ENT_QB = 2, ENT_QPW = ENT_WAVES * 32 * ENT_QB;
 template <int D>
 __global__ __launch_bounds__(256, 3) void entropy_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kbar,
-    const float* __restrict__ pool_w, int N, int NP, EntropyArgs ea, float* __restrict__ Hout,
-    int16_t* __restrict__ lvout) {
+    const float* __restrict__ pool_w, int N, int NP, int NFULL, float WFULL, EntropyArgs ea,
+    float* __restrict__ Hout, int16_t* __restrict__ lvout) {
   constexpr int NCH = D / 8;
   constexpr int KS = D / 16;
   __shared__ __attribute__((aligned(1024))) uint16_t kb_lds[2][32 * D];
@@ -239,6 +240,9 @@ __global__ __launch_bounds__(256, 3) void entropy_bf16_kernel(
         }
       }
     }
+    // A chunk of full rectangles only (they come first) has one weight, which
+    // then scales the chunk's two sums instead of each term.
+    const bool uniform = (ci + 1) * 32 <= NFULL;
 #pragma unroll
     for (int qb = 0; qb < ENT_QB; ++qb) {
       const f32x16& sc = acc[qb];
@@ -248,12 +252,24 @@ __global__ __launch_bounds__(256, 3) void entropy_bf16_kernel(
       mx = fmaxf(mx, sc[15]);
       const float mnew = fmaxf(m[qb], mx * c1);
       float sA = 0.f, sB = 0.f;
+      if (uniform) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float t = fmaf(sc[i], c1, -mnew);
-        const float e = __builtin_amdgcn_exp2f(t) * w[i];
-        sA += e;
-        sB = fmaf(e, t, sB);
+        for (int i = 0; i < 16; ++i) {
+          const float t = fmaf(sc[i], c1, -mnew);
+          const float e = __builtin_amdgcn_exp2f(t);
+          sA += e;
+          sB = fmaf(e, t, sB);
+        }
+        sA *= WFULL;
+        sB *= WFULL;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float t = fmaf(sc[i], c1, -mnew);
+          const float e = __builtin_amdgcn_exp2f(t) * w[i];
+          sA += e;
+          sB = fmaf(e, t, sB);
+        }
       }
       if (A[qb] > 0.f) {
         const float alpha = __builtin_amdgcn_exp2f(m[qb] - mnew);
@@ -1548,15 +1564,20 @@ hipError_t launch_pool(int dtype, int d, const void* k, void* kbar, int BH, cons
 }
 
 hipError_t launch_entropy(int dtype, int d, const void* q, const void* kbar, const float* pool_w,
-                          int BH, int N, int n_pool, const EntropyArgs& ea, float* H_out,
+                          int BH, int N, const Grid& pool, const EntropyArgs& ea, float* H_out,
                           int16_t* lv_out, hipStream_t s) {
   const dim3 grid((N + 255) / 256, BH), block(256);
+  const int n_pool = pool.count;
   if (dtype == 1) {
     const auto* qq = static_cast<const uint16_t*>(q);
     const auto* kb = static_cast<const uint16_t*>(kbar);
     const dim3 grid16((N + ENT_QPW - 1) / ENT_QPW, BH), block16(ENT_WAVES * 64);
-    if (d == 128) entropy_bf16_kernel<128><<<grid16, block16, 0, s>>>(qq, kb, pool_w, N, n_pool, ea, H_out, lv_out);
-    else entropy_bf16_kernel<64><<<grid16, block16, 0, s>>>(qq, kb, pool_w, N, n_pool, ea, H_out, lv_out);
+    const int nfull = pool_full_count(pool);
+    const float wfull = static_cast<float>(pool.th * pool.tw);
+    if (d == 128)
+      entropy_bf16_kernel<128><<<grid16, block16, 0, s>>>(qq, kb, pool_w, N, n_pool, nfull, wfull, ea, H_out, lv_out);
+    else
+      entropy_bf16_kernel<64><<<grid16, block16, 0, s>>>(qq, kb, pool_w, N, n_pool, nfull, wfull, ea, H_out, lv_out);
   } else {
     const auto* qq = static_cast<const float*>(q);
     const auto* kb = static_cast<const float*>(kbar);
