@@ -78,7 +78,11 @@ class Workload:
 #   wan21_14b_720p   c = -0.8125  density 0.1206 (8 heads)
 #   hunyuan_720p     c = -0.8125  density 0.0901 (6 heads)
 #   long_video_2x    c = -3.25    cap 8192: about 45% of queries at the cap,
-#                                 density 0.0152 (4 heads)
+#                                 density 0.0152 (4 heads).  With this cap no
+#                                 scale reaches a 5% density (1.72% with every
+#                                 query capped); -3.25 is the largest multiple
+#                                 of 1/16 that leaves fewer than half of the
+#                                 queries at the cap (-3.1875: 57%).
 CONFIGS = {
     "tiny": Workload(
         name="tiny", heads=2, head_dim=64, T=8, H=16, W=16, dtype="fp32",
