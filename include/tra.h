@@ -197,6 +197,12 @@ tra_status tra_radius_table(const tra_shape* shape, const tra_params* params, in
  * runs on first use by tra_plan_export (row_ptr / col_idx), tra_plan_stats
  * or tra_plan_get_info, which then synchronise.  Other plans (fp32, vote
  * threshold) build the CSR at once and synchronise `stream` once to size it.
+ * An asynchronous rebuild and the attention calls that follow it can be
+ * captured in a HIP graph (they launch kernels and record one event, nothing
+ * else).  The plan's host-side state (its validity, whether its CSR is
+ * complete) follows the calls the host makes, not graph replays: after a
+ * replay that rebuilt the plan from other inputs, make an eager rebuild
+ * before exporting the CSR.
  * *out receives the plan, which owns all its device memory (including the
  * scratch of tra_plan_stats and tra_plan_drift); on failure nothing is kept
  * and *out stays NULL.
