@@ -401,11 +401,14 @@ __device__ __forceinline__ int mask_half_width(int thr, int dh) {
 
 // One wave per query tile (8 x 8 tiles: 64 queries).  The wave's four rows of
 // 16 lanes take four (temporal distance, key-tile row) pairs at a time; in a
-// pair, lane i folds the footprints of queries i, 16 + i, 32 + i and 48 + i
-// in registers, and one reduction over the 16 lanes of the row gives the
-// run.  The radius table is staged in LDS (dynamic): per level row its
-// largest active distance and the offset of its active entries in the
-// compact table, then the compact table itself.
+// pair, lane i folds the footprints of queries i, 16 + i, 32 + i and 48 + i,
+// and one reduction over the 16 lanes of the row gives the run.  Those four
+// queries share one column w (tiles are 8 wide), so their intervals
+// [w - a, w + a] are nested and the widest decides: a lane takes the largest
+// R2 - dh^2 (L1: R - |dh|) of its four queries and one square root.  The
+// radius table is staged in LDS (dynamic): per level row its largest active
+// distance and the offset of its active entries in the compact table, then
+// the compact table itself.
 template <bool L1>
 __global__ __launch_bounds__(256) void csr_runs_kernel(const int16_t* __restrict__ lv,
                                                       const int32_t* __restrict__ r2c,
@@ -460,23 +463,33 @@ __global__ __launch_bounds__(256) void csr_runs_kernel(const int16_t* __restrict
   int32_t* rrow = runs + row * static_cast<int64_t>((2 * DM + 1) * g.nh);
   int count = 0;
   // Pairs (delta, key-tile row), delta-major; frames tq - delta and tq +
-  // delta see the same disks, so each pair's run is written for both.
+  // delta see the same disks, so each pair's run is written for both.  The
+  // pair index p = p0 + grp advances by 4 per step; (delta, tr) follow it.
   const int npairs = (dmw + 1) * g.nh;
+  int delta = grp / g.nh, tr = grp % g.nh;
+  const int wl = wq[0];  // the lane's column: the same for its four queries (tiles are 8 wide)
   for (int p0 = 0; p0 < npairs; p0 += 4) {
-    const int p = p0 + grp;
-    const bool live = p < npairs;
-    const int delta = live ? p / g.nh : 0, tr = live ? p % g.nh : 0;
+    const bool live = p0 + grp < npairs;
     const int r0 = tr * g.th, r1 = min(g.H, r0 + g.th) - 1;
-    int lo = 0x7fffffff, hi = -1;
+    // Largest squared (L1: plain) half-width over the lane's four queries at
+    // the nearest key row of the tile row; negative when none keeps a key.
+    // (the four table reads are in bounds for every lane and issued
+    // together; `live` only masks the result)
+    int vt[4];
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) vt[k4] = r2c_s[toff[k4] + min(delta, max(dm[k4], 0))];
+    int best = -1;
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4) {
-      const int thr = (live && delta <= dm[k4]) ? r2c_s[toff[k4] + delta] : -1;
       const int dh = max(0, max(r0 - hq[k4], hq[k4] - r1));
-      const int a = thr >= 0 ? mask_half_width<L1>(thr, dh) : -1;
-      if (a >= 0) {
-        lo = min(lo, max(0, wq[k4] - a) >> tw_shift);
-        hi = max(hi, min(g.W - 1, wq[k4] + a) >> tw_shift);
-      }
+      const int w2 = L1 ? vt[k4] - dh : vt[k4] - dh * dh;
+      best = max(best, (delta <= dm[k4] && vt[k4] >= 0) ? w2 : -1);
+    }
+    const int a = (live && best >= 0) ? mask_reach<L1>(best) : -1;
+    int lo = 0x7fffffff, hi = -1;
+    if (a >= 0) {
+      lo = max(0, wl - a) >> tw_shift;
+      hi = min(g.W - 1, wl + a) >> tw_shift;
     }
     // Min / max over the 16 lanes of this row (DPP inside rows of 16).
     lo = min(lo, __builtin_amdgcn_update_dpp(0, lo, 0xB1, 0xF, 0xF, false));
@@ -493,6 +506,11 @@ __global__ __launch_bounds__(256) void csr_runs_kernel(const int16_t* __restrict
       if (hi >= lo) count += (hi - lo + 1) * ((below ? 1 : 0) + (above ? 1 : 0));
       if (below) rrow[(tq - delta - t_lo) * g.nh + tr] = run;
       if (above) rrow[(tq + delta - t_lo) * g.nh + tr] = run;
+    }
+    tr += 4;
+    while (tr >= g.nh) {
+      tr -= g.nh;
+      ++delta;
     }
   }
   count = wave_sum_u(count);
