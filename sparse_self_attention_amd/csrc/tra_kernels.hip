@@ -399,13 +399,12 @@ __device__ __forceinline__ int mask_half_width(int thr, int dh) {
   return rem >= 0 ? isqrt_i(rem) : -1;
 }
 
-// One wave per query tile (8 x 8 tiles: 64 queries).  The wave's four rows of
-// 16 lanes take four (temporal distance, key-tile row) pairs at a time; in a
-// pair, lane i folds the footprints of queries i, 16 + i, 32 + i and 48 + i,
-// and one reduction over the 16 lanes of the row gives the run.  Those four
-// queries share one column w (tiles are 8 wide), so their intervals
-// [w - a, w + a] are nested and the widest decides: a lane takes the largest
-// R2 - dh^2 (L1: R - |dh|) of its four queries and one square root.  The
+// One wave per query tile (8 x 8 tiles: 64 queries).  The wave's eight groups
+// of 8 lanes take eight (temporal distance, key-tile row) pairs at a time; in
+// a pair, lane c folds the 8 queries of tile column c, and one reduction over
+// the group's 8 lanes gives the run.  A column's queries share their center
+// w, so their intervals [w - a, w + a] are nested and the widest decides: the
+// lane takes the largest R2 - dh^2 (L1: R - |dh|) and one square root.  The
 // radius table is staged in LDS (dynamic): per level row its largest active
 // distance and the offset of its active entries in the compact table, then
 // the compact table itself.
@@ -437,26 +436,24 @@ __global__ __launch_bounds__(256) void csr_runs_kernel(const int16_t* __restrict
   const int64_t row = static_cast<int64_t>(bh) * g.count + tile;
   const int tq = tile / g.per_frame, rem = tile % g.per_frame;
   const int h0 = (rem / g.nw) * g.th, w0 = (rem % g.nw) * g.tw;
-  const int li = lane & 15, grp = lane >> 4;
-  // This lane's four queries (tile-local index 16*k + li, row-major in the
-  // 8 x 8 tile): coordinates, table offset and largest active distance
+  // Lane 8*grp + c takes column c of the tile (its 8 queries, one per tile
+  // row) in pair group grp: table offset and largest active distance per row
   // (dm = -1 for positions outside the grid).
-  int hq[4], wq[4], toff[4], dm[4];
+  const int c = lane & 7, grp = lane >> 3;
+  const int wl = w0 + c;
+  int toff[8], dm[8];
   int dmx = -1;
 #pragma unroll
-  for (int k4 = 0; k4 < 4; ++k4) {
-    const int qi = 16 * k4 + li;
-    hq[k4] = h0 + (qi >> tw_shift);
-    wq[k4] = w0 + (qi & (g.tw - 1));
-    toff[k4] = 0;
-    dm[k4] = -1;
-    if (hq[k4] < g.H && wq[k4] < g.W) {
+  for (int r = 0; r < 8; ++r) {
+    toff[r] = 0;
+    dm[r] = -1;
+    if (h0 + r < g.H && wl < g.W) {
       const int trow =
-          lv[static_cast<size_t>(bh) * N + (static_cast<size_t>(tq) * g.H + hq[k4]) * g.W + wq[k4]] - row_base;
-      toff[k4] = off_s[trow];
-      dm[k4] = dmax_s[trow];
+          lv[static_cast<size_t>(bh) * N + (static_cast<size_t>(tq) * g.H + h0 + r) * g.W + wl] - row_base;
+      toff[r] = off_s[trow];
+      dm[r] = dmax_s[trow];
     }
-    dmx = max(dmx, dm[k4]);
+    dmx = max(dmx, dm[r]);
   }
   const int dmw = wave_max_u(dmx);
   const int t_lo = max(0, tq - dmw), t_hi = min(T - 1, tq + dmw);
@@ -464,26 +461,28 @@ __global__ __launch_bounds__(256) void csr_runs_kernel(const int16_t* __restrict
   int count = 0;
   // Pairs (delta, key-tile row), delta-major; frames tq - delta and tq +
   // delta see the same disks, so each pair's run is written for both.  The
-  // pair index p = p0 + grp advances by 4 per step; (delta, tr) follow it.
+  // eight lane groups take eight pairs per step: pair p = p0 + grp, with
+  // (delta, tr) advanced incrementally.
   const int npairs = (dmw + 1) * g.nh;
   int delta = grp / g.nh, tr = grp % g.nh;
-  const int wl = wq[0];  // the lane's column: the same for its four queries (tiles are 8 wide)
-  for (int p0 = 0; p0 < npairs; p0 += 4) {
+  for (int p0 = 0; p0 < npairs; p0 += 8) {
     const bool live = p0 + grp < npairs;
     const int r0 = tr * g.th, r1 = min(g.H, r0 + g.th) - 1;
-    // Largest squared (L1: plain) half-width over the lane's four queries at
-    // the nearest key row of the tile row; negative when none keeps a key.
-    // (the four table reads are in bounds for every lane and issued
-    // together; `live` only masks the result)
-    int vt[4];
+    // The column's 8 queries share its center, so their intervals are nested
+    // and the widest decides: the largest R2 - dh^2 (L1: R - |dh|) at the
+    // nearest key row of the tile row, then one square root.  (The table
+    // reads are in bounds for every lane and issued together; `live` only
+    // masks the result.)
+    int vt[8];
 #pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) vt[k4] = r2c_s[toff[k4] + min(delta, max(dm[k4], 0))];
+    for (int r = 0; r < 8; ++r) vt[r] = r2c_s[toff[r] + min(delta, max(dm[r], 0))];
     int best = -1;
 #pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-      const int dh = max(0, max(r0 - hq[k4], hq[k4] - r1));
-      const int w2 = L1 ? vt[k4] - dh : vt[k4] - dh * dh;
-      best = max(best, (delta <= dm[k4] && vt[k4] >= 0) ? w2 : -1);
+    for (int r = 0; r < 8; ++r) {
+      const int hq = h0 + r;
+      const int dh = max(0, max(r0 - hq, hq - r1));
+      const int w2 = L1 ? vt[r] - dh : vt[r] - dh * dh;
+      best = max(best, delta <= dm[r] ? w2 : -1);
     }
     const int a = (live && best >= 0) ? mask_reach<L1>(best) : -1;
     int lo = 0x7fffffff, hi = -1;
@@ -491,23 +490,22 @@ __global__ __launch_bounds__(256) void csr_runs_kernel(const int16_t* __restrict
       lo = max(0, wl - a) >> tw_shift;
       hi = min(g.W - 1, wl + a) >> tw_shift;
     }
-    // Min / max over the 16 lanes of this row (DPP inside rows of 16).
+    // Min / max over the 8 lanes of the group: within quads, then across the
+    // two quads of each half row (row_half_mirror pairs lane i with 7 - i).
     lo = min(lo, __builtin_amdgcn_update_dpp(0, lo, 0xB1, 0xF, 0xF, false));
     hi = max(hi, __builtin_amdgcn_update_dpp(0, hi, 0xB1, 0xF, 0xF, false));
     lo = min(lo, __builtin_amdgcn_update_dpp(0, lo, 0x4E, 0xF, 0xF, false));
     hi = max(hi, __builtin_amdgcn_update_dpp(0, hi, 0x4E, 0xF, 0xF, false));
-    lo = min(lo, __builtin_amdgcn_update_dpp(0, lo, 0x124, 0xF, 0xF, false));
-    hi = max(hi, __builtin_amdgcn_update_dpp(0, hi, 0x124, 0xF, 0xF, false));
-    lo = min(lo, __builtin_amdgcn_update_dpp(0, lo, 0x128, 0xF, 0xF, false));
-    hi = max(hi, __builtin_amdgcn_update_dpp(0, hi, 0x128, 0xF, 0xF, false));
-    if (live && li == 0) {
+    lo = min(lo, __builtin_amdgcn_update_dpp(0, lo, 0x141, 0xF, 0xF, false));
+    hi = max(hi, __builtin_amdgcn_update_dpp(0, hi, 0x141, 0xF, 0xF, false));
+    if (live && c == 0) {
       const bool below = tq - delta >= 0, above = delta > 0 && tq + delta <= T - 1;
       const int32_t run = hi >= lo ? (lo | (hi << 16)) : RUN_EMPTY;
       if (hi >= lo) count += (hi - lo + 1) * ((below ? 1 : 0) + (above ? 1 : 0));
       if (below) rrow[(tq - delta - t_lo) * g.nh + tr] = run;
       if (above) rrow[(tq + delta - t_lo) * g.nh + tr] = run;
     }
-    tr += 4;
+    tr += 8;
     while (tr >= g.nh) {
       tr -= g.nh;
       ++delta;
