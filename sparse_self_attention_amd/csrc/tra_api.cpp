@@ -332,6 +332,7 @@ struct tra_plan {
   // the counts and runs on first use (export, stats, info).
   bool lazy_csr = false;
   bool csr_ready = false;
+  int64_t glist_stride = 0;  // lazy-CSR plans: group g's list starts at entry g * glist_stride
   hipEvent_t built = nullptr;  // recorded at the end of each lazy build
 };
 
@@ -390,19 +391,15 @@ tra_status build(tra_plan* p, const void* q, const void* k, const float* Hin, hi
 tra_status build_group_lists_only(tra_plan* p, hipStream_t st) {
   const tra_shape& s = p->shape;
   p->csr_ready = false;
+  // Each group writes its list into its own fixed slot (gptr[g] = g * stride,
+  // set at creation) and its length to glen: no counting pass, no scan.
   if (p->params.generator == TRA_GEN_WINDOW_1D) {
-    TRA_LAUNCH(tra::launch_window_groups(false, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, nullptr,
-                                      nullptr, p->glen, st));
-    TRA_LAUNCH(tra::launch_scan(p->glen, p->n_groups, p->gptr, p->totals + 4, st));
     TRA_LAUNCH(tra::launch_window_groups(true, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, p->gptr,
                                       p->glist, p->glen, st));
   } else {
     TRA_LAUNCH(tra::launch_csr_runs(p->params.generator == TRA_GEN_MANHATTAN, p->lv, radius_table_of(p),
                                     p->table.n_levels, p->row_base, p->BH, p->tiles, p->DM, p->counts, p->runs,
                                     p->rowwin, st));
-    TRA_LAUNCH(tra::launch_group_lists(false, p->BH, p->tiles, p->DM, p->runs, p->rowwin, nullptr, nullptr, nullptr,
-                                    nullptr, p->glen, st));
-    TRA_LAUNCH(tra::launch_scan(p->glen, p->n_groups, p->gptr, p->totals + 4, st));
     TRA_LAUNCH(tra::launch_group_lists(true, p->BH, p->tiles, p->DM, p->runs, p->rowwin, nullptr, nullptr, p->gptr,
                                     p->glist, p->glen, st));
   }
@@ -636,6 +633,10 @@ tra_status create_plan(const tra_shape* shape, const tra_params* params, Table&&
       p->lazy_csr = true;
       TRA_HIP_P(dev_alloc(&p->glist, bound * 2 * sizeof(int32_t)));
       p->glist_cap = bound;
+      p->glist_stride = per_group;
+      std::vector<int32_t> slots(p->n_groups + 1);
+      for (int64_t g = 0; g <= p->n_groups; ++g) slots[g] = static_cast<int32_t>(g * per_group);
+      TRA_HIP_P(hipMemcpy(p->gptr, slots.data(), slots.size() * sizeof(int32_t), hipMemcpyHostToDevice));
       TRA_HIP_P(hipEventCreateWithFlags(&p->built, hipEventDisableTiming));
     }
   }
@@ -963,6 +964,33 @@ tra_status tra_plan_export_groups(const tra_plan* plan, int64_t* n_groups, int64
   if (plan->shape.dtype != TRA_BF16) return fail(TRA_ERR_DTYPE, "group lists exist for bf16 plans only");
   hipStream_t hs = static_cast<hipStream_t>(stream);
   TRA_HIP(hipStreamSynchronize(hs));
+  if (plan->glist_stride > 0) {
+    // Lists in fixed per-group slots: returned packed, in group order.
+    std::vector<int32_t> len(plan->n_groups);
+    TRA_HIP(hipMemcpy(len.data(), plan->glen, plan->n_groups * sizeof(int32_t), hipMemcpyDeviceToHost));
+    int64_t entries = 0;
+    for (int32_t l : len) entries += l;
+    if (n_groups) *n_groups = plan->n_groups;
+    if (n_entries) *n_entries = entries;
+    if (glen) std::memcpy(glen, len.data(), len.size() * sizeof(int32_t));
+    if (gptr) {
+      int64_t off = 0;
+      for (int64_t g = 0; g < plan->n_groups; ++g) {
+        gptr[g] = static_cast<int32_t>(off);
+        off += len[g];
+      }
+    }
+    if (glist && entries > 0) {
+      std::vector<int32_t> all(static_cast<size_t>(plan->n_groups) * plan->glist_stride * 2);
+      TRA_HIP(hipMemcpy(all.data(), plan->glist, all.size() * sizeof(int32_t), hipMemcpyDeviceToHost));
+      int64_t off = 0;
+      for (int64_t g = 0; g < plan->n_groups; ++g) {
+        std::memcpy(glist + 2 * off, all.data() + 2 * g * plan->glist_stride, 2 * len[g] * sizeof(int32_t));
+        off += len[g];
+      }
+    }
+    return TRA_OK;
+  }
   int32_t last[2] = {0, 0};
   TRA_HIP(hipMemcpy(&last[0], plan->gptr + plan->n_groups - 1, sizeof(int32_t), hipMemcpyDeviceToHost));
   TRA_HIP(hipMemcpy(&last[1], plan->glen + plan->n_groups - 1, sizeof(int32_t), hipMemcpyDeviceToHost));
