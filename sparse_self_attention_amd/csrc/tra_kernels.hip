@@ -243,65 +243,87 @@ __global__ __launch_bounds__(256, 3) void entropy_bf16_kernel(
     // A chunk of full rectangles only (they come first) has one weight, which
     // then scales the chunk's two sums instead of each term.
     const bool uniform = (ci + 1) * 32 <= NFULL;
-#pragma unroll
-    for (int qb = 0; qb < ENT_QB; ++qb) {
-      const f32x16& sc = acc[qb];
-      float mx = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
-#pragma unroll
-      for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sc[i]), sc[i + 1]);
-      mx = fmaxf(mx, sc[15]);
-      const float mnew = fmaxf(m[qb], mx * c1);
-      float sA = 0.f, sB = 0.f;
+    // A lane's terms against the reference ref, unweighted in a uniform chunk.
+    auto sums = [&](const f32x16& sc, float ref, float& sA, float& sB) __attribute__((always_inline)) {
+      sA = 0.f;
+      sB = 0.f;
       if (uniform) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float t = fmaf(sc[i], c1, -mnew);
+          const float t = fmaf(sc[i], c1, -ref);
           const float e = __builtin_amdgcn_exp2f(t);
           sA += e;
           sB = fmaf(e, t, sB);
         }
-        sA *= WFULL;
-        sB *= WFULL;
       } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float t = fmaf(sc[i], c1, -mnew);
+          const float t = fmaf(sc[i], c1, -ref);
           const float e = __builtin_amdgcn_exp2f(t) * w[i];
           sA += e;
           sB = fmaf(e, t, sB);
         }
       }
-      if (A[qb] > 0.f) {
-        const float alpha = __builtin_amdgcn_exp2f(m[qb] - mnew);
-        Bm[qb] = alpha * fmaf(m[qb] - mnew, A[qb], Bm[qb]) + sB;
-        A[qb] = fmaf(A[qb], alpha, sA);
+    };
+    // Lazy reference: the terms are formed against the current reference;
+    // only when some lane's sum leaves its bound (2^10 unweighted, 2^24
+    // weighted) or is not finite, as on the first chunk (no reference yet),
+    // does the wave move the reference to the exact maximum and form them
+    // again.  The bounds keep every term and sum far from overflow, and a
+    // reference above the chunk's scores loses nothing: it is at least the
+    // largest score seen so far.
+    const float bound = uniform ? 1024.f : 16777216.f;
+#pragma unroll
+    for (int qb = 0; qb < ENT_QB; ++qb) {
+      const f32x16& sc = acc[qb];
+      float sA, sB;
+      sums(sc, m[qb], sA, sB);
+      if (__any(!(sA <= bound))) {
+        float mx = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
+#pragma unroll
+        for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sc[i]), sc[i + 1]);
+        mx = fmaxf(mx, sc[15]);
+        // The two lane halves hold the same queries (16 keys each) and keep
+        // one reference: each takes the other's chunk maximum.
+        const auto mxs = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(mxs[0]), __uint_as_float(mxs[1]));
+        const float mnew = fmaxf(m[qb], mx * c1);
+        sums(sc, mnew, sA, sB);
+        if (uniform) {
+          sA *= WFULL;
+          sB *= WFULL;
+        }
+        if (A[qb] > 0.f) {
+          const float alpha = __builtin_amdgcn_exp2f(m[qb] - mnew);
+          Bm[qb] = alpha * fmaf(m[qb] - mnew, A[qb], Bm[qb]) + sB;
+          A[qb] = fmaf(A[qb], alpha, sA);
+        } else {
+          Bm[qb] = sB;
+          A[qb] = sA;
+        }
+        m[qb] = mnew;
       } else {
-        Bm[qb] = sB;
-        A[qb] = sA;
+        if (uniform) {
+          sA *= WFULL;
+          sB *= WFULL;
+        }
+        Bm[qb] += sB;
+        A[qb] += sA;
       }
-      m[qb] = mnew;
     }
   }
-#pragma unroll
-  for (int qb = 0; qb < ENT_QB; ++qb) {
-    const int n = n0 + 32 * qb;
-    const float mp = __shfl_xor(m[qb], 32), Ap = __shfl_xor(A[qb], 32), Bp = __shfl_xor(Bm[qb], 32);
-    if (h == 0 && n < N) {
-      const double M = fmax(static_cast<double>(m[qb]), static_cast<double>(mp));
-      double At = 0.0, Bt = 0.0;
-      if (A[qb] > 0.f) {
-        const double s0 = exp2(static_cast<double>(m[qb]) - M);
-        At += s0 * A[qb];
-        Bt += s0 * (static_cast<double>(Bm[qb]) + (static_cast<double>(m[qb]) - M) * A[qb]);
-      }
-      if (Ap > 0.f) {
-        const double s1 = exp2(static_cast<double>(mp) - M);
-        At += s1 * Ap;
-        Bt += s1 * (static_cast<double>(Bp) + (static_cast<double>(mp) - M) * Ap);
-      }
-      const double Hd = log(At) - 0.6931471805599453 * Bt / At;
-      entropy_store(Hd, ea, static_cast<size_t>(bh) * N + n, Hout, lvout);
-    }
+  // Both halves share the reference, so a query's sums are the plain sums of
+  // its two halves.  Lanes 0-31 finish query block 0 and lanes 32-63 block 1:
+  // one swap gives each half the other half's sums of its block.
+  static_assert(ENT_QB == 2, "one query block per lane half");
+  const auto As = __builtin_amdgcn_permlane32_swap(__float_as_uint(A[0]), __float_as_uint(A[1]), false, false);
+  const auto Bs = __builtin_amdgcn_permlane32_swap(__float_as_uint(Bm[0]), __float_as_uint(Bm[1]), false, false);
+  const int n = n0 + 32 * h;
+  if (n < N) {
+    const double At = static_cast<double>(__uint_as_float(As[0])) + static_cast<double>(__uint_as_float(As[1]));
+    const double Bt = static_cast<double>(__uint_as_float(Bs[0])) + static_cast<double>(__uint_as_float(Bs[1]));
+    const double Hd = log(At) - 0.6931471805599453 * Bt / At;
+    entropy_store(Hd, ea, static_cast<size_t>(bh) * N + n, Hout, lvout);
   }
 }
 
