@@ -25,7 +25,8 @@
 //                         O^T += V^T P^T on 32x32x16 bf16 MFMA, K/V tiles staged
 //                         in LDS (V read back transposed with ds_read_b64_tr_b16),
 //                         exact radius mask in registers, fp32 online softmax
-//   attn_f32_kernel       plain fp32 vector variant for fp32 inputs
+//   attn_f32_kernel       fp32 vector variant for fp32 inputs: one query per
+//                         lane, the tile's list split over the workgroup's waves
 //   retained_kernel,      exact retained / listed pair counts
 //   listed_kernel
 //   level_diff_kernel     plan drift: queries whose level a rebuild would change
@@ -1433,16 +1434,24 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
   }
 }
 
-// fp32 inputs: one thread per query, K/V tiles in LDS, fp32 online softmax.
+// fp32 inputs: a workgroup of f32_split<D> waves per query tile, lane =
+// query (tile-local row-major).  The work units are the half key tiles (32
+// keys: rows 0-3 or 4-7) of the tile's list; wave w takes units w, w + S, ...
+// into its own LDS slot and runs an fp32 online softmax over them.  The
+// waves' partial states (reference, sum, accumulator) are then merged in
+// pairs through LDS.  The split puts S waves to work per query tile on small
+// grids, two per SIMD at d = 64.
+template <int D> constexpr int f32_split() { return D == 64 ? 8 : 4; }  // 128 KB of LDS either way
 template <int D, int METRIC, bool BLOCK>
-__global__ __launch_bounds__(64) void attn_f32_kernel(
+__global__ __launch_bounds__(64 * f32_split<D>()) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, const int16_t* __restrict__ lv, const int32_t* __restrict__ r2,
     int row_base, int T, Grid g, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx) {
-  __shared__ float k_lds[64][D];
-  __shared__ float v_lds[64][D];
-  const int lane = threadIdx.x;
+  constexpr int S = f32_split<D>();
+  __shared__ float kv_lds[S][2][32][D];  // per wave: K rows, V rows of its current half tile
+  static_assert((S / 2) * 64 * (D + 2) <= S * 2 * 32 * D, "a merge round fits in the tile slots");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = blockIdx.x;
   const int bh = row / g.count, tile = row % g.count;
   const size_t N = static_cast<size_t>(g.T) * g.H * g.W;
@@ -1464,53 +1473,90 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
   float mref = TRA_NEG_INF, lsum = 0.f;
   const float* kbase = k + static_cast<size_t>(bh) * N * D;
   const float* vbase = v + static_cast<size_t>(bh) * N * D;
+  float (*k_lds)[D] = kv_lds[wave][0];
+  float (*v_lds)[D] = kv_lds[wave][1];
   const int beg = row_ptr[row], end = row_ptr[row + 1];
-  for (int e = beg; e < end; ++e) {
-    const int kt = col_idx[e];
+  const int units = 2 * (end - beg);
+  const int steps = (units + S - 1) / S;  // the same for every wave of the workgroup
+  for (int it = 0; it < steps; ++it) {
+    const int u = it * S + wave;
+    const bool have = u < units;  // wave-uniform
+    const int kt = have ? col_idx[beg + (u >> 1)] : 0;
     const int tk = kt / g.per_frame, krem = kt % g.per_frame;
-    const int kr0 = (krem / g.nw) * 8, kc0 = (krem % g.nw) * 8;
+    const int kr0 = (krem / g.nw) * 8 + 4 * (u & 1), kc0 = (krem % g.nw) * 8;
     __syncthreads();
-    for (int idx = lane; idx < 64 * D / 4; idx += 64) {
-      const int kk = idx / (D / 4), c = idx % (D / 4);
-      const int kr = min(kr0 + (kk >> 3), g.H - 1), kc = min(kc0 + (kk & 7), g.W - 1);
-      const size_t nk = (static_cast<size_t>(tk) * g.H + kr) * g.W + kc;
-      *reinterpret_cast<float4*>(&k_lds[kk][4 * c]) = *reinterpret_cast<const float4*>(kbase + nk * D + 4 * c);
-      *reinterpret_cast<float4*>(&v_lds[kk][4 * c]) = *reinterpret_cast<const float4*>(vbase + nk * D + 4 * c);
+    if (have) {
+      for (int idx = lane; idx < 32 * D / 4; idx += 64) {
+        const int kk = idx / (D / 4), c = idx % (D / 4);
+        const int kr = min(kr0 + (kk >> 3), g.H - 1), kc = min(kc0 + (kk & 7), g.W - 1);
+        const size_t nk = (static_cast<size_t>(tk) * g.H + kr) * g.W + kc;
+        *reinterpret_cast<float4*>(&k_lds[kk][4 * c]) = *reinterpret_cast<const float4*>(kbase + nk * D + 4 * c);
+        *reinterpret_cast<float4*>(&v_lds[kk][4 * c]) = *reinterpret_cast<const float4*>(vbase + nk * D + 4 * c);
+      }
     }
     __syncthreads();
-    const int delta = tk > tq ? tk - tq : tq - tk;
-    const int thr = qvalid ? r2row[delta] : -1;
-    for (int kk = 0; kk < 64; ++kk) {
-      const int kr = kr0 + (kk >> 3), kc = kc0 + (kk & 7);
-      const int dh = hq - kr, dw = wq - kc;
-      if (kr >= g.H || kc >= g.W) continue;
-      if (!BLOCK) {
-        if (thr < 0) continue;
-        if (METRIC == METRIC_WINDOW) {
-          const long long dn = static_cast<long long>(nq) - ((static_cast<long long>(tk) * g.H + kr) * g.W + kc);
-          if (dn > thr || -dn > thr) continue;
-        } else if ((METRIC == METRIC_L1 ? abs(dh) + abs(dw) : dh * dh + dw * dw) > thr) {
-          continue;
+    if (have) {
+      const int delta = tk > tq ? tk - tq : tq - tk;
+      const int thr = qvalid ? r2row[delta] : -1;
+      for (int kk = 0; kk < 32; ++kk) {
+        const int kr = kr0 + (kk >> 3), kc = kc0 + (kk & 7);
+        const int dh = hq - kr, dw = wq - kc;
+        if (kr >= g.H || kc >= g.W) continue;
+        if (!BLOCK) {
+          if (thr < 0) continue;
+          if (METRIC == METRIC_WINDOW) {
+            const long long dn = static_cast<long long>(nq) - ((static_cast<long long>(tk) * g.H + kr) * g.W + kc);
+            if (dn > thr || -dn > thr) continue;
+          } else if ((METRIC == METRIC_L1 ? abs(dh) + abs(dw) : dh * dh + dw * dw) > thr) {
+            continue;
+          }
         }
+        float sc = 0.f;
+#pragma unroll
+        for (int dd = 0; dd < D; ++dd) sc = fmaf(qr[dd], k_lds[kk][dd], sc);
+        sc *= scale;
+        if (sc > mref) {
+          const float alpha = expf(mref - sc);
+          lsum *= alpha;
+#pragma unroll
+          for (int dd = 0; dd < D; ++dd) acc[dd] *= alpha;
+          mref = sc;
+        }
+        const float p = expf(sc - mref);
+        lsum += p;
+#pragma unroll
+        for (int dd = 0; dd < D; ++dd) acc[dd] = fmaf(p, v_lds[kk][dd], acc[dd]);
       }
-      float s = 0.f;
-#pragma unroll
-      for (int dd = 0; dd < D; ++dd) s = fmaf(qr[dd], k_lds[kk][dd], s);
-      s *= scale;
-      if (s > mref) {
-        const float alpha = expf(mref - s);
-        lsum *= alpha;
-#pragma unroll
-        for (int dd = 0; dd < D; ++dd) acc[dd] *= alpha;
-        mref = s;
-      }
-      const float p = expf(s - mref);
-      lsum += p;
-#pragma unroll
-      for (int dd = 0; dd < D; ++dd) acc[dd] = fmaf(p, v_lds[kk][dd], acc[dd]);
     }
   }
-  if (qvalid) {
+  // Pairwise merge: in each round the upper half of the remaining waves
+  // writes its state, and wave w of the lower half folds in wave w + half's.
+  // A state without a kept key (reference -inf) adds nothing.
+  float* st = &kv_lds[0][0][0][0];
+#pragma unroll
+  for (int half = S / 2; half >= 1; half /= 2) {
+    __syncthreads();
+    if (wave >= half && wave < 2 * half) {
+      float* mine = st + ((wave - half) * 64 + lane) * (D + 2);
+      mine[0] = mref;
+      mine[1] = lsum;
+#pragma unroll
+      for (int dd = 0; dd < D; ++dd) mine[2 + dd] = acc[dd];
+    }
+    __syncthreads();
+    if (wave < half) {
+      const float* other = st + (wave * 64 + lane) * (D + 2);
+      const float mo = other[0];
+      const float M = fmaxf(mref, mo);
+      const float fa = mref == TRA_NEG_INF ? 0.f : expf(mref - M);
+      const float fb = mo == TRA_NEG_INF ? 0.f : expf(mo - M);
+      lsum = lsum * fa + other[1] * fb;
+#pragma unroll
+      for (int dd = 0; dd < D; ++dd) acc[dd] = acc[dd] * fa + other[2 + dd] * fb;
+      mref = M;
+    }
+  }
+  if (wave == 0 && qvalid) {
     float* op = o + (static_cast<size_t>(bh) * N + nq) * D;
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;  // no key under a vote threshold: O = 0
 #pragma unroll
@@ -1776,7 +1822,8 @@ hipError_t launch_attention(int dtype, int d, const void* q, const void* k, cons
     const auto* vv = static_cast<const float*>(v);
     auto* oo = static_cast<float*>(o);
 #define TRA_ATTN32(DD, M, B) \
-  attn_f32_kernel<DD, M, B><<<rows, 64, 0, s>>>(qq, kk, vv, oo, lv, r2, row_base, tiles.T, tiles, row_ptr, col_idx)
+  attn_f32_kernel<DD, M, B><<<rows, 64 * f32_split<DD>(), 0, s>>>(qq, kk, vv, oo, lv, r2, row_base, tiles.T, tiles, \
+                                                                 row_ptr, col_idx)
     if (block_mask) {
       if (d == 128) TRA_ATTN32(128, METRIC_L2, true);
       else TRA_ATTN32(64, METRIC_L2, true);
