@@ -109,6 +109,9 @@ def main():
                     help="plan variant: list a key tile only with at least this many retained pairs")
     ap.add_argument("--block-mask", action="store_true",
                     help="plan variant: block-only masks (every key of a listed tile)")
+    ap.add_argument("--regroup", action="store_true",
+                    help="plan variant: each query-tile group's queries dealt to the attention "
+                         "kernel's waves in level order")
     ap.add_argument("--generator", choices=["entropy_disk", "manhattan", "radial", "window_1d"],
                     default="entropy_disk")
     ap.add_argument("--radius", type=float, default=None, help="fixed radius (static generators)")
@@ -138,6 +141,8 @@ def main():
         variant["vote_threshold"] = args.vote_threshold
     if args.block_mask:
         variant["block_mask"] = 1
+    if args.regroup:
+        variant["regroup"] = 1
     if args.generator != "entropy_disk":
         variant["generator"] = tra.GENERATORS[args.generator]
         if args.radius is not None or args.generator != "window_1d":

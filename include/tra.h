@@ -108,6 +108,18 @@ typedef struct {
   int32_t block_mask;     /* 0: exact per-token mask inside listed tiles;
                              1: block-only mask, every key of a listed tile
                              (the block-sparse execution the pages feed) */
+  int32_t regroup;        /* 0: each 32-query wave of the bf16 attention kernel
+                             takes half of one 8 x 8 query tile; 1: the queries
+                             of each group of 2 x 2 query tiles are sorted by
+                             budget level (ties in raster order within the
+                             group) and dealt to the waves in that order, so
+                             that a wave's queries have nearly one radius ([TRA] section
+                             2, "Exécution Efficace", tile-major layout, read
+                             as query regrouping by level).  The tile lists and
+                             the retained pairs are the same either way.  bf16
+                             only, with the exact mask (block_mask 0) and
+                             vote_threshold 1, which define the keys per
+                             query rather than per query tile. */
 } tra_params;
 
 /*
@@ -279,6 +291,18 @@ tra_status tra_plan_export(const tra_plan* plan, int16_t* levels, float* entropy
  */
 tra_status tra_plan_export_groups(const tra_plan* plan, int64_t* n_groups, int64_t* n_entries, int32_t* gptr,
                                   int32_t* glen, int32_t* glist, void* stream);
+
+/*
+ * Query regrouping ([TRA] section 2, "Exécution Efficace"; plans created with
+ * params.regroup = 1; host copy, synchronises `stream`): for each group, in
+ * the order of tra_plan_export_groups, its 256 query positions as slots
+ * (row * 16 + column inside the group's 16 x 16 positions) in the order the
+ * attention kernel deals them to its waves, 32 per wave: ascending budget
+ * level, ties by slot, positions outside the grid last.  perm: uint8
+ * [n_groups * 256].  TRA_ERR_INVALID_ARG for a plan created without regroup
+ * or a NULL argument.
+ */
+tra_status tra_plan_export_regroup(const tra_plan* plan, uint8_t* perm, void* stream);
 
 /*
  * Exact pair counts of a plan (synchronises `stream`; counters live in the

@@ -43,7 +43,7 @@ class _Params(ctypes.Structure):
                 ("radius_override", ctypes.c_double), ("levels_per_nat", ctypes.c_int32),
                 ("pool_h", ctypes.c_int32), ("pool_w", ctypes.c_int32), ("tile_h", ctypes.c_int32),
                 ("tile_w", ctypes.c_int32), ("generator", ctypes.c_int32), ("vote_threshold", ctypes.c_int32),
-                ("block_mask", ctypes.c_int32)]
+                ("block_mask", ctypes.c_int32), ("regroup", ctypes.c_int32)]
 
 
 class _Info(ctypes.Structure):
@@ -87,6 +87,7 @@ _SIGS = {
     "tra_dense_attention": (ctypes.c_int, [ctypes.POINTER(_Shape), _P, _P, _P, _P, _P, _P]),
     "tra_plan_export_groups": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
                                               _P, _P, _P, _P]),
+    "tra_plan_export_regroup": (ctypes.c_int, [_P, _P, _P]),
     "tra_schedule_create": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.POINTER(_Params),
                                            ctypes.POINTER(_SchedParams), ctypes.POINTER(_P)]),
     "tra_schedule_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.POINTER(_StepInfo)]),
@@ -132,7 +133,7 @@ def _check(status, fn):
 
 DEFAULT_PARAMS = dict(a=1.0, c=0.0, budget_min=16.0, budget_max=2048.0, decay=0.5,
                       radius_override=-1.0, levels_per_nat=8, pool_h=16, pool_w=16,
-                      tile_h=8, tile_w=8, generator=0, vote_threshold=1, block_mask=0)
+                      tile_h=8, tile_w=8, generator=0, vote_threshold=1, block_mask=0, regroup=0)
 GENERATORS = {"entropy_disk": 0, "manhattan": 1, "radial": 2, "window_1d": 3}
 _DTYPES = {torch.bfloat16: 1, torch.float32: 0}
 
@@ -263,6 +264,20 @@ class Plan:
                                           glen.ctypes.data_as(_P), gl.ctypes.data_as(_P), _stream(self.device)),
                "tra_plan_export_groups")
         return gptr, glen, gl[:ne.value]
+
+    def export_regroup(self):
+        """Plans created with regroup=1: each group's query slots (row * 16 +
+        column inside the group) in the order the attention kernel deals them
+        to its waves, as a numpy uint8 array [n_groups, 256]."""
+        import numpy as np
+        lib = load_library()
+        ng, ne = ctypes.c_int64(), ctypes.c_int64()
+        _check(lib.tra_plan_export_groups(self.handle, ctypes.byref(ng), ctypes.byref(ne), None, None, None,
+                                          _stream(self.device)), "tra_plan_export_groups")
+        perm = np.zeros((ng.value, 256), dtype=np.uint8)
+        _check(lib.tra_plan_export_regroup(self.handle, perm.ctypes.data_as(_P), _stream(self.device)),
+               "tra_plan_export_regroup")
+        return perm
 
     def stats(self):
         """(retained pairs, listed pairs): exact counts over the whole plan."""

@@ -168,6 +168,13 @@ tra_status check_params(const tra_shape* s, const tra_params* p, Table* tab) {
   if (p->vote_threshold < 1 || p->vote_threshold > p->tile_h * p->tile_w * p->tile_h * p->tile_w)
     return fail(TRA_ERR_INVALID_ARG, "vote_threshold must lie in [1, (tile_h*tile_w)^2]");
   if (p->block_mask != 0 && p->block_mask != 1) return fail(TRA_ERR_INVALID_ARG, "block_mask must be 0 or 1");
+  if (p->regroup != 0 && p->regroup != 1) return fail(TRA_ERR_INVALID_ARG, "regroup must be 0 or 1");
+  if (p->regroup && s->dtype != TRA_BF16)
+    return fail(TRA_ERR_INVALID_ARG, "regroup is a layout of the bf16 attention kernel (dtype TRA_BF16)");
+  // Block-only masks and vote-filtered lists are defined per query tile; a
+  // regrouped wave holds queries of all four tiles of its group.
+  if (p->regroup && (p->block_mask || p->vote_threshold > 1))
+    return fail(TRA_ERR_INVALID_ARG, "regroup takes the exact mask with vote_threshold 1");
   if ((p->generator == TRA_GEN_MANHATTAN || p->generator == TRA_GEN_RADIAL) && !(p->radius_override >= 0.0))
     return fail(TRA_ERR_INVALID_ARG, "the Manhattan and Radial generators take their radius from radius_override (>= 0)");
   const int T = s->T;
@@ -302,6 +309,7 @@ struct tra_plan {
   int32_t* glen = nullptr;   // per group: list length
   int32_t* gptr = nullptr;   // per group: list offset (exclusive scan of glen)
   int64_t n_groups = 0;
+  uint8_t* perm = nullptr;   // regroup: per group, its query slots in level order (GROUP_SLOTS each)
   int64_t* totals = nullptr;      // device: nnz, longest row, overflow flag (+4: groups, +8: filtered CSR)
   // vote threshold > 1: per-entry votes of the unfiltered CSR, the filtered CSR's
   // second buffers (swapped in after filtering) and the retained-pair count
@@ -342,7 +350,7 @@ void release(tra_plan* p) {
   if (!p) return;
   void* bufs[] = {p->kbar, p->H, p->lv, p->r2, p->dmax, p->r2c, p->r2off, p->pool_w,
                   p->counts, p->row_ptr, p->col_idx, p->runs, p->rowwin, p->glist, p->glen, p->gptr, p->totals, p->votes,
-                  p->row_ptr2, p->col_idx2, p->kept_votes, p->counters, p->kbar2, p->lv2};
+                  p->row_ptr2, p->col_idx2, p->kept_votes, p->counters, p->kbar2, p->lv2, p->perm};
   for (void* b : bufs)
     if (b) (void)hipFree(b);
   if (p->totals_host) (void)hipHostFree(p->totals_host);
@@ -445,6 +453,7 @@ tra_status ensure_csr(tra_plan* p, hipStream_t st) {
 // Tile lists (CSR, votes, group lists) from the levels in p->lv.
 tra_status build_lists(tra_plan* p, hipStream_t st) {
   Range r_lists("tra.plan.tile_lists");
+  if (p->perm) TRA_LAUNCH(tra::launch_regroup(p->lv, p->BH, p->tiles, p->perm, st));
   if (p->lazy_csr) return build_group_lists_only(p, st);
   const tra_shape& s = p->shape;
   const bool window = p->params.generator == TRA_GEN_WINDOW_1D;
@@ -623,6 +632,7 @@ tra_status create_plan(const tra_shape* shape, const tra_params* params, Table&&
   if (shape->dtype == TRA_BF16) {
     p->n_groups = tra::group_count(p->BH, p->tiles);
     TRA_HIP_P(dev_alloc(&p->glen, p->n_groups * sizeof(int32_t)));
+    if (params->regroup) TRA_HIP_P(dev_alloc(&p->perm, p->n_groups * tra::GROUP_SLOTS));
     TRA_HIP_P(dev_alloc(&p->gptr, (p->n_groups + 1) * sizeof(int32_t)));
     // A group's list holds at most every key tile of the frames within the
     // table's reach of its own frame.
@@ -886,7 +896,7 @@ tra_status tra_attention(const tra_plan* plan, const void* q, const void* k, con
   const tra::RadiusTable tab = radius_table_of(plan);
   TRA_LAUNCH(tra::launch_attention(s.dtype, s.head_dim, q, k, v, o, plan->lv, tab, plan->row_base,
                                 plan->BH, plan->tiles, plan->row_ptr, plan->col_idx,
-                                plan->gptr, plan->glist, plan->glen, plan->params.block_mask != 0,
+                                plan->gptr, plan->glist, plan->glen, plan->perm, plan->params.block_mask != 0,
                                 plan->params.vote_threshold == 1, static_cast<hipStream_t>(stream)));
   return TRA_OK;
 }
@@ -954,6 +964,16 @@ tra_status tra_plan_export(const tra_plan* plan, int16_t* levels, float* entropy
         std::memcpy(static_cast<char*>(kbar) + (static_cast<size_t>(bh) * plan->pool.count + b) * row,
                     &tmp[(static_cast<size_t>(bh) * plan->pool.count + tra::pool_pos(plan->pool, b)) * row], row);
   }
+  return TRA_OK;
+}
+
+tra_status tra_plan_export_regroup(const tra_plan* plan, uint8_t* perm, void* stream) {
+  if (!plan || !perm) return fail(TRA_ERR_INVALID_ARG, "plan or perm is NULL");
+  if (!plan->valid) return fail(TRA_ERR_PLAN_INVALID, "the plan's last build failed");
+  if (!plan->perm) return fail(TRA_ERR_INVALID_ARG, "the plan was created without regroup");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  TRA_HIP(hipMemcpyAsync(perm, plan->perm, plan->n_groups * tra::GROUP_SLOTS, hipMemcpyDeviceToHost, hs));
+  TRA_HIP(hipStreamSynchronize(hs));
   return TRA_OK;
 }
 

@@ -90,11 +90,14 @@ hipError_t launch_scan(const int32_t* counts, int64_t n_rows, int32_t* row_ptr,
 hipError_t launch_csr_expand(int BH, const Grid& tiles, int DM, const int32_t* runs,
                              const int32_t* rowwin, const int32_t* row_ptr, int32_t* col_idx,
                              hipStream_t s);
+// perm (bf16, may be null): per group, the order in which its queries are
+// dealt to the waves (see launch_regroup); null deals the spatial half tiles.
 hipError_t launch_attention(int dtype, int d, const void* q, const void* k, const void* v,
                             void* o, const int16_t* lv, const RadiusTable& tab, int row_base,
                             int BH, const Grid& tiles, const int32_t* row_ptr,
                             const int32_t* col_idx, const int32_t* gptr, const int32_t* glist,
-                            const int32_t* glen, bool block_mask, bool self_ref, hipStream_t s);
+                            const int32_t* glen, const uint8_t* perm, bool block_mask, bool self_ref,
+                            hipStream_t s);
 // Work unit of the bf16 attention kernel: a group of GROUP_ROWS x 2 query
 // tiles of one frame, run by one workgroup of ATTN_THREADS threads (two waves
 // per query tile).
@@ -106,6 +109,12 @@ constexpr int ATTN_THREADS = 256 * GROUP_ROWS;
 inline int64_t group_count(int BH, const Grid& tiles) {
   return static_cast<int64_t>(BH) * tiles.T * ((tiles.nh + GROUP_ROWS - 1) / GROUP_ROWS) * ((tiles.nw + 1) / 2);
 }
+// Query regrouping: a group covers 8*GROUP_ROWS x 16 query positions (slot s
+// = row * 16 + column within the group); perm + GROUP_SLOTS * group lists
+// them sorted by (level, slot), positions outside the grid last.  Wave w of
+// the attention kernel takes entries 32w .. 32w + 31.
+constexpr int GROUP_SLOTS = 128 * GROUP_ROWS;
+hipError_t launch_regroup(const int16_t* lv, int BH, const Grid& tiles, uint8_t* perm, hipStream_t s);
 // Merged tile lists of the groups, from the runs: with fill = false the length
 // of each group's list to glen; with fill = true the entries (two int32 each)
 // at glist + 2 * gptr[group] (gptr: exclusive scan of the lengths).  The sum

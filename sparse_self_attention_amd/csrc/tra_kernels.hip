@@ -850,6 +850,42 @@ __global__ __launch_bounds__(256) void window_csr_kernel(const int16_t* __restri
   if (!FILL && lane == 0) counts[row] = out;
 }
 
+// Query regrouping by level: one workgroup of GROUP_SLOTS threads per group
+// of query tiles sorts the keys (level << 8 | slot) of the group's positions
+// (slot = row * 16 + column inside the group; positions outside the grid get
+// the largest level) with a bitonic network in LDS and stores the sorted
+// slots.  The keys are distinct, so the order is deterministic.
+__global__ __launch_bounds__(GROUP_SLOTS) void regroup_kernel(const int16_t* __restrict__ lv, Grid g, int ngh,
+                                                             int ngw, uint8_t* __restrict__ perm) {
+  __shared__ uint32_t key[GROUP_SLOTS];
+  const int64_t gid = blockIdx.x;
+  const int per_head = g.T * ngh * ngw;
+  const int bh = static_cast<int>(gid / per_head), grem = static_cast<int>(gid % per_head);
+  const int tq = grem / (ngh * ngw), gr = (grem % (ngh * ngw)) / ngw, gc = grem % ngw;
+  const int s = threadIdx.x;
+  const int hq = gr * 8 * GROUP_ROWS + (s >> 4), wq = gc * 16 + (s & 15);
+  const size_t N = static_cast<size_t>(g.T) * g.H * g.W;
+  const uint32_t level = (hq < g.H && wq < g.W)
+                             ? static_cast<uint32_t>(lv[static_cast<size_t>(bh) * N + (static_cast<size_t>(tq) * g.H + hq) * g.W + wq] + 32768)
+                             : 0xffffu;
+  key[s] = (level << 8) | static_cast<uint32_t>(s);
+  __syncthreads();
+  for (int kk = 2; kk <= GROUP_SLOTS; kk <<= 1) {
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      const int p = s ^ j;
+      if (p > s) {
+        const uint32_t a = key[s], b = key[p];
+        if ((a > b) == ((s & kk) == 0)) {
+          key[s] = b;
+          key[p] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  perm[gid * GROUP_SLOTS + s] = static_cast<uint8_t>(key[s] & 0xffu);
+}
+
 // Group lists (GROUP_ROWS x 2 query tiles, the entries and membership bits of
 // group_list_kernel).  One wave per group.
 template <bool FILL>
@@ -1010,7 +1046,7 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
     const int32_t* __restrict__ r2c, const int32_t* __restrict__ r2off,
     const int32_t* __restrict__ dmax, int n_r2c, int row_base, Grid g, int ngh, int ngw, int n_groups,
     const int32_t* __restrict__ gptr, const int2* __restrict__ glist,
-    const int32_t* __restrict__ glen, int self_ref) {
+    const int32_t* __restrict__ glen, const uint8_t* __restrict__ perm, int self_ref) {
   using L = AttnLds<D>;
   constexpr int NWAVES = ATTN_THREADS / 64;
   constexpr int KS = D / 16;  // k-steps of S^T
@@ -1046,15 +1082,27 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
   // a SIMD; they take tiles of different rows and columns, so that a key tile
   // listed by one row or one column of the group keeps every SIMD busy.
   const int wcol = ((wave >> 1) ^ (wave >> 2)) & 1;
-  const int tc = gc * 2 + wcol;
-  const int trq = gr * GROUP_ROWS + (wave >> 2);
-  const bool tvalid = tc < g.nw && trq < g.nh;
-  const int wq = tc * 8 + (col & 7);
-  const int hq = trq * 8 + 4 * (wave & 1) + (col >> 3);
-  // This wave's query tile in the group's membership bits (see group_list_kernel).
-  const int mbit = 1 << (2 * (wave >> 2) + wcol);
+  int hq, wq, mbit;
+  bool qvalid;
+  if (perm) {
+    // Regrouped: the wave's queries are entries 32*wave .. +31 of the
+    // group's level order, anywhere in the group's 8*GROUP_ROWS x 16
+    // positions, so every tile the group lists may hold keys for them.
+    const int slot = perm[static_cast<size_t>(gid) * GROUP_SLOTS + 32 * wave + col];
+    hq = gr * 8 * GROUP_ROWS + (slot >> 4);
+    wq = gc * 16 + (slot & 15);
+    mbit = 0xf;
+    qvalid = hq < g.H && wq < g.W;
+  } else {
+    const int tc = gc * 2 + wcol;
+    const int trq = gr * GROUP_ROWS + (wave >> 2);
+    wq = tc * 8 + (col & 7);
+    hq = trq * 8 + 4 * (wave & 1) + (col >> 3);
+    // This wave's query tile in the group's membership bits (see group_list_kernel).
+    mbit = 1 << (2 * (wave >> 2) + wcol);
+    qvalid = tc < g.nw && trq < g.nh && hq < g.H && wq < g.W;
+  }
   [[maybe_unused]] const int nqh = (tq * g.H + hq) * g.W + wq;  // raster index (1-D window mask)
-  const bool qvalid = tvalid && hq < g.H && wq < g.W;
   const size_t nq = (static_cast<size_t>(tq) * g.H + (qvalid ? hq : 0)) * g.W + (qvalid ? wq : 0);
   bf16x8 qf[KS];
   {
@@ -1780,11 +1828,21 @@ hipError_t launch_vote_compact(int64_t n_rows, const int32_t* row_ptr, const int
   return hipGetLastError();
 }
 
+hipError_t launch_regroup(const int16_t* lv, int BH, const Grid& tiles, uint8_t* perm, hipStream_t s) {
+  static_assert(GROUP_SLOTS == 32 * (ATTN_THREADS / 64), "one slot per query lane of the attention workgroup");
+  static_assert(8 * GROUP_ROWS <= 16, "slots hold 4-bit rows");
+  const int ngh = (tiles.nh + GROUP_ROWS - 1) / GROUP_ROWS, ngw = (tiles.nw + 1) / 2;
+  const int64_t groups = group_count(BH, tiles);
+  regroup_kernel<<<static_cast<unsigned>(groups), GROUP_SLOTS, 0, s>>>(lv, tiles, ngh, ngw, perm);
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(int dtype, int d, const void* q, const void* k, const void* v,
                             void* o, const int16_t* lv, const RadiusTable& tab, int row_base,
                             int BH, const Grid& tiles, const int32_t* row_ptr,
                             const int32_t* col_idx, const int32_t* gptr, const int32_t* glist,
-                            const int32_t* glen, bool block_mask, bool self_ref, hipStream_t s) {
+                            const int32_t* glen, const uint8_t* perm, bool block_mask, bool self_ref,
+                            hipStream_t s) {
   const int32_t* r2 = tab.r2;
   const unsigned rows = static_cast<unsigned>(BH) * tiles.count;
   if (dtype == 1) {
@@ -1800,7 +1858,7 @@ hipError_t launch_attention(int dtype, int d, const void* q, const void* k, cons
 #define TRA_ATTN(DD, M, B)                                                                                 \
   attn_bf16_kernel<DD, M, B><<<grid, ATTN_THREADS, lds_tab, s>>>(qq, kk, vv, oo, lv, tab.r2c, tab.r2off, tab.dmax, \
                                                                  tab.n_r2c, row_base, tiles, ngh, ngw, ng, gptr,     \
-                                                                 reinterpret_cast<const int2*>(glist), glen,         \
+                                                                 reinterpret_cast<const int2*>(glist), glen, perm,   \
                                                                  self_ref ? 1 : 0)
     if (block_mask) {
       if (d == 128) TRA_ATTN(128, METRIC_L2, true);

@@ -181,3 +181,41 @@ def check_group_lists(cfg, run, bh):
         got = gl[gptr[gid]:gptr[gid] + glen[gid]].astype(np.int64)
         assert np.array_equal(got, ent), f"group {gid}: {got[:6].tolist()} vs {ent[:6].tolist()}"
     return len(want)
+
+
+def _onehot_values(N, perm, gpu):
+    j = perm if perm is not None else np.arange(N)
+    v = torch.zeros((N, 128), dtype=torch.float32)
+    v[np.arange(N), torch.from_numpy(j % 64)] = 1.0
+    v[np.arange(N), torch.from_numpy(64 + j // 64)] = 1.0
+    return v.to(torch.bfloat16).reshape(1, 1, N, 128).to(gpu)
+
+
+def check_key_sets(cfg, plan, lv, gpu, seed):
+    """Every query's retained key set, recovered exactly from O (Q = 0, so each
+    retained key weighs the same, and V one-hot encodes the key index; see the
+    exact key-set tests in test_gpu_parity.py), against the oracle's
+    brute-force mask for the levels lv.  Returns (largest set, worst distance
+    of a scaled entry from its integer count)."""
+    p = cfg.params()
+    N = cfg.N
+    assert N <= 64 * 64
+    R2 = O.radius_table(p, cfg.T)
+    mask = O.dense_mask(lv, R2, cfg.T, cfg.H, cfg.W, p)  # oracle's brute-force N x N mask
+    size = mask.sum(axis=1).astype(np.float64)
+    q = torch.zeros((1, 1, N, 128), dtype=torch.bfloat16, device=gpu)
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    k = torch.randn((1, 1, N, 128), generator=g).to(torch.bfloat16).to(gpu)
+    perm = np.random.default_rng(seed).permutation(N)
+    worst = 0.0
+    for enc in (None, perm):
+        v = _onehot_values(N, enc, gpu)
+        o = tra.attention(q, k, v, plan)
+        torch.cuda.synchronize()
+        scaled = o[0, 0].double().cpu().numpy() * size[:, None]
+        got = np.rint(scaled).astype(np.int64)
+        want = np.rint(mask.astype(np.float64) @ v[0, 0].double().cpu().numpy()).astype(np.int64)
+        bad = np.nonzero(np.any(got != want, axis=1))[0]
+        assert len(bad) == 0, f"{len(bad)} queries with a different key set, first {bad[:8].tolist()}"
+        worst = max(worst, float(np.abs(scaled - got).max()))
+    return int(size.max()), worst

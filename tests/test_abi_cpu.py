@@ -74,6 +74,10 @@ def _validate(**kw):
     (dict(generator=3, vote_threshold=2), "TRA_ERR_INVALID_ARG"),
     (dict(generator=1), "TRA_ERR_INVALID_ARG"),  # the static generators need radius_override >= 0
     (dict(generator=2, radius_override=-1.0), "TRA_ERR_INVALID_ARG"),
+    (dict(regroup=2), "TRA_ERR_INVALID_ARG"),
+    (dict(regroup=1, dtype=torch.float32), "TRA_ERR_INVALID_ARG"),  # a layout of the bf16 kernel
+    (dict(regroup=1, block_mask=1), "TRA_ERR_INVALID_ARG"),  # block masks are per query tile
+    (dict(regroup=1, vote_threshold=4), "TRA_ERR_INVALID_ARG"),  # so are vote-filtered lists
     # every frame active (decay 1) over 2,000 frames at 88 levels: the radius
     # table's active entries (88 x 2,000) exceed what the tile-list kernel stages
     (dict(grid=(2000, 4, 4), heads=1, dtype=torch.float32, decay=1.0, budget_max=float(2 ** 20)),
@@ -83,6 +87,11 @@ def test_validation_rejects(kw, code):
     with pytest.raises(tra.TraError) as ei:
         _validate(**kw)
     assert ei.value.name == code
+
+
+def test_validation_accepts_regroup():
+    _validate(regroup=1)
+    _validate(regroup=1, generator=3)
 
 
 def test_validation_accepts_large_fp32_head():

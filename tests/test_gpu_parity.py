@@ -12,7 +12,7 @@ from workloads import CONFIGS, make_inputs, perturb, small_workload
 from oracle import runner
 
 import ref_tiles
-from parity_util import check_csr_properties, check_group_lists, check_head, check_levels, gpu_run
+from parity_util import check_csr_properties, check_group_lists, check_head, check_key_sets, check_levels, gpu_run
 
 pytestmark = pytest.mark.gpu
 
@@ -357,39 +357,6 @@ def test_vote_threshold_full_size_sampled(gpu, theta, block):
 # so that two different key sets with equal histograms under one encoding are
 # told apart by the other.
 # ---------------------------------------------------------------------------
-def _onehot_values(N, perm, gpu):
-    j = perm if perm is not None else np.arange(N)
-    v = torch.zeros((N, 128), dtype=torch.float32)
-    v[np.arange(N), torch.from_numpy(j % 64)] = 1.0
-    v[np.arange(N), torch.from_numpy(64 + j // 64)] = 1.0
-    return v.to(torch.bfloat16).reshape(1, 1, N, 128).to(gpu)
-
-
-def _check_key_sets(cfg, plan, lv, gpu, seed):
-    p = cfg.params()
-    N = cfg.N
-    assert N <= 64 * 64
-    R2 = O.radius_table(p, cfg.T)
-    mask = O.dense_mask(lv, R2, cfg.T, cfg.H, cfg.W, p)  # oracle's brute-force N x N mask
-    size = mask.sum(axis=1).astype(np.float64)
-    q = torch.zeros((1, 1, N, 128), dtype=torch.bfloat16, device=gpu)
-    g = torch.Generator(device="cpu").manual_seed(seed)
-    k = torch.randn((1, 1, N, 128), generator=g).to(torch.bfloat16).to(gpu)
-    perm = np.random.default_rng(seed).permutation(N)
-    worst = 0.0
-    for enc in (None, perm):
-        v = _onehot_values(N, enc, gpu)
-        o = tra.attention(q, k, v, plan)
-        torch.cuda.synchronize()
-        scaled = o[0, 0].double().cpu().numpy() * size[:, None]
-        got = np.rint(scaled).astype(np.int64)
-        want = np.rint(mask.astype(np.float64) @ v[0, 0].double().cpu().numpy()).astype(np.int64)
-        bad = np.nonzero(np.any(got != want, axis=1))[0]
-        assert len(bad) == 0, f"{len(bad)} queries with a different key set, first {bad[:8].tolist()}"
-        worst = max(worst, float(np.abs(scaled - got).max()))
-    return int(size.max()), worst
-
-
 KEYSET_CASES = [
     # (T, H, W, generator, radius): static radii up to production size (the
     # 30 x 45 frame is ragged in both directions: 4 x 6 tiles, the last of each
@@ -410,7 +377,7 @@ def test_key_sets_exact(gpu, case):
     q = torch.zeros((1, 1, cfg.N, 128), dtype=torch.bfloat16, device=gpu)
     plan = tra.plan(q, q, grid=(T, H, W), **cfg.params())
     lv = np.full(cfg.N, -1, dtype=np.int64)
-    largest, worst = _check_key_sets(cfg, plan, lv, gpu, seed=5)
+    largest, worst = check_key_sets(cfg, plan, lv, gpu, seed=5)
     _say("largest key set", largest, "worst distance from an integer count", worst)
 
 
@@ -433,5 +400,5 @@ def test_key_sets_exact_mixed_levels(gpu, T, H, W, gen):
     assert np.array_equal(lv, O.levels(Hq.astype(np.float64), p))
     k_lo, k_hi = O.level_range(p)
     assert len(np.unique(lv)) > (k_hi - k_lo) // 2  # many distinct levels
-    largest, worst = _check_key_sets(cfg, plan, lv, gpu, seed=9)
+    largest, worst = check_key_sets(cfg, plan, lv, gpu, seed=9)
     _say("levels", k_lo, "..", k_hi, "largest key set", largest, "worst distance from an integer count", worst)

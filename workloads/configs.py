@@ -46,6 +46,7 @@ class Workload:
     #                     3: 1-D window along the raster order (ablation)
     vote_threshold: int = 1  # key tile listed when >= this many pairs are retained
     block_mask: int = 0  # 1: block-only mask (every key of a listed tile)
+    regroup: int = 0  # 1: the attention kernel deals each group's queries to its waves in level order
     seed: int = 0
     batch: int = 1
     reuse_calls: int = 1  # attention calls that reuse one plan
@@ -62,7 +63,7 @@ class Workload:
         """Method parameters (what the planning call receives)."""
         keys = ("a", "c", "budget_min", "budget_max", "decay", "levels_per_nat",
                 "pool_h", "pool_w", "tile_h", "tile_w", "radius_override", "generator",
-                "vote_threshold", "block_mask")
+                "vote_threshold", "block_mask", "regroup")
         d = asdict(self)
         return {k: d[k] for k in keys}
 
