@@ -104,6 +104,31 @@ def _check_order(cfg, plan):
                     g += 1
 
 
+def test_regroup_follows_rebuild_and_import(gpu):
+    """A rebuild on other inputs re-sorts every group; an imported plan holds
+    the same order and attends bit for bit like the exported one."""
+    from workloads import make_inputs, perturb
+    cfg = small_workload(T=3, H=30, W=45, heads=2, c=-0.5, budget_max=4050.0, regroup=1)
+    _say("case: regroup rebuild and import")
+    q, k, v = make_inputs(cfg, device=gpu)
+    grid = (cfg.T, cfg.H, cfg.W)
+    plan = tra.plan(q, k, grid=grid, **cfg.params())
+    first = plan.export_regroup()
+    q2, k2 = perturb(q, 2, 0, rel=0.5), perturb(k, 2, 1, rel=0.5)
+    plan.rebuild(q2, k2)
+    _check_order(cfg, plan)
+    fresh = tra.plan(q2, k2, grid=grid, **cfg.params())
+    assert np.array_equal(plan.export_regroup(), fresh.export_regroup())
+    saved = plan.export()
+    back = tra.import_plan(saved, 1, cfg.heads, grid, cfg.head_dim, device=gpu, **cfg.params())
+    assert np.array_equal(back.export_regroup(), plan.export_regroup())
+    o1, o2 = tra.attention(q2, k2, v, plan), tra.attention(q2, k2, v, back)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    _say("groups re-sorted by the rebuild:", int(np.sum(np.any(first != plan.export_regroup(), axis=1))),
+         "of", len(first))
+
+
 def test_regroup_rejected_with_block_masks(gpu):
     cfg = small_workload(T=3, H=13, W=21, heads=1, regroup=1, block_mask=1)
     q = torch.zeros((1, 1, cfg.N, 128), dtype=torch.bfloat16, device=gpu)
