@@ -59,6 +59,11 @@ int main(void) {
   bp = p;
   bp.generator = 7;
   EXPECT(tra_params_validate(&wan, &bp) == TRA_ERR_INVALID_ARG);
+  bp = p;
+  bp.regroup = 1;
+  EXPECT(tra_params_validate(&wan, &bp) == TRA_OK);
+  bp.block_mask = 1; /* block masks are per query tile */
+  EXPECT(tra_params_validate(&wan, &bp) == TRA_ERR_INVALID_ARG);
   EXPECT(strlen(tra_last_error()) > 0);
 
   /* radius tables: size query, then the table */
@@ -94,6 +99,7 @@ int main(void) {
   EXPECT(tra_plan_drift(NULL, fake, fake, &a, NULL) == TRA_ERR_INVALID_ARG);
   EXPECT(tra_plan_drift_noalloc(NULL, fake, fake, &a, NULL) == TRA_ERR_INVALID_ARG);
   EXPECT(tra_plan_export(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL) == TRA_ERR_INVALID_ARG);
+  EXPECT(tra_plan_export_regroup(NULL, NULL, NULL) == TRA_ERR_INVALID_ARG);
   EXPECT(tra_plan_rebuild(NULL, fake, fake, NULL) == TRA_ERR_INVALID_ARG);
   EXPECT(tra_dense_attention(&wan, fake, fake, fake, fake, NULL, NULL) == TRA_ERR_INVALID_ARG); /* o aliases q */
   EXPECT(tra_dense_attention(&wan, (void*)(uintptr_t)4100, fake, fake, (void*)(uintptr_t)8192, NULL, NULL) ==
