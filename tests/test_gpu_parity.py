@@ -54,6 +54,18 @@ def test_small_fp32_d128_parity(gpu):
     assert m["o_max_abs"] < 1e-4
 
 
+@pytest.mark.parametrize("kw", [dict(generator=1, radius_override=5.0), dict(generator=2, radius_override=6.0),
+                                dict(generator=3, c=-2.0, budget_max=300.0)])
+def test_small_fp32_d128_generators(gpu, kw):
+    """The fp32 kernel at d = 128 (four waves per query tile) with the
+    Manhattan, Radial and 1-D window masks: every output against the oracle."""
+    cfg = small_workload(T=3, H=11, W=19, heads=1, head_dim=128, dtype="fp32", **kw)
+    _say("case: small fp32 d128", kw)
+    run = gpu_run(cfg, gpu)
+    m = check_head(cfg, run, 0, 0)
+    assert m["o_max_abs"] < 1e-4
+
+
 def test_batch_of_two(gpu):
     cfg = small_workload(T=2, H=9, W=12, heads=2, batch=2, c=-0.25, budget_max=216.0)
     _say("case: batch 2")
@@ -301,12 +313,14 @@ def _check_listed(cfg, run, h, block_only, tile_sample=None, query_sample=None):
 MAX_ABS_, MEAN_ABS_ = 2e-2, 2e-3
 
 
-@pytest.mark.parametrize("theta,block,dtype", [(4, 0, "bf16"), (40, 0, "bf16"), (1, 1, "bf16"), (8, 1, "bf16"),
-                                               (300, 1, "bf16"), (6, 0, "fp32"), (1, 1, "fp32"), (20, 1, "fp32")])
-def test_vote_threshold_and_block_mask_small(gpu, theta, block, dtype):
+@pytest.mark.parametrize("theta,block,dtype,d", [(4, 0, "bf16", 128), (40, 0, "bf16", 128), (1, 1, "bf16", 128),
+                                                 (8, 1, "bf16", 128), (300, 1, "bf16", 128), (6, 0, "fp32", 64),
+                                                 (1, 1, "fp32", 64), (20, 1, "fp32", 64), (6, 0, "fp32", 128),
+                                                 (20, 1, "fp32", 128)])
+def test_vote_threshold_and_block_mask_small(gpu, theta, block, dtype, d):
     cfg = small_workload(T=3, H=13, W=21, heads=2, c=-0.5, budget_max=819.0, vote_threshold=theta,
-                         block_mask=block, dtype=dtype, head_dim=128 if dtype == "bf16" else 64)
-    _say("case: votes", theta, "block", block, dtype)
+                         block_mask=block, dtype=dtype, head_dim=d)
+    _say("case: votes", theta, "block", block, dtype, "d", d)
     run = gpu_run(cfg, gpu)
     for h in range(cfg.heads):
         err = _check_listed(cfg, run, h, bool(block))
