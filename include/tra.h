@@ -209,6 +209,11 @@ tra_status tra_radius_table(const tra_shape* shape, const tra_params* params, in
  * runs on first use by tra_plan_export (row_ptr / col_idx), tra_plan_stats
  * or tra_plan_get_info, which then synchronise.  Other plans (fp32, vote
  * threshold) build the CSR at once and synchronise `stream` once to size it.
+ * The calls that copy plan data to the host (tra_plan_export,
+ * tra_plan_export_groups, tra_plan_export_regroup, tra_plan_stats,
+ * tra_plan_get_info) order themselves after the plan's latest build, on
+ * whatever stream it ran; the kernel-launching calls (tra_attention,
+ * tra_plan_drift) follow their own stream's order only.
  * An asynchronous rebuild and the attention calls that follow it can be
  * captured in a HIP graph (they launch kernels and record one event, nothing
  * else).  The plan's host-side state (its validity, whether its CSR is

@@ -341,7 +341,7 @@ struct tra_plan {
   bool lazy_csr = false;
   bool csr_ready = false;
   int64_t glist_stride = 0;  // lazy-CSR plans: group g's list starts at entry g * glist_stride
-  hipEvent_t built = nullptr;  // recorded at the end of each lazy build
+  hipEvent_t built = nullptr;  // recorded at the end of each build
 };
 
 namespace {
@@ -547,6 +547,7 @@ tra_status build_lists(tra_plan* p, hipStream_t st) {
                                       p->glist, p->glen, st));
     }
   }
+  TRA_HIP(hipEventRecord(p->built, st));  // the host-copy calls wait for it
   return TRA_OK;
 }
 
@@ -647,9 +648,11 @@ tra_status create_plan(const tra_shape* shape, const tra_params* params, Table&&
       std::vector<int32_t> slots(p->n_groups + 1);
       for (int64_t g = 0; g <= p->n_groups; ++g) slots[g] = static_cast<int32_t>(g * per_group);
       TRA_HIP_P(hipMemcpy(p->gptr, slots.data(), slots.size() * sizeof(int32_t), hipMemcpyHostToDevice));
-      TRA_HIP_P(hipEventCreateWithFlags(&p->built, hipEventDisableTiming));
     }
   }
+  // Recorded at the end of every build; the calls that copy plan data to the
+  // host wait for it on their own stream.
+  TRA_HIP_P(hipEventCreateWithFlags(&p->built, hipEventDisableTiming));
   TRA_HIP_P(host_alloc(&p->totals_host, 8 * sizeof(int64_t)));
   TRA_HIP_P(dev_alloc(&p->counters, 4 * sizeof(unsigned long long)));
   if (params->radius_override < 0.0) {
@@ -947,6 +950,8 @@ tra_status tra_plan_export(const tra_plan* plan, int16_t* levels, float* entropy
     const tra_status st = ensure_csr(const_cast<tra_plan*>(plan), hs);
     if (st != TRA_OK) return st;
   }
+  // An asynchronous build may still run on another stream.
+  if (plan->built) TRA_HIP(hipStreamWaitEvent(hs, plan->built, 0));
   TRA_HIP(hipStreamSynchronize(hs));
   if (levels) TRA_HIP(hipMemcpy(levels, plan->lv, plan->n_queries * sizeof(int16_t), hipMemcpyDeviceToHost));
   if (entropy) TRA_HIP(hipMemcpy(entropy, plan->H, plan->n_queries * sizeof(float), hipMemcpyDeviceToHost));
@@ -972,6 +977,8 @@ tra_status tra_plan_export_regroup(const tra_plan* plan, uint8_t* perm, void* st
   if (!plan->valid) return fail(TRA_ERR_PLAN_INVALID, "the plan's last build failed");
   if (!plan->perm) return fail(TRA_ERR_INVALID_ARG, "the plan was created without regroup");
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  // An asynchronous build may still run on another stream.
+  if (plan->built) TRA_HIP(hipStreamWaitEvent(hs, plan->built, 0));
   TRA_HIP(hipMemcpyAsync(perm, plan->perm, plan->n_groups * tra::GROUP_SLOTS, hipMemcpyDeviceToHost, hs));
   TRA_HIP(hipStreamSynchronize(hs));
   return TRA_OK;
@@ -983,6 +990,8 @@ tra_status tra_plan_export_groups(const tra_plan* plan, int64_t* n_groups, int64
   if (!plan->valid) return fail(TRA_ERR_PLAN_INVALID, "the plan's last build failed");
   if (plan->shape.dtype != TRA_BF16) return fail(TRA_ERR_DTYPE, "group lists exist for bf16 plans only");
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  // An asynchronous build may still run on another stream.
+  if (plan->built) TRA_HIP(hipStreamWaitEvent(hs, plan->built, 0));
   TRA_HIP(hipStreamSynchronize(hs));
   if (plan->glist_stride > 0) {
     // Lists in fixed per-group slots: returned packed, in group order.
@@ -1034,6 +1043,7 @@ tra_status tra_plan_stats(const tra_plan* plan, int64_t* retained, int64_t* list
   tra_plan* p = const_cast<tra_plan*>(plan);
   const tra_status cs = ensure_csr(p, hs);
   if (cs != TRA_OK) return cs;
+  TRA_HIP(hipStreamWaitEvent(hs, p->built, 0));  // the latest build, on whatever stream it ran
   TRA_LAUNCH(tra::launch_clear_counters(p->counters, 2, hs));
   TRA_LAUNCH(tra::launch_stats(metric_of(plan->params), plan->lv, plan->r2, plan->shape.T, plan->row_base, plan->BH,
                                plan->tiles, plan->row_ptr, plan->col_idx, p->counters, hs));

@@ -49,6 +49,7 @@ def test_csr_completed_on_another_stream(gpu):
     ref = tra.plan(q, k, grid=grid, **cfg.params())
     want = _csr(ref)
     side = torch.cuda.Stream(device=gpu)  # default priority
+    side.wait_stream(torch.cuda.current_stream(gpu))  # the inputs are written on the default stream
     with torch.cuda.stream(side):
         plan = tra.plan(q, k, grid=grid, **cfg.params())
         q2 = perturb(q, 3, 0, rel=0.5)
@@ -104,3 +105,37 @@ def test_reuse_step_in_a_graph(gpu):
         e = plan.export()  # the CSR completed after a replay is the replayed build's
         ref = tra.plan(q, k, grid=grid, **cfg.params()).export()
         assert np.array_equal(e["col_idx"], ref["col_idx"]) and np.array_equal(e["levels"], ref["levels"])
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(vote_threshold=4), dict(dtype="fp32", head_dim=64), dict(regroup=1)])
+def test_host_copies_follow_a_build_on_another_stream(gpu, kw):
+    """Every call that copies plan data to the host orders itself after the
+    plan's latest build, also when that build ran on another stream and the
+    caller does not synchronise: levels, pooled keys, CSR, group lists, the
+    regroup order and the pair counts equal a plan built from those inputs."""
+    cfg = small_workload(T=3, H=13, W=21, heads=2, **kw)
+    grid = (cfg.T, cfg.H, cfg.W)
+    print("case: host copies after a side-stream build", kw, flush=True)
+    q, k, v = make_inputs(cfg, device=gpu)
+    q2, k2 = perturb(q, 2, 0, rel=0.5), perturb(k, 2, 1, rel=0.5)
+    plan = tra.plan(q, k, grid=grid, **cfg.params())
+    want = tra.plan(q2, k2, grid=grid, **cfg.params())
+    e_want, s_want = want.export(), want.stats()
+    g_want = want.export_groups() if cfg.dtype == "bf16" else None
+    r_want = want.export_regroup() if cfg.regroup else None
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(device=gpu)  # default priority
+    side.wait_stream(torch.cuda.current_stream(gpu))
+    with torch.cuda.stream(side):
+        plan.rebuild(q2, k2)
+    # no synchronisation: each host copy below orders itself after the rebuild
+    if cfg.regroup:
+        assert np.array_equal(tra.Plan.export_regroup(plan), r_want)
+    if g_want is not None:
+        for a, b in zip(tra.Plan.export_groups(plan), g_want):
+            assert np.array_equal(a, b)
+    got = tra.Plan.export(plan)
+    for key in ("levels", "kbar", "row_ptr", "col_idx"):
+        assert np.array_equal(got[key], e_want[key]), key
+    assert tra.Plan.stats(plan) == s_want
+    torch.cuda.synchronize()
