@@ -405,11 +405,10 @@ tra_status build_group_lists_only(tra_plan* p, hipStream_t st) {
     TRA_LAUNCH(tra::launch_window_groups(true, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, p->gptr,
                                       p->glist, p->glen, st));
   } else {
+    // One pass: each workgroup writes the runs of a group's tiles, then the group's list.
     TRA_LAUNCH(tra::launch_csr_runs(p->params.generator == TRA_GEN_MANHATTAN, p->lv, radius_table_of(p),
                                     p->table.n_levels, p->row_base, p->BH, p->tiles, p->DM, p->counts, p->runs,
-                                    p->rowwin, st));
-    TRA_LAUNCH(tra::launch_group_lists(true, p->BH, p->tiles, p->DM, p->runs, p->rowwin, nullptr, nullptr, p->gptr,
-                                    p->glist, p->glen, st));
+                                    p->rowwin, st, p->gptr, p->glist, p->glen));
   }
   TRA_HIP(hipEventRecord(p->built, st));
   return TRA_OK;

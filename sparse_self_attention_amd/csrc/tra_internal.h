@@ -82,9 +82,12 @@ hipError_t launch_fill_levels(int16_t* lv, float* H, int64_t n, hipStream_t s);
 // row) plus the count and the frame window (csr_runs), the scan of the counts,
 // and the expansion of the runs into col_idx.  DM is the largest active frame
 // distance of the radius table; runs holds n_rows * (2*DM + 1) * nh int32.
+// With glist, the groups' lists are filled too (fixed slots at gptr, lengths to
+// glen; see launch_group_lists), in the same pass.
 hipError_t launch_csr_runs(bool l1, const int16_t* lv, const RadiusTable& tab, int n_levels, int row_base,
                            int BH, const Grid& tiles, int DM, int32_t* counts, int32_t* runs, int32_t* rowwin,
-                           hipStream_t s);
+                           hipStream_t s, const int32_t* gptr = nullptr, int32_t* glist = nullptr,
+                           int32_t* glen = nullptr);
 hipError_t launch_scan(const int32_t* counts, int64_t n_rows, int32_t* row_ptr,
                        int64_t* totals, hipStream_t s);
 hipError_t launch_csr_expand(int BH, const Grid& tiles, int DM, const int32_t* runs,

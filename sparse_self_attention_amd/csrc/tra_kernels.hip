@@ -431,7 +431,19 @@ __device__ __forceinline__ int mask_half_width(int thr, int dh) {
 // radius table is staged in LDS (dynamic): per level row its largest active
 // distance and the offset of its active entries in the compact table, then
 // the compact table itself.
-template <bool L1>
+template <bool FILL>
+__device__ __forceinline__ void group_fill(Grid g, int DM, int ngh, int ngw, int64_t gid, int lane,
+                                           const int32_t* __restrict__ runs, const int32_t* __restrict__ rowwin,
+                                           const int32_t* __restrict__ frow_ptr, const int32_t* __restrict__ fcol,
+                                           const int32_t* __restrict__ gptr, int2* __restrict__ glist,
+                                           int32_t* __restrict__ glen);
+
+// GROUPS: a workgroup takes the GROUP_ROWS x 2 query tiles of one group of the
+// bf16 attention kernel (wave m: tile row m / 2, column m % 2 of the group;
+// grid (groups per head, BH)), and once the runs of its tiles are written
+// wave 0 merges them into the group's list at gptr[group] (group_fill), so
+// that no second pass reads the runs back.
+template <bool L1, bool GROUPS>
 __global__ __launch_bounds__(256) void csr_runs_kernel(const int16_t* __restrict__ lv,
                                                       const int32_t* __restrict__ r2c,
                                                       const int32_t* __restrict__ r2off,
@@ -440,7 +452,9 @@ __global__ __launch_bounds__(256) void csr_runs_kernel(const int16_t* __restrict
                                                       int row_base, Grid g, int tw_shift, int DM,
                                                       int32_t* __restrict__ counts,
                                                       int32_t* __restrict__ runs,
-                                                      int32_t* __restrict__ rowwin) {
+                                                      int32_t* __restrict__ rowwin, int ngh, int ngw,
+                                                      const int32_t* __restrict__ gptr,
+                                                      int2* __restrict__ glist, int32_t* __restrict__ glen) {
   extern __shared__ int32_t tab_s[];
   int32_t* dmax_s = tab_s;
   int32_t* off_s = tab_s + n_levels;
@@ -452,9 +466,20 @@ __global__ __launch_bounds__(256) void csr_runs_kernel(const int16_t* __restrict
   for (int i = threadIdx.x; i < n_r2c; i += 256) r2c_s[i] = r2c[i];
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tile = blockIdx.x * 4 + wave;
-  if (tile >= g.count) return;  // wave-uniform, after the block's only barrier
   const int bh = blockIdx.y;
+  int tile;
+  bool valid;
+  if constexpr (GROUPS) {
+    const int grem = blockIdx.x;  // group within the head
+    const int gc = grem % ngw, gr = (grem / ngw) % ngh, tg = grem / (ngw * ngh);
+    const int tr = gr * GROUP_ROWS + (wave >> 1), tc = 2 * gc + (wave & 1);
+    valid = wave < 2 * GROUP_ROWS && tr < g.nh && tc < g.nw;
+    tile = (tg * g.nh + tr) * g.nw + tc;
+  } else {
+    tile = blockIdx.x * 4 + wave;
+    valid = tile < g.count;
+  }
+  if (valid) {  // wave-uniform
   const size_t N = static_cast<size_t>(g.T) * g.H * g.W;
   const int64_t row = static_cast<int64_t>(bh) * g.count + tile;
   const int tq = tile / g.per_frame, rem = tile % g.per_frame;
@@ -539,6 +564,13 @@ __global__ __launch_bounds__(256) void csr_runs_kernel(const int16_t* __restrict
     counts[row] = count;
     rowwin[row] = t_lo | (max(0, t_hi - t_lo + 1) << 16);
   }
+  }
+  if constexpr (GROUPS) {
+    __syncthreads();  // the group's runs and windows, written above, are visible to wave 0
+    if (wave == 0)
+      group_fill<true>(g, DM, ngh, ngw, static_cast<int64_t>(bh) * g.T * ngh * ngw + blockIdx.x, lane, runs, rowwin,
+                       nullptr, nullptr, gptr, glist, glen);
+  }
 }
 
 // Step 3: expand the runs of each row into col_idx (ascending tile index).
@@ -593,16 +625,11 @@ __device__ __forceinline__ bool sorted_contains(const int32_t* __restrict__ a, i
 // glen[gid]; FILL = true: the entries from glist + gptr[gid].  One wave per
 // group.
 template <bool FILL>
-__global__ __launch_bounds__(256) void group_list_kernel(Grid g, int DM, int ngh, int ngw, int64_t n_groups,
-                                                        const int32_t* __restrict__ runs,
-                                                        const int32_t* __restrict__ rowwin,
-                                                        const int32_t* __restrict__ frow_ptr,
-                                                        const int32_t* __restrict__ fcol,
-                                                        const int32_t* __restrict__ gptr,
-                                                        int2* __restrict__ glist, int32_t* __restrict__ glen) {
-  const int lane = threadIdx.x & 63;
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (gid >= n_groups) return;  // wave-uniform
+__device__ __forceinline__ void group_fill(Grid g, int DM, int ngh, int ngw, int64_t gid, int lane,
+                                           const int32_t* __restrict__ runs, const int32_t* __restrict__ rowwin,
+                                           const int32_t* __restrict__ frow_ptr, const int32_t* __restrict__ fcol,
+                                           const int32_t* __restrict__ gptr, int2* __restrict__ glist,
+                                           int32_t* __restrict__ glen) {
   const int64_t per_head = static_cast<int64_t>(g.T) * ngh * ngw;
   const int64_t bh = gid / per_head;
   const int grem = static_cast<int>(gid % per_head);
@@ -683,6 +710,20 @@ __global__ __launch_bounds__(256) void group_list_kernel(Grid g, int DM, int ngh
     out += total;
   }
   if (lane == 0) glen[gid] = static_cast<int32_t>(out - beg);
+}
+
+template <bool FILL>
+__global__ __launch_bounds__(256) void group_list_kernel(Grid g, int DM, int ngh, int ngw, int64_t n_groups,
+                                                        const int32_t* __restrict__ runs,
+                                                        const int32_t* __restrict__ rowwin,
+                                                        const int32_t* __restrict__ frow_ptr,
+                                                        const int32_t* __restrict__ fcol,
+                                                        const int32_t* __restrict__ gptr,
+                                                        int2* __restrict__ glist, int32_t* __restrict__ glen) {
+  const int lane = threadIdx.x & 63;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (gid >= n_groups) return;  // wave-uniform
+  group_fill<FILL>(g, DM, ngh, ngw, gid, lane, runs, rowwin, frow_ptr, fcol, gptr, glist, glen);
 }
 
 // Token votes of every tile-list entry: one wave per query tile (lane =
@@ -1732,16 +1773,25 @@ static int log2i(int x) {
 
 hipError_t launch_csr_runs(bool l1, const int16_t* lv, const RadiusTable& tab, int n_levels, int row_base,
                            int BH, const Grid& tiles, int DM, int32_t* counts, int32_t* runs, int32_t* rowwin,
-                           hipStream_t s) {
-  const dim3 grid((tiles.count + 3) / 4, BH), block(256);
+                           hipStream_t s, const int32_t* gptr, int32_t* glist, int32_t* glen) {
   const size_t lds = (2 * static_cast<size_t>(n_levels) + tab.n_r2c) * sizeof(int32_t);
   if (lds > 65536) return hipErrorInvalidValue;  // the parameter check bounds the table well below this
-  if (l1)
-    csr_runs_kernel<true><<<grid, block, lds, s>>>(lv, tab.r2c, tab.r2off, tab.dmax, n_levels, tab.n_r2c, tab.T,
-                                                   row_base, tiles, log2i(tiles.tw), DM, counts, runs, rowwin);
-  else
-    csr_runs_kernel<false><<<grid, block, lds, s>>>(lv, tab.r2c, tab.r2off, tab.dmax, n_levels, tab.n_r2c, tab.T,
-                                                    row_base, tiles, log2i(tiles.tw), DM, counts, runs, rowwin);
+  const int ngh = (tiles.nh + GROUP_ROWS - 1) / GROUP_ROWS, ngw = (tiles.nw + 1) / 2;
+  int2* gl = reinterpret_cast<int2*>(glist);
+#define TRA_RUNS(L, G, GRID)                                                                                     \
+  csr_runs_kernel<L, G><<<GRID, 256, lds, s>>>(lv, tab.r2c, tab.r2off, tab.dmax, n_levels, tab.n_r2c, tab.T, row_base, \
+                                              tiles, log2i(tiles.tw), DM, counts, runs, rowwin, ngh, ngw, gptr, gl, glen)
+  if (glist) {
+    static_assert(2 * GROUP_ROWS <= 4, "one wave per query tile of a group");
+    const dim3 grid(tiles.T * ngh * ngw, BH);
+    if (l1) TRA_RUNS(true, true, grid);
+    else TRA_RUNS(false, true, grid);
+  } else {
+    const dim3 grid((tiles.count + 3) / 4, BH);
+    if (l1) TRA_RUNS(true, false, grid);
+    else TRA_RUNS(false, false, grid);
+  }
+#undef TRA_RUNS
   return hipGetLastError();
 }
 
