@@ -112,6 +112,8 @@ def main():
     ap.add_argument("--regroup", action="store_true",
                     help="plan variant: each query-tile group's queries dealt to the attention "
                          "kernel's waves in level order")
+    ap.add_argument("--group-rows", type=int, choices=[2, 3], default=None,
+                    help="query-tile rows per attention group (default: the plan's choice)")
     ap.add_argument("--generator", choices=["entropy_disk", "manhattan", "radial", "window_1d"],
                     default="entropy_disk")
     ap.add_argument("--radius", type=float, default=None, help="fixed radius (static generators)")
@@ -143,6 +145,8 @@ def main():
         variant["block_mask"] = 1
     if args.regroup:
         variant["regroup"] = 1
+    if args.group_rows is not None:
+        variant["group_rows"] = args.group_rows
     if args.generator != "entropy_disk":
         variant["generator"] = tra.GENERATORS[args.generator]
         if args.radius is not None or args.generator != "window_1d":
@@ -304,6 +308,7 @@ def main():
         "config": {"workload": cfg.name + ("+" + "+".join(f"{k}={v}" for k, v in variant.items()) if variant else ""),
                    "B": cfg.batch, "heads": cfg.heads, "grid": list(grid),
                    "head_dim": cfg.head_dim, "attention_calls_per_plan": calls,
+                   "group_rows": info["group_rows"],
                    "retained_density": retained / (cfg.heads * cfg.N ** 2),
                    "tile_efficiency": retained / listed},
         "ms_per_call": {"attention": attn_ms, "plan": plan_ms, "step_per_call": ms_step / calls},

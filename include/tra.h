@@ -120,6 +120,15 @@ typedef struct {
                              only, with the exact mask (block_mask 0) and
                              vote_threshold 1, which define the keys per
                              query rather than per query tile. */
+  int32_t group_rows;     /* query-tile rows of the bf16 attention kernel's
+                             unit of work, a group of group_rows x 2 query
+                             tiles of one frame ([TRA] section 2, "Exécution
+                             Efficace": block-sparse execution, key tiles
+                             loaded once per group): 2 or 3, or 0 to choose
+                             (3 unless that leaves more tile rows of the grid
+                             uncovered than 2, regroup is set, or the
+                             generator is the 1-D window).  Results are the
+                             same for either shape; regroup takes 2. */
 } tra_params;
 
 /*
@@ -169,6 +178,7 @@ typedef struct {
   int32_t k_lo;         /* level of table row 0 (-1 under radius_override)       */
   int32_t T;            /* columns of the radius table                           */
   int32_t max_row_len;  /* longest CSR row                                       */
+  int32_t group_rows;   /* bf16: query-tile rows per attention group (2 or 3)  */
 } tra_plan_info;
 
 /*
@@ -284,8 +294,9 @@ tra_status tra_plan_export(const tra_plan* plan, int16_t* levels, float* entropy
 
 /*
  * The bf16 attention kernel's unit of work (host copies; synchronises
- * `stream`): a group is 2 x 2 query tiles of one frame (group id = (b*heads +
- * head, frame, group row, group column) in row-major order), walked over the
+ * `stream`): a group is group_rows x 2 query tiles of one frame (group_rows
+ * from tra_plan_get_info; group id = (b*heads + head, frame, group row, group
+ * column) in row-major order), walked over the
  * ascending union of their tile lists.  *n_groups and *n_entries receive the
  * counts (call with NULL arrays first); gptr/glen int32 [n_groups] the offset
  * and length of each group's list in glist; glist int32 [2*n_entries], entry

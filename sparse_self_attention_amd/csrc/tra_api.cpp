@@ -175,6 +175,10 @@ tra_status check_params(const tra_shape* s, const tra_params* p, Table* tab) {
   // regrouped wave holds queries of all four tiles of its group.
   if (p->regroup && (p->block_mask || p->vote_threshold > 1))
     return fail(TRA_ERR_INVALID_ARG, "regroup takes the exact mask with vote_threshold 1");
+  if (p->group_rows != 0 && p->group_rows != 2 && p->group_rows != 3)
+    return fail(TRA_ERR_INVALID_ARG, "group_rows must be 0 (automatic), 2 or 3");
+  if (p->regroup && p->group_rows == 3)
+    return fail(TRA_ERR_INVALID_ARG, "regroup orders the queries of 2 x 2 groups (group_rows 0 or 2)");
   if ((p->generator == TRA_GEN_MANHATTAN || p->generator == TRA_GEN_RADIAL) && !(p->radius_override >= 0.0))
     return fail(TRA_ERR_INVALID_ARG, "the Manhattan and Radial generators take their radius from radius_override (>= 0)");
   const int T = s->T;
@@ -309,6 +313,7 @@ struct tra_plan {
   int32_t* glen = nullptr;   // per group: list length
   int32_t* gptr = nullptr;   // per group: list offset (exclusive scan of glen)
   int64_t n_groups = 0;
+  int group_rows = 0;        // bf16: query-tile rows per group (2 or 3)
   uint8_t* perm = nullptr;   // regroup: per group, its query slots in level order (GROUP_SLOTS each)
   int64_t* totals = nullptr;      // device: nnz, longest row, overflow flag (+4: groups, +8: filtered CSR)
   // vote threshold > 1: per-entry votes of the unfiltered CSR, the filtered CSR's
@@ -363,6 +368,20 @@ tra::RadiusTable radius_table_of(const tra_plan* p) {
                           metric_of(p->params)};
 }
 
+// Query-tile rows per group of the bf16 attention kernel.  A group of 3 x 2
+// query tiles shares each key tile among 384 queries and puts three waves on
+// every SIMD, which overlap one another's matrix and vector phases better
+// than two.  It is taken unless it would leave more tile rows of the grid
+// empty than 2 x 2 groups, the plan regroups queries (a 2 x 2 layout), or the
+// 1-D window generator is used (its masks need more registers than three
+// waves per SIMD leave at head_dim 128).
+int group_rows_for(const tra_params& p, const tra::Grid& tiles) {
+  if (p.group_rows) return p.group_rows;
+  if (p.regroup || p.generator == TRA_GEN_WINDOW_1D) return 2;
+  const int pad3 = (3 - tiles.nh % 3) % 3, pad2 = tiles.nh % 2;
+  return pad3 <= pad2 ? 3 : 2;
+}
+
 tra_status build_lists(tra_plan* p, hipStream_t st);
 
 // Steps entropy -> level -> tile lists into the plan's buffers.  The levels
@@ -402,13 +421,13 @@ tra_status build_group_lists_only(tra_plan* p, hipStream_t st) {
   // Each group writes its list into its own fixed slot (gptr[g] = g * stride,
   // set at creation) and its length to glen: no counting pass, no scan.
   if (p->params.generator == TRA_GEN_WINDOW_1D) {
-    TRA_LAUNCH(tra::launch_window_groups(true, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, p->gptr,
-                                      p->glist, p->glen, st));
+    TRA_LAUNCH(tra::launch_window_groups(true, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles,
+                                      p->group_rows, p->gptr, p->glist, p->glen, st));
   } else {
     // One pass: each workgroup writes the runs of a group's tiles, then the group's list.
     TRA_LAUNCH(tra::launch_csr_runs(p->params.generator == TRA_GEN_MANHATTAN, p->lv, radius_table_of(p),
                                     p->table.n_levels, p->row_base, p->BH, p->tiles, p->DM, p->counts, p->runs,
-                                    p->rowwin, st, p->gptr, p->glist, p->glen));
+                                    p->rowwin, st, p->group_rows, p->gptr, p->glist, p->glen));
   }
   TRA_HIP(hipEventRecord(p->built, st));
   return TRA_OK;
@@ -532,18 +551,18 @@ tra_status build_lists(tra_plan* p, hipStream_t st) {
       p->glist_cap = p->col_cap;
     }
     if (window) {
-      TRA_LAUNCH(tra::launch_window_groups(false, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, nullptr,
-                                        nullptr, p->glen, st));
+      TRA_LAUNCH(tra::launch_window_groups(false, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles,
+                                        p->group_rows, nullptr, nullptr, p->glen, st));
       TRA_LAUNCH(tra::launch_scan(p->glen, p->n_groups, p->gptr, p->totals + 4, st));
-      TRA_LAUNCH(tra::launch_window_groups(true, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles, p->gptr,
-                                        p->glist, p->glen, st));
+      TRA_LAUNCH(tra::launch_window_groups(true, p->lv, p->r2, p->dmax, s.T, p->row_base, p->BH, p->tiles,
+                                        p->group_rows, p->gptr, p->glist, p->glen, st));
     } else {
       const int32_t* frp = theta > 1 ? p->row_ptr : nullptr;
-      TRA_LAUNCH(tra::launch_group_lists(false, p->BH, p->tiles, p->DM, p->runs, p->rowwin, frp, p->col_idx, nullptr,
-                                      nullptr, p->glen, st));
+      TRA_LAUNCH(tra::launch_group_lists(false, p->BH, p->tiles, p->group_rows, p->DM, p->runs, p->rowwin, frp,
+                                      p->col_idx, nullptr, nullptr, p->glen, st));
       TRA_LAUNCH(tra::launch_scan(p->glen, p->n_groups, p->gptr, p->totals + 4, st));
-      TRA_LAUNCH(tra::launch_group_lists(true, p->BH, p->tiles, p->DM, p->runs, p->rowwin, frp, p->col_idx, p->gptr,
-                                      p->glist, p->glen, st));
+      TRA_LAUNCH(tra::launch_group_lists(true, p->BH, p->tiles, p->group_rows, p->DM, p->runs, p->rowwin, frp,
+                                      p->col_idx, p->gptr, p->glist, p->glen, st));
     }
   }
   TRA_HIP(hipEventRecord(p->built, st));  // the host-copy calls wait for it
@@ -630,7 +649,8 @@ tra_status create_plan(const tra_shape* shape, const tra_params* params, Table&&
     TRA_HIP_P(dev_alloc(&p->rowwin, p->n_rows * sizeof(int32_t)));
   }
   if (shape->dtype == TRA_BF16) {
-    p->n_groups = tra::group_count(p->BH, p->tiles);
+    p->group_rows = group_rows_for(*params, p->tiles);
+    p->n_groups = tra::group_count(p->BH, p->tiles, p->group_rows);
     TRA_HIP_P(dev_alloc(&p->glen, p->n_groups * sizeof(int32_t)));
     if (params->regroup) TRA_HIP_P(dev_alloc(&p->perm, p->n_groups * tra::GROUP_SLOTS));
     TRA_HIP_P(dev_alloc(&p->gptr, (p->n_groups + 1) * sizeof(int32_t)));
@@ -898,7 +918,8 @@ tra_status tra_attention(const tra_plan* plan, const void* q, const void* k, con
   const tra::RadiusTable tab = radius_table_of(plan);
   TRA_LAUNCH(tra::launch_attention(s.dtype, s.head_dim, q, k, v, o, plan->lv, tab, plan->row_base,
                                 plan->BH, plan->tiles, plan->row_ptr, plan->col_idx,
-                                plan->gptr, plan->glist, plan->glen, plan->perm, plan->params.block_mask != 0,
+                                plan->gptr, plan->glist, plan->glen, plan->group_rows, plan->perm,
+                                plan->params.block_mask != 0,
                                 plan->params.vote_threshold == 1, static_cast<hipStream_t>(stream)));
   return TRA_OK;
 }
@@ -936,6 +957,7 @@ tra_status tra_plan_get_info(const tra_plan* plan, tra_plan_info* info) {
   info->k_lo = plan->table.k_lo;
   info->T = plan->shape.T;
   info->max_row_len = plan->max_row_len;
+  info->group_rows = plan->group_rows;
   return TRA_OK;
 }
 

@@ -86,8 +86,8 @@ hipError_t launch_fill_levels(int16_t* lv, float* H, int64_t n, hipStream_t s);
 // glen; see launch_group_lists), in the same pass.
 hipError_t launch_csr_runs(bool l1, const int16_t* lv, const RadiusTable& tab, int n_levels, int row_base,
                            int BH, const Grid& tiles, int DM, int32_t* counts, int32_t* runs, int32_t* rowwin,
-                           hipStream_t s, const int32_t* gptr = nullptr, int32_t* glist = nullptr,
-                           int32_t* glen = nullptr);
+                           hipStream_t s, int group_rows = 2, const int32_t* gptr = nullptr,
+                           int32_t* glist = nullptr, int32_t* glen = nullptr);
 hipError_t launch_scan(const int32_t* counts, int64_t n_rows, int32_t* row_ptr,
                        int64_t* totals, hipStream_t s);
 hipError_t launch_csr_expand(int BH, const Grid& tiles, int DM, const int32_t* runs,
@@ -99,30 +99,27 @@ hipError_t launch_attention(int dtype, int d, const void* q, const void* k, cons
                             void* o, const int16_t* lv, const RadiusTable& tab, int row_base,
                             int BH, const Grid& tiles, const int32_t* row_ptr,
                             const int32_t* col_idx, const int32_t* gptr, const int32_t* glist,
-                            const int32_t* glen, const uint8_t* perm, bool block_mask, bool self_ref,
-                            hipStream_t s);
-// Work unit of the bf16 attention kernel: a group of GROUP_ROWS x 2 query
-// tiles of one frame, run by one workgroup of ATTN_THREADS threads (two waves
-// per query tile).
-#ifndef TRA_GROUP_ROWS
-#define TRA_GROUP_ROWS 2
-#endif
-constexpr int GROUP_ROWS = TRA_GROUP_ROWS;
-constexpr int ATTN_THREADS = 256 * GROUP_ROWS;
-inline int64_t group_count(int BH, const Grid& tiles) {
-  return static_cast<int64_t>(BH) * tiles.T * ((tiles.nh + GROUP_ROWS - 1) / GROUP_ROWS) * ((tiles.nw + 1) / 2);
+                            const int32_t* glen, int group_rows, const uint8_t* perm, bool block_mask,
+                            bool self_ref, hipStream_t s);
+// Work unit of the bf16 attention kernel: a group of group_rows x 2 query
+// tiles of one frame (group_rows 2 or 3, fixed per plan), run by one
+// workgroup of 256 * group_rows threads (two waves per query tile).
+inline int group_grid_rows(const Grid& tiles, int group_rows) { return (tiles.nh + group_rows - 1) / group_rows; }
+inline int group_grid_cols(const Grid& tiles) { return (tiles.nw + 1) / 2; }
+inline int64_t group_count(int BH, const Grid& tiles, int group_rows) {
+  return static_cast<int64_t>(BH) * tiles.T * group_grid_rows(tiles, group_rows) * group_grid_cols(tiles);
 }
-// Query regrouping: a group covers 8*GROUP_ROWS x 16 query positions (slot s
-// = row * 16 + column within the group); perm + GROUP_SLOTS * group lists
-// them sorted by (level, slot), positions outside the grid last.  Wave w of
-// the attention kernel takes entries 32w .. 32w + 31.
-constexpr int GROUP_SLOTS = 128 * GROUP_ROWS;
+// Query regrouping (groups of 2 x 2 query tiles): a group covers 16 x 16
+// query positions (slot s = row * 16 + column within the group); perm +
+// GROUP_SLOTS * group lists them sorted by (level, slot), positions outside
+// the grid last.  Wave w of the attention kernel takes entries 32w .. 32w + 31.
+constexpr int GROUP_SLOTS = 256;
 hipError_t launch_regroup(const int16_t* lv, int BH, const Grid& tiles, uint8_t* perm, hipStream_t s);
 // Merged tile lists of the groups, from the runs: with fill = false the length
 // of each group's list to glen; with fill = true the entries (two int32 each)
 // at glist + 2 * gptr[group] (gptr: exclusive scan of the lengths).  The sum
 // of the lengths is at most nnz.
-hipError_t launch_group_lists(bool fill, int BH, const Grid& tiles, int DM, const int32_t* runs,
+hipError_t launch_group_lists(bool fill, int BH, const Grid& tiles, int group_rows, int DM, const int32_t* runs,
                               const int32_t* rowwin, const int32_t* frow_ptr, const int32_t* fcol,
                               const int32_t* gptr, int32_t* glist, int32_t* glen, hipStream_t s);
 // Token votes per CSR entry (votes, int16 per entry), per-row count of entries
@@ -135,8 +132,8 @@ hipError_t launch_window_csr(bool fill, const int16_t* lv, const int32_t* r2, co
                              int row_base, int BH, const Grid& tiles, const int32_t* row_ptr, int32_t* counts,
                              int32_t* col_idx, hipStream_t s);
 hipError_t launch_window_groups(bool fill, const int16_t* lv, const int32_t* r2, const int32_t* dmax, int T,
-                                int row_base, int BH, const Grid& tiles, const int32_t* gptr, int32_t* glist,
-                                int32_t* glen, hipStream_t s);
+                                int row_base, int BH, const Grid& tiles, int group_rows, const int32_t* gptr,
+                                int32_t* glist, int32_t* glen, hipStream_t s);
 hipError_t launch_votes(bool l1, const int16_t* lv, const int32_t* r2, const int32_t* dmax, int T, int row_base,
                         int BH, const Grid& tiles, const int32_t* row_ptr, const int32_t* col_idx, int theta,
                         int16_t* votes, int32_t* counts2, unsigned long long* kept_votes, hipStream_t s);

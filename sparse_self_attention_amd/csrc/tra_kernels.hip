@@ -431,20 +431,21 @@ __device__ __forceinline__ int mask_half_width(int thr, int dh) {
 // radius table is staged in LDS (dynamic): per level row its largest active
 // distance and the offset of its active entries in the compact table, then
 // the compact table itself.
-template <bool FILL>
+template <bool FILL, int GR>
 __device__ __forceinline__ void group_fill(Grid g, int DM, int ngh, int ngw, int64_t gid, int lane,
                                            const int32_t* __restrict__ runs, const int32_t* __restrict__ rowwin,
                                            const int32_t* __restrict__ frow_ptr, const int32_t* __restrict__ fcol,
                                            const int32_t* __restrict__ gptr, int2* __restrict__ glist,
                                            int32_t* __restrict__ glen);
 
-// GROUPS: a workgroup takes the GROUP_ROWS x 2 query tiles of one group of the
-// bf16 attention kernel (wave m: tile row m / 2, column m % 2 of the group;
-// grid (groups per head, BH)), and once the runs of its tiles are written
-// wave 0 merges them into the group's list at gptr[group] (group_fill), so
-// that no second pass reads the runs back.
-template <bool L1, bool GROUPS>
-__global__ __launch_bounds__(256) void csr_runs_kernel(const int16_t* __restrict__ lv,
+// GR = 2 or 3: a workgroup of 2 * GR waves takes the GR x 2 query tiles of
+// one group of the bf16 attention kernel (wave m: tile row m / 2, column m %
+// 2 of the group; grid (groups per head, BH)), and once the runs of its tiles
+// are written wave 0 merges them into the group's list at gptr[group]
+// (group_fill), so that no second pass reads the runs back.  GR = 0: four
+// waves, one query tile each (grid (ceil(tiles per head / 4), BH)).
+template <bool L1, int GR>
+__global__ __launch_bounds__(GR == 3 ? 384 : 256) void csr_runs_kernel(const int16_t* __restrict__ lv,
                                                       const int32_t* __restrict__ r2c,
                                                       const int32_t* __restrict__ r2off,
                                                       const int32_t* __restrict__ dmax, int n_levels,
@@ -455,15 +456,17 @@ __global__ __launch_bounds__(256) void csr_runs_kernel(const int16_t* __restrict
                                                       int32_t* __restrict__ rowwin, int ngh, int ngw,
                                                       const int32_t* __restrict__ gptr,
                                                       int2* __restrict__ glist, int32_t* __restrict__ glen) {
+  constexpr bool GROUPS = GR > 0;
+  constexpr int NT = GR == 3 ? 384 : 256;
   extern __shared__ int32_t tab_s[];
   int32_t* dmax_s = tab_s;
   int32_t* off_s = tab_s + n_levels;
   int32_t* r2c_s = tab_s + 2 * n_levels;
-  for (int i = threadIdx.x; i < n_levels; i += 256) {
+  for (int i = threadIdx.x; i < n_levels; i += NT) {
     dmax_s[i] = dmax[i];
     off_s[i] = r2off[i];
   }
-  for (int i = threadIdx.x; i < n_r2c; i += 256) r2c_s[i] = r2c[i];
+  for (int i = threadIdx.x; i < n_r2c; i += NT) r2c_s[i] = r2c[i];
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int bh = blockIdx.y;
@@ -472,8 +475,8 @@ __global__ __launch_bounds__(256) void csr_runs_kernel(const int16_t* __restrict
   if constexpr (GROUPS) {
     const int grem = blockIdx.x;  // group within the head
     const int gc = grem % ngw, gr = (grem / ngw) % ngh, tg = grem / (ngw * ngh);
-    const int tr = gr * GROUP_ROWS + (wave >> 1), tc = 2 * gc + (wave & 1);
-    valid = wave < 2 * GROUP_ROWS && tr < g.nh && tc < g.nw;
+    const int tr = gr * GR + (wave >> 1), tc = 2 * gc + (wave & 1);
+    valid = tr < g.nh && tc < g.nw;
     tile = (tg * g.nh + tr) * g.nw + tc;
   } else {
     tile = blockIdx.x * 4 + wave;
@@ -568,8 +571,8 @@ __global__ __launch_bounds__(256) void csr_runs_kernel(const int16_t* __restrict
   if constexpr (GROUPS) {
     __syncthreads();  // the group's runs and windows, written above, are visible to wave 0
     if (wave == 0)
-      group_fill<true>(g, DM, ngh, ngw, static_cast<int64_t>(bh) * g.T * ngh * ngw + blockIdx.x, lane, runs, rowwin,
-                       nullptr, nullptr, gptr, glist, glen);
+      group_fill<true, GR>(g, DM, ngh, ngw, static_cast<int64_t>(bh) * g.T * ngh * ngw + blockIdx.x, lane, runs,
+                           rowwin, nullptr, nullptr, gptr, glist, glen);
   }
 }
 
@@ -611,7 +614,7 @@ __device__ __forceinline__ bool sorted_contains(const int32_t* __restrict__ a, i
   return lo < n && a[lo] == key;
 }
 
-// Union of the tile lists of a group of GROUP_ROWS x 2 query tiles of one
+// Union of the tile lists of a group of GR x 2 query tiles of one
 // frame (the unit of work of the bf16 attention kernel), from the runs of
 // their rows: per (frame, tile row) the union of the runs is again a run
 // (each nonempty run contains its own query tile's column, and the group's
@@ -624,7 +627,7 @@ __device__ __forceinline__ bool sorted_contains(const int32_t* __restrict__ a, i
 // tiles no query tile lists are left out.  FILL = false: the list's length to
 // glen[gid]; FILL = true: the entries from glist + gptr[gid].  One wave per
 // group.
-template <bool FILL>
+template <bool FILL, int GR>
 __device__ __forceinline__ void group_fill(Grid g, int DM, int ngh, int ngw, int64_t gid, int lane,
                                            const int32_t* __restrict__ runs, const int32_t* __restrict__ rowwin,
                                            const int32_t* __restrict__ frow_ptr, const int32_t* __restrict__ fcol,
@@ -635,13 +638,13 @@ __device__ __forceinline__ void group_fill(Grid g, int DM, int ngh, int ngw, int
   const int grem = static_cast<int>(gid % per_head);
   const int gc = grem % ngw, gr = (grem / ngw) % ngh, tq = grem / (ngw * ngh);
   const int64_t RS = static_cast<int64_t>((2 * DM + 1) * g.nh);
-  constexpr int NR = 2 * GROUP_ROWS;
+  constexpr int NR = 2 * GR;
   int64_t rows[NR];
   int wlo[NR], wn[NR];
   int t_lo = 0x7fffffff, t_hi = -1;
 #pragma unroll
   for (int m = 0; m < NR; ++m) {
-    const int tr = gr * GROUP_ROWS + (m >> 1), tc = 2 * gc + (m & 1);
+    const int tr = gr * GR + (m >> 1), tc = 2 * gc + (m & 1);
     rows[m] = bh * g.count + (static_cast<int64_t>(tq) * g.nh + tr) * g.nw + tc;
     const int w = (tr < g.nh && tc < g.nw) ? rowwin[rows[m]] : 0;
     wlo[m] = w & 0xffff;
@@ -712,7 +715,7 @@ __device__ __forceinline__ void group_fill(Grid g, int DM, int ngh, int ngw, int
   if (lane == 0) glen[gid] = static_cast<int32_t>(out - beg);
 }
 
-template <bool FILL>
+template <bool FILL, int GR>
 __global__ __launch_bounds__(256) void group_list_kernel(Grid g, int DM, int ngh, int ngw, int64_t n_groups,
                                                         const int32_t* __restrict__ runs,
                                                         const int32_t* __restrict__ rowwin,
@@ -723,7 +726,7 @@ __global__ __launch_bounds__(256) void group_list_kernel(Grid g, int DM, int ngh
   const int lane = threadIdx.x & 63;
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (gid >= n_groups) return;  // wave-uniform
-  group_fill<FILL>(g, DM, ngh, ngw, gid, lane, runs, rowwin, frow_ptr, fcol, gptr, glist, glen);
+  group_fill<FILL, GR>(g, DM, ngh, ngw, gid, lane, runs, rowwin, frow_ptr, fcol, gptr, glist, glen);
 }
 
 // Token votes of every tile-list entry: one wave per query tile (lane =
@@ -892,7 +895,7 @@ __global__ __launch_bounds__(256) void window_csr_kernel(const int16_t* __restri
 }
 
 // Query regrouping by level: one workgroup of GROUP_SLOTS threads per group
-// of query tiles sorts the keys (level << 8 | slot) of the group's positions
+// of 2 x 2 query tiles sorts the keys (level << 8 | slot) of the group's positions
 // (slot = row * 16 + column inside the group; positions outside the grid get
 // the largest level) with a bitonic network in LDS and stores the sorted
 // slots.  The keys are distinct, so the order is deterministic.
@@ -904,7 +907,7 @@ __global__ __launch_bounds__(GROUP_SLOTS) void regroup_kernel(const int16_t* __r
   const int bh = static_cast<int>(gid / per_head), grem = static_cast<int>(gid % per_head);
   const int tq = grem / (ngh * ngw), gr = (grem % (ngh * ngw)) / ngw, gc = grem % ngw;
   const int s = threadIdx.x;
-  const int hq = gr * 8 * GROUP_ROWS + (s >> 4), wq = gc * 16 + (s & 15);
+  const int hq = gr * 16 + (s >> 4), wq = gc * 16 + (s & 15);
   const size_t N = static_cast<size_t>(g.T) * g.H * g.W;
   const uint32_t level = (hq < g.H && wq < g.W)
                              ? static_cast<uint32_t>(lv[static_cast<size_t>(bh) * N + (static_cast<size_t>(tq) * g.H + hq) * g.W + wq] + 32768)
@@ -927,9 +930,9 @@ __global__ __launch_bounds__(GROUP_SLOTS) void regroup_kernel(const int16_t* __r
   perm[gid * GROUP_SLOTS + s] = static_cast<uint8_t>(key[s] & 0xffu);
 }
 
-// Group lists (GROUP_ROWS x 2 query tiles, the entries and membership bits of
+// Group lists (GR x 2 query tiles, the entries and membership bits of
 // group_list_kernel).  One wave per group.
-template <bool FILL>
+template <bool FILL, int GR>
 __global__ __launch_bounds__(256) void window_group_kernel(const int16_t* __restrict__ lv, const int32_t* __restrict__ r2,
                                                           const int32_t* __restrict__ dmax, int T, int row_base, Grid g,
                                                           int ngh, int ngw, int64_t n_groups,
@@ -942,12 +945,12 @@ __global__ __launch_bounds__(256) void window_group_kernel(const int16_t* __rest
   const int bh = static_cast<int>(gid / per_head);
   const int grem = static_cast<int>(gid % per_head);
   const int gc = grem % ngw, gr = (grem / ngw) % ngh, tq = grem / (ngw * ngh);
-  constexpr int NR = 2 * GROUP_ROWS;
+  constexpr int NR = 2 * GR;
   WindowQuery wq[NR];
   int dm = -1;
 #pragma unroll
   for (int m = 0; m < NR; ++m) {
-    const int tr = gr * GROUP_ROWS + (m >> 1), tc = 2 * gc + (m & 1);
+    const int tr = gr * GR + (m >> 1), tc = 2 * gc + (m & 1);
     wq[m] = WindowQuery{1, 0, -1};
     if (tr < g.nh && tc < g.nw)
       wq[m] = window_query(lv, r2, dmax, T, row_base, g, bh, tq, tr * g.th + (lane >> 3), tc * g.tw + (lane & 7));
@@ -1048,13 +1051,13 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
 // ---------------------------------------------------------------------------
 // Block-sparse attention, bf16, 8x8 tiles.
 //
-// Work decomposition.  A workgroup of 4 * GROUP_ROWS waves owns a group of
-// GROUP_ROWS x 2 query tiles of one frame (2 x 2 by default) and walks the
+// Work decomposition.  A workgroup of 4 * GR waves owns a group of GR x 2
+// query tiles of one frame (GR = 2 or 3, chosen per plan) and walks the
 // ascending union of their tile lists, prepared by the plan
 // (group_list_kernel).  Each key tile is streamed once per workgroup into one
 // of two LDS buffers by range-checked buffer DMA (buffer_load_dwordx4 ... lds),
 // so the next tile streams in while the current one is consumed, and all
-// waves use it: a 2 x 2 group loads each key tile once for 256 queries.  A
+// waves use it: a 3 x 2 group loads each key tile once for 384 queries.  A
 // wave owns 32 queries (lane % 32 = query) and skips a 32-key half of a tile
 // whenever none of its queries retains a key there: tiles that only the other
 // query tiles of the group need cost loads but no matrix work.
@@ -1080,8 +1083,8 @@ template <int D> struct AttnLds {
   static_assert(64 * KSTR % 1024 == 0 && 64 * VSTR % 1024 == 0, "tile must be whole segments");
 };
 
-template <int D, int METRIC, bool BLOCK>
-__global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf16_kernel(
+template <int D, int METRIC, bool BLOCK, int GR>
+__global__ __launch_bounds__(256 * GR, 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, const int16_t* __restrict__ lv,
     const int32_t* __restrict__ r2c, const int32_t* __restrict__ r2off,
@@ -1089,7 +1092,8 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
     const int32_t* __restrict__ gptr, const int2* __restrict__ glist,
     const int32_t* __restrict__ glen, const uint8_t* __restrict__ perm, int self_ref) {
   using L = AttnLds<D>;
-  constexpr int NWAVES = ATTN_THREADS / 64;
+  constexpr int NTHREADS = 256 * GR;
+  constexpr int NWAVES = NTHREADS / 64;
   constexpr int KS = D / 16;  // k-steps of S^T
   constexpr int DB = D / 32;  // 32-row blocks of O^T
   constexpr int NONE = 0x7fffffff;
@@ -1106,10 +1110,10 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
   const int per_xcd = gridDim.x / 8;
   const int gid = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   if (gid >= n_groups) return;  // uniform over the workgroup, before any barrier
-  for (int i = threadIdx.x; i < n_r2c; i += ATTN_THREADS) r2s[i] = r2c[i];
+  for (int i = threadIdx.x; i < n_r2c; i += NTHREADS) r2s[i] = r2c[i];
   __syncthreads();
 
-  // Group = GROUP_ROWS x 2 query tiles of one frame.
+  // Group = GR x 2 query tiles of one frame.
   const int groups_per_frame = ngh * ngw;
   const int per_head = g.T * groups_per_frame;
   const int bh = gid / per_head;
@@ -1118,25 +1122,26 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
   const int gr = (grem % groups_per_frame) / ngw, gc = grem % ngw;
   const size_t N = static_cast<size_t>(g.T) * g.H * g.W;
 
-  // This wave: tile row gr*GROUP_ROWS + wave/4, tile column gc*2 + wcol, query
-  // rows 4*(wave%2)..+3 of that tile; lane%32 -> query.  Waves w and w+4 share
-  // a SIMD; they take tiles of different rows and columns, so that a key tile
-  // listed by one row or one column of the group keeps every SIMD busy.
+  // This wave: tile row gr*GR + wave/4, tile column gc*2 + wcol, query rows
+  // 4*(wave%2)..+3 of that tile; lane%32 -> query.  Waves w, w+4 (and w+8)
+  // share a SIMD; they take tiles of different rows and alternating columns,
+  // so that a key tile listed by one row or one column of the group keeps
+  // every SIMD busy.
   const int wcol = ((wave >> 1) ^ (wave >> 2)) & 1;
   int hq, wq, mbit;
   bool qvalid;
   if (perm) {
-    // Regrouped: the wave's queries are entries 32*wave .. +31 of the
-    // group's level order, anywhere in the group's 8*GROUP_ROWS x 16
-    // positions, so every tile the group lists may hold keys for them.
+    // Regrouped (2 x 2 groups only): the wave's queries are entries
+    // 32*wave .. +31 of the group's level order, anywhere in the group's
+    // 16 x 16 positions, so every tile the group lists may hold keys for them.
     const int slot = perm[static_cast<size_t>(gid) * GROUP_SLOTS + 32 * wave + col];
-    hq = gr * 8 * GROUP_ROWS + (slot >> 4);
+    hq = gr * 16 + (slot >> 4);
     wq = gc * 16 + (slot & 15);
     mbit = 0xf;
     qvalid = hq < g.H && wq < g.W;
   } else {
     const int tc = gc * 2 + wcol;
-    const int trq = gr * GROUP_ROWS + (wave >> 2);
+    const int trq = gr * GR + (wave >> 2);
     wq = tc * 8 + (col & 7);
     hq = trq * 8 + 4 * (wave & 1) + (col >> 3);
     // This wave's query tile in the group's membership bits (see group_list_kernel).
@@ -1178,7 +1183,7 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
     }
     const int ex = __builtin_amdgcn_readlane(cur.x, j & 63);
     const int ey = __builtin_amdgcn_readlane(cur.y, j & 63);
-    return TileGeo{ex & 0xffff, ey & 0xffff, ey >> 16, (ex >> 16) & 0xf, ex < 0};
+    return TileGeo{ex & 0xffff, ey & 0xffff, ey >> 16, (ex >> 16) & 0x3f, ex < 0};
   };
 
   // One buffer resource per head for K and V: every tile, edge tiles
@@ -1271,18 +1276,24 @@ __global__ __launch_bounds__(ATTN_THREADS, GROUP_ROWS == 1 ? 2 : 1) void attn_bf
   const int partner = (lane ^ 32) << 2;  // ds_bpermute address of the other half
 
   // S^T block blk (keys 32*blk..+31 of the tile x this wave's 32 queries).
-  // All eight K fragments are read before the chain starts (the scheduling
-  // fence keeps the compiler from spreading the reads between the MFMAs,
-  // where each pair of them would wait out a full LDS latency).
+  // The K fragments are read in NP parts, each part's reads before its MFMAs
+  // (the scheduling fence keeps the compiler from spreading the reads between
+  // the MFMAs, where each pair of them would wait out a full LDS latency): one
+  // part with two waves per SIMD, two with three, whose registers are fewer.
   auto scores = [&](const char* buf, int blk) {
-    bf16x8 af[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      af[ks] = *reinterpret_cast<const bf16x8*>(buf + kread + 32 * blk * L::KSTR + 32 * ks);
-    __builtin_amdgcn_sched_barrier(0);
+    constexpr int NP = GR == 3 ? 2 : 1, KP = KS / NP;
     f32x16 acc = (f32x16){0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qf[ks], acc, 0, 0, 0);
+    for (int pp = 0; pp < NP; ++pp) {
+      bf16x8 af[KP];
+#pragma unroll
+      for (int ks = 0; ks < KP; ++ks)
+        af[ks] = *reinterpret_cast<const bf16x8*>(buf + kread + 32 * blk * L::KSTR + 32 * (pp * KP + ks));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < KP; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qf[pp * KP + ks], acc, 0, 0, 0);
+    }
     return acc;
   };
   // Online softmax of one 32-key block.  msk[x] holds the radius mask of
@@ -1773,23 +1784,28 @@ static int log2i(int x) {
 
 hipError_t launch_csr_runs(bool l1, const int16_t* lv, const RadiusTable& tab, int n_levels, int row_base,
                            int BH, const Grid& tiles, int DM, int32_t* counts, int32_t* runs, int32_t* rowwin,
-                           hipStream_t s, const int32_t* gptr, int32_t* glist, int32_t* glen) {
+                           hipStream_t s, int group_rows, const int32_t* gptr, int32_t* glist, int32_t* glen) {
   const size_t lds = (2 * static_cast<size_t>(n_levels) + tab.n_r2c) * sizeof(int32_t);
   if (lds > 65536) return hipErrorInvalidValue;  // the parameter check bounds the table well below this
-  const int ngh = (tiles.nh + GROUP_ROWS - 1) / GROUP_ROWS, ngw = (tiles.nw + 1) / 2;
+  if (glist && group_rows != 2 && group_rows != 3) return hipErrorInvalidValue;
+  const int ngh = group_grid_rows(tiles, glist ? group_rows : 2), ngw = group_grid_cols(tiles);
   int2* gl = reinterpret_cast<int2*>(glist);
-#define TRA_RUNS(L, G, GRID)                                                                                     \
-  csr_runs_kernel<L, G><<<GRID, 256, lds, s>>>(lv, tab.r2c, tab.r2off, tab.dmax, n_levels, tab.n_r2c, tab.T, row_base, \
-                                              tiles, log2i(tiles.tw), DM, counts, runs, rowwin, ngh, ngw, gptr, gl, glen)
+#define TRA_RUNS(L, G, GRID, NT)                                                                                  \
+  csr_runs_kernel<L, G><<<GRID, NT, lds, s>>>(lv, tab.r2c, tab.r2off, tab.dmax, n_levels, tab.n_r2c, tab.T, row_base, \
+                                             tiles, log2i(tiles.tw), DM, counts, runs, rowwin, ngh, ngw, gptr, gl, glen)
   if (glist) {
-    static_assert(2 * GROUP_ROWS <= 4, "one wave per query tile of a group");
     const dim3 grid(tiles.T * ngh * ngw, BH);
-    if (l1) TRA_RUNS(true, true, grid);
-    else TRA_RUNS(false, true, grid);
+    if (group_rows == 3) {
+      if (l1) TRA_RUNS(true, 3, grid, 384);
+      else TRA_RUNS(false, 3, grid, 384);
+    } else {
+      if (l1) TRA_RUNS(true, 2, grid, 256);
+      else TRA_RUNS(false, 2, grid, 256);
+    }
   } else {
     const dim3 grid((tiles.count + 3) / 4, BH);
-    if (l1) TRA_RUNS(true, false, grid);
-    else TRA_RUNS(false, false, grid);
+    if (l1) TRA_RUNS(true, 0, grid, 256);
+    else TRA_RUNS(false, 0, grid, 256);
   }
 #undef TRA_RUNS
   return hipGetLastError();
@@ -1815,18 +1831,24 @@ size_t attention_lds_bytes(int d, int n_r2c) {
   return kv + static_cast<size_t>(n_r2c) * sizeof(int32_t);
 }
 
-hipError_t launch_group_lists(bool fill, int BH, const Grid& tiles, int DM, const int32_t* runs,
+hipError_t launch_group_lists(bool fill, int BH, const Grid& tiles, int group_rows, int DM, const int32_t* runs,
                               const int32_t* rowwin, const int32_t* frow_ptr, const int32_t* fcol,
                               const int32_t* gptr, int32_t* glist, int32_t* glen, hipStream_t s) {
-  const int ngh = (tiles.nh + GROUP_ROWS - 1) / GROUP_ROWS, ngw = (tiles.nw + 1) / 2;
-  const int64_t n_groups = static_cast<int64_t>(BH) * tiles.T * ngh * ngw;
+  if (group_rows != 2 && group_rows != 3) return hipErrorInvalidValue;
+  const int ngh = group_grid_rows(tiles, group_rows), ngw = group_grid_cols(tiles);
+  const int64_t n_groups = group_count(BH, tiles, group_rows);
   const unsigned grid = static_cast<unsigned>((n_groups + 3) / 4);
-  if (fill)
-    group_list_kernel<true><<<grid, 256, 0, s>>>(tiles, DM, ngh, ngw, n_groups, runs, rowwin, frow_ptr, fcol,
-                                                 gptr, reinterpret_cast<int2*>(glist), glen);
-  else
-    group_list_kernel<false><<<grid, 256, 0, s>>>(tiles, DM, ngh, ngw, n_groups, runs, rowwin, frow_ptr, fcol,
-                                                  gptr, reinterpret_cast<int2*>(glist), glen);
+  auto* gl = reinterpret_cast<int2*>(glist);
+#define TRA_GL(F, G) \
+  group_list_kernel<F, G><<<grid, 256, 0, s>>>(tiles, DM, ngh, ngw, n_groups, runs, rowwin, frow_ptr, fcol, gptr, gl, glen)
+  if (group_rows == 3) {
+    if (fill) TRA_GL(true, 3);
+    else TRA_GL(false, 3);
+  } else {
+    if (fill) TRA_GL(true, 2);
+    else TRA_GL(false, 2);
+  }
+#undef TRA_GL
   return hipGetLastError();
 }
 
@@ -1843,17 +1865,23 @@ hipError_t launch_window_csr(bool fill, const int16_t* lv, const int32_t* r2, co
 }
 
 hipError_t launch_window_groups(bool fill, const int16_t* lv, const int32_t* r2, const int32_t* dmax, int T,
-                                int row_base, int BH, const Grid& tiles, const int32_t* gptr, int32_t* glist,
-                                int32_t* glen, hipStream_t s) {
-  const int ngh = (tiles.nh + GROUP_ROWS - 1) / GROUP_ROWS, ngw = (tiles.nw + 1) / 2;
-  const int64_t n_groups = static_cast<int64_t>(BH) * tiles.T * ngh * ngw;
+                                int row_base, int BH, const Grid& tiles, int group_rows, const int32_t* gptr,
+                                int32_t* glist, int32_t* glen, hipStream_t s) {
+  if (group_rows != 2 && group_rows != 3) return hipErrorInvalidValue;
+  const int ngh = group_grid_rows(tiles, group_rows), ngw = group_grid_cols(tiles);
+  const int64_t n_groups = group_count(BH, tiles, group_rows);
   const unsigned grid = static_cast<unsigned>((n_groups + 3) / 4);
-  if (fill)
-    window_group_kernel<true><<<grid, 256, 0, s>>>(lv, r2, dmax, T, row_base, tiles, ngh, ngw, n_groups, gptr,
-                                                   reinterpret_cast<int2*>(glist), glen);
-  else
-    window_group_kernel<false><<<grid, 256, 0, s>>>(lv, r2, dmax, T, row_base, tiles, ngh, ngw, n_groups, gptr,
-                                                    reinterpret_cast<int2*>(glist), glen);
+  auto* gl = reinterpret_cast<int2*>(glist);
+#define TRA_WG(F, G) \
+  window_group_kernel<F, G><<<grid, 256, 0, s>>>(lv, r2, dmax, T, row_base, tiles, ngh, ngw, n_groups, gptr, gl, glen)
+  if (group_rows == 3) {
+    if (fill) TRA_WG(true, 3);
+    else TRA_WG(false, 3);
+  } else {
+    if (fill) TRA_WG(true, 2);
+    else TRA_WG(false, 2);
+  }
+#undef TRA_WG
   return hipGetLastError();
 }
 
@@ -1879,10 +1907,9 @@ hipError_t launch_vote_compact(int64_t n_rows, const int32_t* row_ptr, const int
 }
 
 hipError_t launch_regroup(const int16_t* lv, int BH, const Grid& tiles, uint8_t* perm, hipStream_t s) {
-  static_assert(GROUP_SLOTS == 32 * (ATTN_THREADS / 64), "one slot per query lane of the attention workgroup");
-  static_assert(8 * GROUP_ROWS <= 16, "slots hold 4-bit rows");
-  const int ngh = (tiles.nh + GROUP_ROWS - 1) / GROUP_ROWS, ngw = (tiles.nw + 1) / 2;
-  const int64_t groups = group_count(BH, tiles);
+  static_assert(GROUP_SLOTS == 32 * 8, "one slot per query lane of a 2 x 2 group's attention workgroup");
+  const int ngh = group_grid_rows(tiles, 2), ngw = group_grid_cols(tiles);
+  const int64_t groups = group_count(BH, tiles, 2);
   regroup_kernel<<<static_cast<unsigned>(groups), GROUP_SLOTS, 0, s>>>(lv, tiles, ngh, ngw, perm);
   return hipGetLastError();
 }
@@ -1891,8 +1918,8 @@ hipError_t launch_attention(int dtype, int d, const void* q, const void* k, cons
                             void* o, const int16_t* lv, const RadiusTable& tab, int row_base,
                             int BH, const Grid& tiles, const int32_t* row_ptr,
                             const int32_t* col_idx, const int32_t* gptr, const int32_t* glist,
-                            const int32_t* glen, const uint8_t* perm, bool block_mask, bool self_ref,
-                            hipStream_t s) {
+                            const int32_t* glen, int group_rows, const uint8_t* perm, bool block_mask,
+                            bool self_ref, hipStream_t s) {
   const int32_t* r2 = tab.r2;
   const unsigned rows = static_cast<unsigned>(BH) * tiles.count;
   if (dtype == 1) {
@@ -1900,29 +1927,37 @@ hipError_t launch_attention(int dtype, int d, const void* q, const void* k, cons
     const auto* kk = static_cast<const uint16_t*>(k);
     const auto* vv = static_cast<const uint16_t*>(v);
     auto* oo = static_cast<uint16_t*>(o);
-    const int ngh = (tiles.nh + GROUP_ROWS - 1) / GROUP_ROWS, ngw = (tiles.nw + 1) / 2;
-    const int64_t groups = static_cast<int64_t>(BH) * tiles.T * ngh * ngw;
+    if (group_rows != 2 && group_rows != 3) return hipErrorInvalidValue;
+    if (perm && group_rows != 2) return hipErrorInvalidValue;  // regrouping covers 2 x 2 groups
+    const int ngh = group_grid_rows(tiles, group_rows), ngw = group_grid_cols(tiles);
+    const int64_t groups = group_count(BH, tiles, group_rows);
     const unsigned grid = static_cast<unsigned>((groups + 7) / 8 * 8);
     const int ng = static_cast<int>(groups);
     const size_t lds_tab = static_cast<size_t>(tab.n_r2c) * sizeof(int32_t);
-#define TRA_ATTN(DD, M, B)                                                                                 \
-  attn_bf16_kernel<DD, M, B><<<grid, ATTN_THREADS, lds_tab, s>>>(qq, kk, vv, oo, lv, tab.r2c, tab.r2off, tab.dmax, \
-                                                                 tab.n_r2c, row_base, tiles, ngh, ngw, ng, gptr,     \
-                                                                 reinterpret_cast<const int2*>(glist), glen, perm,   \
-                                                                 self_ref ? 1 : 0)
-    if (block_mask) {
-      if (d == 128) TRA_ATTN(128, METRIC_L2, true);
-      else TRA_ATTN(64, METRIC_L2, true);
-    } else if (tab.metric == METRIC_L1) {
-      if (d == 128) TRA_ATTN(128, METRIC_L1, false);
-      else TRA_ATTN(64, METRIC_L1, false);
-    } else if (tab.metric == METRIC_WINDOW) {
-      if (d == 128) TRA_ATTN(128, METRIC_WINDOW, false);
-      else TRA_ATTN(64, METRIC_WINDOW, false);
-    } else {
-      if (d == 128) TRA_ATTN(128, METRIC_L2, false);
-      else TRA_ATTN(64, METRIC_L2, false);
-    }
+#define TRA_ATTN(DD, M, B, G)                                                                                   \
+  attn_bf16_kernel<DD, M, B, G><<<grid, 256 * G, lds_tab, s>>>(qq, kk, vv, oo, lv, tab.r2c, tab.r2off, tab.dmax, \
+                                                               tab.n_r2c, row_base, tiles, ngh, ngw, ng, gptr,     \
+                                                               reinterpret_cast<const int2*>(glist), glen, perm,   \
+                                                               self_ref ? 1 : 0)
+#define TRA_ATTN_G(G)                                                  \
+  do {                                                                 \
+    if (block_mask) {                                                  \
+      if (d == 128) TRA_ATTN(128, METRIC_L2, true, G);                 \
+      else TRA_ATTN(64, METRIC_L2, true, G);                           \
+    } else if (tab.metric == METRIC_L1) {                              \
+      if (d == 128) TRA_ATTN(128, METRIC_L1, false, G);                \
+      else TRA_ATTN(64, METRIC_L1, false, G);                          \
+    } else if (tab.metric == METRIC_WINDOW) {                          \
+      if (d == 128) TRA_ATTN(128, METRIC_WINDOW, false, G);            \
+      else TRA_ATTN(64, METRIC_WINDOW, false, G);                      \
+    } else {                                                           \
+      if (d == 128) TRA_ATTN(128, METRIC_L2, false, G);                \
+      else TRA_ATTN(64, METRIC_L2, false, G);                          \
+    }                                                                  \
+  } while (0)
+    if (group_rows == 3) TRA_ATTN_G(3);
+    else TRA_ATTN_G(2);
+#undef TRA_ATTN_G
 #undef TRA_ATTN
   } else {
     const auto* qq = static_cast<const float*>(q);

@@ -65,6 +65,16 @@ int main(void) {
   bp.block_mask = 1; /* block masks are per query tile */
   EXPECT(tra_params_validate(&wan, &bp) == TRA_ERR_INVALID_ARG);
   EXPECT(strlen(tra_last_error()) > 0);
+  bp = p; /* attention groups of 2 or 3 query-tile rows; regrouping orders 2 x 2 groups */
+  bp.group_rows = 3;
+  EXPECT(tra_params_validate(&wan, &bp) == TRA_OK);
+  bp.group_rows = 4;
+  EXPECT(tra_params_validate(&wan, &bp) == TRA_ERR_INVALID_ARG);
+  bp.group_rows = 3;
+  bp.regroup = 1;
+  EXPECT(tra_params_validate(&wan, &bp) == TRA_ERR_INVALID_ARG);
+  bp.group_rows = 2;
+  EXPECT(tra_params_validate(&wan, &bp) == TRA_OK);
 
   /* radius tables: size query, then the table */
   int32_t n_levels = 0, k_lo = 0;

@@ -140,20 +140,20 @@ def check_csr_properties(cfg, run):
     assert all(own)
 
 
-def expected_group_lists(cfg, row_ptr, col_idx, bh):
+def expected_group_lists(cfg, row_ptr, col_idx, bh, rows=2):
     """The bf16 kernel's group lists of head slice bh, derived from CSR rows:
-    per 2x2 group of query tiles, the ascending union of the members' key
+    per group of rows x 2 query tiles, the ascending union of the members' key
     tiles with member bits and edge flags (as the C ABI exports them)."""
     tiles = O.Geometry(cfg.T, cfg.H, cfg.W, cfg.tile_h, cfg.tile_w)
     nh, nw = tiles.nbh, tiles.nbw
-    ngh, ngw = (nh + 1) // 2, (nw + 1) // 2
+    ngh, ngw = (nh + rows - 1) // rows, (nw + 1) // 2
     out = {}
     for t in range(cfg.T):
         for gr in range(ngh):
             for gc in range(ngw):
                 members = {}
-                for m in range(4):
-                    tr, tc = 2 * gr + (m >> 1), 2 * gc + (m & 1)
+                for m in range(2 * rows):
+                    tr, tc = rows * gr + (m >> 1), 2 * gc + (m & 1)
                     if tr < nh and tc < nw:
                         r = bh * tiles.count + (t * nh + tr) * nw + tc
                         for K in col_idx[row_ptr[r]:row_ptr[r + 1]]:
@@ -176,7 +176,9 @@ def check_group_lists(cfg, run, bh):
     (which the other checks compare with the oracle), entry for entry."""
     gptr, glen, gl = run["plan"].export_groups()
     exp = run["export"]
-    want = expected_group_lists(cfg, exp["row_ptr"].astype(np.int64), exp["col_idx"].astype(np.int64), bh)
+    rows = run["plan"].info()["group_rows"]
+    assert rows in (2, 3)
+    want = expected_group_lists(cfg, exp["row_ptr"].astype(np.int64), exp["col_idx"].astype(np.int64), bh, rows)
     for gid, ent in want.items():
         got = gl[gptr[gid]:gptr[gid] + glen[gid]].astype(np.int64)
         assert np.array_equal(got, ent), f"group {gid}: {got[:6].tolist()} vs {ent[:6].tolist()}"
@@ -219,3 +221,34 @@ def check_key_sets(cfg, plan, lv, gpu, seed):
         assert len(bad) == 0, f"{len(bad)} queries with a different key set, first {bad[:8].tolist()}"
         worst = max(worst, float(np.abs(scaled - got).max()))
     return int(size.max()), worst
+
+
+LISTED_MAX_ABS, LISTED_MEAN_ABS = 2e-2, 2e-3
+
+
+def check_listed(cfg, run, h, block_only, tile_sample=None, query_sample=None):
+    """Head h of a plan with a vote threshold and/or block-only masks: each
+    query tile's filtered list against the oracle's token votes, and O against
+    the oracle's attention over exactly the listed tiles (every key of a listed
+    tile with block_only, else the exact mask inside them)."""
+    p = cfg.params()
+    exp = run["export"]
+    lv = exp["levels"][h].astype(np.int64)
+    R2 = O.radius_table(p, cfg.T)
+    tiles = O.Geometry(cfg.T, cfg.H, cfg.W, cfg.tile_h, cfg.tile_w)
+    rp = exp["row_ptr"].astype(np.int64)
+    base = h * tiles.count
+    rows_h = rp[base:base + tiles.count + 1]
+    ci_h = exp["col_idx"][rows_h[0]:rows_h[-1]].astype(np.int64)
+    rp_h = rows_h - rows_h[0]
+    theta = p["vote_threshold"]
+    for a in (range(tiles.count) if tile_sample is None else tile_sample):
+        votes = O.tile_votes(int(a), lv, R2, tiles, p)
+        ref = np.array(sorted(b for b, n in votes.items() if n >= theta), dtype=np.int64)
+        assert np.array_equal(ci_h[rp_h[a]:rp_h[a + 1]], ref), f"tile list of query tile {a} differs"
+    qs = np.arange(cfg.N) if query_sample is None else np.asarray(query_sample)
+    qh, kh, vh = (run[x][0, h].double().cpu().numpy() for x in ("q", "k", "v"))
+    ref = O.attention_rows_listed(qh, kh, vh, qs, lv, R2, tiles, p, rp_h, ci_h, block_only)
+    err = np.abs(run["o"][0, h].double().cpu().numpy()[qs] - ref)
+    assert err.max() <= LISTED_MAX_ABS and err.mean() <= LISTED_MEAN_ABS, (err.max(), err.mean())
+    return err

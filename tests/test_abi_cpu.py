@@ -78,6 +78,9 @@ def _validate(**kw):
     (dict(regroup=1, dtype=torch.float32), "TRA_ERR_INVALID_ARG"),  # a layout of the bf16 kernel
     (dict(regroup=1, block_mask=1), "TRA_ERR_INVALID_ARG"),  # block masks are per query tile
     (dict(regroup=1, vote_threshold=4), "TRA_ERR_INVALID_ARG"),  # so are vote-filtered lists
+    (dict(group_rows=1), "TRA_ERR_INVALID_ARG"),  # attention groups have 2 or 3 query-tile rows
+    (dict(group_rows=4), "TRA_ERR_INVALID_ARG"),
+    (dict(group_rows=3, regroup=1), "TRA_ERR_INVALID_ARG"),  # regrouping orders 2 x 2 groups
     # every frame active (decay 1) over 2,000 frames at 88 levels: the radius
     # table's active entries (88 x 2,000) exceed what the tile-list kernel stages
     (dict(grid=(2000, 4, 4), heads=1, dtype=torch.float32, decay=1.0, budget_max=float(2 ** 20)),
@@ -92,6 +95,13 @@ def test_validation_rejects(kw, code):
 def test_validation_accepts_regroup():
     _validate(regroup=1)
     _validate(regroup=1, generator=3)
+    _validate(regroup=1, group_rows=2)
+
+
+def test_validation_accepts_group_rows():
+    for r in (0, 2, 3):
+        _validate(group_rows=r)
+        _validate(group_rows=r, dtype=torch.float32)
 
 
 def test_validation_accepts_large_fp32_head():

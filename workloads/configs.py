@@ -47,6 +47,7 @@ class Workload:
     vote_threshold: int = 1  # key tile listed when >= this many pairs are retained
     block_mask: int = 0  # 1: block-only mask (every key of a listed tile)
     regroup: int = 0  # 1: the attention kernel deals each group's queries to its waves in level order
+    group_rows: int = 0  # query-tile rows per attention group: 2, 3, or 0 to let the plan choose
     seed: int = 0
     batch: int = 1
     reuse_calls: int = 1  # attention calls that reuse one plan
@@ -63,7 +64,7 @@ class Workload:
         """Method parameters (what the planning call receives)."""
         keys = ("a", "c", "budget_min", "budget_max", "decay", "levels_per_nat",
                 "pool_h", "pool_w", "tile_h", "tile_w", "radius_override", "generator",
-                "vote_threshold", "block_mask", "regroup")
+                "vote_threshold", "block_mask", "regroup", "group_rows")
         d = asdict(self)
         return {k: d[k] for k in keys}
 
