@@ -83,7 +83,8 @@ hipError_t launch_fill_levels(int16_t* lv, float* H, int64_t n, hipStream_t s);
 // and the expansion of the runs into col_idx.  DM is the largest active frame
 // distance of the radius table; runs holds n_rows * (2*DM + 1) * nh int32.
 // With glist, the groups' lists are filled too (fixed slots at gptr, lengths to
-// glen; see launch_group_lists), in the same pass.
+// glen; see launch_group_lists): in the same pass for 2 x 2 groups, by a second
+// launch for 3 x 2 groups.
 hipError_t launch_csr_runs(bool l1, const int16_t* lv, const RadiusTable& tab, int n_levels, int row_base,
                            int BH, const Grid& tiles, int DM, int32_t* counts, int32_t* runs, int32_t* rowwin,
                            hipStream_t s, int group_rows = 2, const int32_t* gptr = nullptr,

@@ -438,14 +438,14 @@ __device__ __forceinline__ void group_fill(Grid g, int DM, int ngh, int ngw, int
                                            const int32_t* __restrict__ gptr, int2* __restrict__ glist,
                                            int32_t* __restrict__ glen);
 
-// GR = 2 or 3: a workgroup of 2 * GR waves takes the GR x 2 query tiles of
-// one group of the bf16 attention kernel (wave m: tile row m / 2, column m %
-// 2 of the group; grid (groups per head, BH)), and once the runs of its tiles
-// are written wave 0 merges them into the group's list at gptr[group]
+// GR = 2: a workgroup of 2 * GR waves takes the GR x 2 query tiles of one
+// group of the bf16 attention kernel (wave m: tile row m / 2, column m % 2 of
+// the group; grid (groups per head, BH)), and once the runs of its tiles are
+// written wave 0 merges them into the group's list at gptr[group]
 // (group_fill), so that no second pass reads the runs back.  GR = 0: four
 // waves, one query tile each (grid (ceil(tiles per head / 4), BH)).
 template <bool L1, int GR>
-__global__ __launch_bounds__(GR == 3 ? 384 : 256) void csr_runs_kernel(const int16_t* __restrict__ lv,
+__global__ __launch_bounds__(256) void csr_runs_kernel(const int16_t* __restrict__ lv,
                                                       const int32_t* __restrict__ r2c,
                                                       const int32_t* __restrict__ r2off,
                                                       const int32_t* __restrict__ dmax, int n_levels,
@@ -456,8 +456,9 @@ __global__ __launch_bounds__(GR == 3 ? 384 : 256) void csr_runs_kernel(const int
                                                       int32_t* __restrict__ rowwin, int ngh, int ngw,
                                                       const int32_t* __restrict__ gptr,
                                                       int2* __restrict__ glist, int32_t* __restrict__ glen) {
+  static_assert(GR == 0 || GR == 2, "four waves: one query tile each, or the four tiles of a 2 x 2 group");
   constexpr bool GROUPS = GR > 0;
-  constexpr int NT = GR == 3 ? 384 : 256;
+  constexpr int NT = 256;
   extern __shared__ int32_t tab_s[];
   int32_t* dmax_s = tab_s;
   int32_t* off_s = tab_s + n_levels;
@@ -1793,19 +1794,22 @@ hipError_t launch_csr_runs(bool l1, const int16_t* lv, const RadiusTable& tab, i
 #define TRA_RUNS(L, G, GRID, NT)                                                                                  \
   csr_runs_kernel<L, G><<<GRID, NT, lds, s>>>(lv, tab.r2c, tab.r2off, tab.dmax, n_levels, tab.n_r2c, tab.T, row_base, \
                                              tiles, log2i(tiles.tw), DM, counts, runs, rowwin, ngh, ngw, gptr, gl, glen)
-  if (glist) {
+  if (glist && group_rows == 2) {
     const dim3 grid(tiles.T * ngh * ngw, BH);
-    if (group_rows == 3) {
-      if (l1) TRA_RUNS(true, 3, grid, 384);
-      else TRA_RUNS(false, 3, grid, 384);
-    } else {
-      if (l1) TRA_RUNS(true, 2, grid, 256);
-      else TRA_RUNS(false, 2, grid, 256);
-    }
+    if (l1) TRA_RUNS(true, 2, grid, 256);
+    else TRA_RUNS(false, 2, grid, 256);
   } else {
+    // 3 x 2 groups merge their lists in a pass of their own: in this kernel
+    // one wave would merge six tiles' runs while the other five wait (168
+    // against 118 + 30 us at Wan2.1-14B 720p).
     const dim3 grid((tiles.count + 3) / 4, BH);
     if (l1) TRA_RUNS(true, 0, grid, 256);
     else TRA_RUNS(false, 0, grid, 256);
+    if (glist) {
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      return launch_group_lists(true, BH, tiles, group_rows, DM, runs, rowwin, nullptr, nullptr, gptr, glist, glen, s);
+    }
   }
 #undef TRA_RUNS
   return hipGetLastError();
