@@ -1388,69 +1388,74 @@ __global__ __launch_bounds__(256 * GR, 1) void attn_bf16_kernel(
   // the score MFMAs are in flight, so that the matrix unit works while the
   // DMA instructions wait to issue.
   auto compute = [&](const TileGeo& t, const char* buf, bool more, const TileGeo& tn, char* nbuf) {
-    const int delta = t.tk > tq ? t.tk - tq : tq - t.tk;
-    const int tv = r2s[toff + min(delta, max(tdmax, 0))];
-    const int thr1 = delta <= tdmax ? tv + 1 : 0;
-    const int dwa = wq - t.kc0 - 4 * h;
-    const int dha = hq - t.kr0;
     int dw2[4], rr[8];
     [[maybe_unused]] int dn[8];
-    if constexpr (BLOCK) {  // block-only mask: every key of a listed tile inside the grid
+    bool doq[2] = {false, false};
+    // The geometry is needed only by a wave whose query tile lists the key
+    // tile (wave-uniform membership bit); the others only take part in the
+    // next tile's loads.
+    if (t.member & mbit) {
+      const int delta = t.tk > tq ? t.tk - tq : tq - t.tk;
+      const int tv = r2s[toff + min(delta, max(tdmax, 0))];
+      const int thr1 = delta <= tdmax ? tv + 1 : 0;
+      const int dwa = wq - t.kc0 - 4 * h;
+      const int dha = hq - t.kr0;
+      if constexpr (BLOCK) {  // block-only mask: every key of a listed tile inside the grid
 #pragma unroll
-      for (int b = 0; b < 4; ++b) dw2[b] = 0;
+        for (int b = 0; b < 4; ++b) dw2[b] = 0;
 #pragma unroll
-      for (int a = 0; a < 8; ++a) rr[a] = 1;
-    } else if constexpr (METRIC == METRIC_WINDOW) {
-      // 1-D window: key (a, b) is kept iff |x| <= rho, x = base - a*W - b the
-      // query's raster index minus the key's.  Upper bound: -b < rr[a]; lower
-      // bound: b < dn[a].
-      const int rho = delta <= tdmax ? tv : -1;
-      const int base = nqh - ((t.tk * g.H + t.kr0) * g.W + t.kc0 + 4 * h);
+        for (int a = 0; a < 8; ++a) rr[a] = 1;
+      } else if constexpr (METRIC == METRIC_WINDOW) {
+        // 1-D window: key (a, b) is kept iff |x| <= rho, x = base - a*W - b the
+        // query's raster index minus the key's.  Upper bound: -b < rr[a]; lower
+        // bound: b < dn[a].
+        const int rho = delta <= tdmax ? tv : -1;
+        const int base = nqh - ((t.tk * g.H + t.kr0) * g.W + t.kc0 + 4 * h);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) dw2[b] = -b;
+        for (int b = 0; b < 4; ++b) dw2[b] = -b;
 #pragma unroll
-      for (int a = 0; a < 8; ++a) {
-        rr[a] = rho - base + a * g.W + 1;
-        dn[a] = rho + base - a * g.W + 1;
-      }
-    } else if constexpr (METRIC == METRIC_L1) {
+        for (int a = 0; a < 8; ++a) {
+          rr[a] = rho - base + a * g.W + 1;
+          dn[a] = rho + base - a * g.W + 1;
+        }
+      } else if constexpr (METRIC == METRIC_L1) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b) dw2[b] = abs(dwa - b);
+        for (int b = 0; b < 4; ++b) dw2[b] = abs(dwa - b);
 #pragma unroll
-      for (int a = 0; a < 8; ++a) rr[a] = thr1 - abs(dha - a);
-    } else {
-      dw2[0] = __mul24(dwa, dwa);
-#pragma unroll
-      for (int b = 1; b < 4; ++b) dw2[b] = dw2[b - 1] - 2 * dwa + (2 * b - 1);
-      rr[0] = thr1 - __mul24(dha, dha);
-#pragma unroll
-      for (int a = 1; a < 8; ++a) rr[a] = rr[a - 1] + 2 * dha - (2 * a - 1);
-    }
-    if (t.ragged) {  // tile at the bottom/right edge of the grid (wave-uniform)
-      // The window's entries span up to 2^26 either side of zero, so its
-      // sentinels are +-2^29: their differences (up to 2^30) stay inside int32
-      // also where an out-of-grid row meets an out-of-grid column.
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        if (t.kc0 + 4 * h + b >= g.W) dw2[b] = METRIC == METRIC_WINDOW ? WIN_COL_OUT : COL_OUT;
-#pragma unroll
-      for (int a = 0; a < 8; ++a)
-        if (t.kr0 + a >= g.H) rr[a] = METRIC == METRIC_WINDOW ? WIN_ROW_OUT : ROW_OUT;
-    }
-    const int mindw = min(min(dw2[0], dw2[1]), min(dw2[2], dw2[3]));
-    bool doq[2];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const int* r = rr + 4 * blk;
-      if constexpr (METRIC == METRIC_WINDOW && !BLOCK) {
-        // Some b in [0, 3] with -b < rr[a] and b < dn[a] (edge columns count;
-        // their masks drop them).
-        bool any = false;
-#pragma unroll
-        for (int a = 4 * blk; a < 4 * blk + 4; ++a) any |= max(0, 1 - rr[a]) <= min(3, dn[a] - 1);
-        doq[blk] = (t.member & mbit) && __any(any);
+        for (int a = 0; a < 8; ++a) rr[a] = thr1 - abs(dha - a);
       } else {
-        doq[blk] = (t.member & mbit) && __any(mindw < max(max(r[0], r[1]), max(r[2], r[3])));
+        dw2[0] = __mul24(dwa, dwa);
+#pragma unroll
+        for (int b = 1; b < 4; ++b) dw2[b] = dw2[b - 1] - 2 * dwa + (2 * b - 1);
+        rr[0] = thr1 - __mul24(dha, dha);
+#pragma unroll
+        for (int a = 1; a < 8; ++a) rr[a] = rr[a - 1] + 2 * dha - (2 * a - 1);
+      }
+      if (t.ragged) {  // tile at the bottom/right edge of the grid (wave-uniform)
+        // The window's entries span up to 2^26 either side of zero, so its
+        // sentinels are +-2^29: their differences (up to 2^30) stay inside int32
+        // also where an out-of-grid row meets an out-of-grid column.
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          if (t.kc0 + 4 * h + b >= g.W) dw2[b] = METRIC == METRIC_WINDOW ? WIN_COL_OUT : COL_OUT;
+#pragma unroll
+        for (int a = 0; a < 8; ++a)
+          if (t.kr0 + a >= g.H) rr[a] = METRIC == METRIC_WINDOW ? WIN_ROW_OUT : ROW_OUT;
+      }
+      const int mindw = min(min(dw2[0], dw2[1]), min(dw2[2], dw2[3]));
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const int* r = rr + 4 * blk;
+        if constexpr (METRIC == METRIC_WINDOW && !BLOCK) {
+          // Some b in [0, 3] with -b < rr[a] and b < dn[a] (edge columns count;
+          // their masks drop them).
+          bool any = false;
+#pragma unroll
+          for (int a = 4 * blk; a < 4 * blk + 4; ++a) any |= max(0, 1 - rr[a]) <= min(3, dn[a] - 1);
+          doq[blk] = __any(any);
+        } else {
+          doq[blk] = __any(mindw < max(max(r[0], r[1]), max(r[2], r[3])));
+        }
       }
     }
     // Sign bytes of the two differences -> 16-bit keep masks of block blk.
